@@ -1,0 +1,174 @@
+/*
+ * tb.h -- C ABI of libtb, the MI355X (gfx950) decode-time hot path of
+ * TokenButler: a learned low-dimensional importance query, produced by a small
+ * MLP at a producer layer, is dotted with the consumer layer's cached keys
+ * projected into the same space; a fixed budget of the best-scoring tokens,
+ * widened by neighbour fetching, is kept on top of an always-kept sink and a
+ * local window; decode attention then reads only those tokens' K/V rows.
+ *
+ * Method source: "TokenButler" technical summary, sections "Core
+ * architecture" (query prediction, key-cache projection, scoring),
+ * "Inference strategy" (sink / local window / important buffers; batched key
+ * projection; prediction interval; neighbour fetching) and "Significance"
+ * (the full cache is kept, only the most relevant tokens are read).
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE pointers unless stated, owned by the caller, to
+ *    contiguous row-major arrays (innermost index last), 16-byte aligned.
+ *    bf16 = bfloat16, fp16 = IEEE binary16, passed as `const void*`.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls only enqueue kernels on it; none synchronizes, none allocates.
+ *  - Host-side arguments are validated before anything is enqueued; on any
+ *    error the call returns a non-zero tb_status and enqueues nothing.
+ *    Device-resident lengths are checked by the kernels where noted.
+ *  - The library keeps no mutable global state; calls are reentrant. Calls
+ *    that share a workspace must be ordered on one stream (they race
+ *    otherwise).
+ *  - Workspaces: size them with the matching *_workspace_bytes() query and
+ *    zero-fill them once before first use (e.g. torch.zeros). Every call
+ *    that takes a workspace leaves it zero-filled again when its kernels
+ *    complete, so it can be reused without clearing.
+ */
+#ifndef TB_H
+#define TB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int tb_status;
+#define TB_OK 0
+#define TB_ERR_INVALID_ARGUMENT 1     /* null/misaligned pointer, bad size  */
+#define TB_ERR_UNSUPPORTED_SHAPE 2    /* shape outside the compiled set      */
+#define TB_ERR_WORKSPACE_TOO_SMALL 3
+#define TB_ERR_HIP 4                  /* a HIP launch failed                 */
+
+/* Neighbour-fetching modes of tb_select (low byte of `mode`). */
+#define TB_NF_FILL 0     /* neighbours count against the fixed budget       */
+#define TB_NF_DILATE 1   /* reserved: neighbours added beyond the budget     */
+/* Flag of tb_select's `mode`: leave the local window out of idx (the list is
+ * sink U important); tb_sparse_decode_attn then adds the window itself from
+ * ctx_len, so one selection serves every step of a prediction interval. */
+#define TB_SEL_OMIT_WINDOW 0x100
+
+/* Human-readable text for a status code (static storage). */
+const char *tb_status_string(tb_status s);
+/* Detail of the last error raised on the calling thread (thread-local). */
+const char *tb_last_error_detail(void);
+/* Library ABI version: 1. */
+int tb_abi_version(void);
+
+/*
+ * Query prediction ("Core architecture", query prediction): a lightweight MLP
+ * reads the producer layer's hidden state and emits one low-dimensional
+ * query per query head (and per slot):
+ *     h    = bf16_rne( SiLU( x w1^T ) )        fp32 accumulation
+ *     qhat = h w2^T                             fp32 accumulation, fp32 out
+ *   x     [B, E]                 bf16
+ *   w1    [Eh, E]                bf16  (out x in)
+ *   w2    [n_out, Eh]            bf16  (out x in); n_out = n_slots * Hq * dp
+ *   qhat  [B, n_out]             fp32  (read as [B, n_slots, Hq, dp])
+ * Limits: E % 128 == 0, Eh % 128 == 0, n_out % 16 == 0, 1 <= B <= 64.
+ * The workspace holds the split partial sums of x w1^T.
+ */
+size_t tb_predict_workspace_bytes(int B, int E, int Eh, int n_out);
+tb_status tb_predict_queries(const void *x, const void *w1, const void *w2, float *qhat,
+                             int B, int E, int Eh, int n_out,
+                             void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Key-cache projection ("Core architecture", key projection; "Inference
+ * strategy", batching: run once per batch of new tokens, not every step):
+ *     kp[b, j, t, :] = fp16_rne( k_cache[b, j, t, :] wk[j]^T )   fp32 accumulation
+ * for t in [pos0[b], pos0[b] + n_tokens) intersected with [0, Lmax).
+ *   k_cache [B, Hkv, Lmax, D]   bf16
+ *   wk      [Hkv, dp, D]        bf16  (out x in, one matrix per KV head)
+ *   kp      [B, Hkv, Lmax, dp]  fp16  (only the projected rows are written)
+ *   pos0    [B]                 int32, device
+ * Limits: D in {64, 128}, dp in {16, 32}, n_tokens >= 0.
+ */
+tb_status tb_project_keys(const void *k_cache, const void *wk, void *kp,
+                          const int32_t *pos0, int n_tokens,
+                          int B, int Hkv, int Lmax, int D, int dp, void *stream);
+
+/*
+ * Scoring ("Core architecture", scoring): token importance is the dot product
+ * of the predicted query with the projected key; query head h reads KV head
+ * h / (Hq / Hkv):
+ *     scores[b, h, t] = sum_c qhat[b, slot, h, c] * kp[b, h / g, t, c]   (fp32)
+ * for t < proj_len[b] (clamped to Lmax); other positions are not written.
+ *   qhat     [B, n_slots, Hq, dp] fp32
+ *   kp       [B, Hkv, Lmax, dp]   fp16
+ *   proj_len [B]                  int32, device
+ *   scores   [B, Hq, Lmax]        fp32
+ * Limits: Hq % Hkv == 0, 1 <= Hq / Hkv <= 8, dp in {16, 32}.
+ */
+tb_status tb_score(const float *qhat, int n_slots, int slot, const void *kp,
+                   const int32_t *proj_len, float *scores,
+                   int B, int Hq, int Hkv, int Lmax, int dp, void *stream);
+
+/*
+ * Selection ("Inference strategy": sink buffer of the first `sink` tokens,
+ * circular local window of the most recent `window` tokens, important buffer
+ * filled from the predicted scores; "Optimizations": neighbour fetching;
+ * "Core architecture": selection under a fixed budget). Per (b, h):
+ *   eligible E = [sink, min(ctx_len[b] - window, proj_len[b])) (empty if the
+ *     bound is <= sink);
+ *   the important buffer takes min(budget, |E|) tokens of E, filled greedily:
+ *     visit E in descending score order (IEEE totalOrder, so -0 < +0; equal
+ *     scores: lower position first); each visited centre c brings c, c-1,
+ *     c+1, ..., c-radius, c+radius (those in E and not yet taken) until the
+ *     buffer is full (mode TB_NF_FILL);
+ *   idx[b, h, 0:count) = sink U window U important, ascending, where
+ *     sink = [0, min(sink, L)), window = [max(0, L - window), L), L = ctx_len[b];
+ *     with TB_SEL_OMIT_WINDOW in mode the window is left out.
+ *   scores  [B, Hq, Lmax] fp32 (read only at eligible positions; finite)
+ *   ctx_len [B], proj_len [B]  int32, device
+ *   idx     [B, Hq, cap]  int32 (slots >= count are left unspecified)
+ *   count   [B, Hq]       int32 (-1 when ctx_len or proj_len is outside
+ *                                [0, Lmax]; idx is then not written)
+ * Limits: cap >= min(Lmax, sink + window + budget) (sink + budget with
+ * TB_SEL_OMIT_WINDOW); 0 <= radius <= 64;
+ * Lmax <= 2^24; sink, window, budget >= 0; mode is TB_NF_FILL, optionally
+ * ORed with TB_SEL_OMIT_WINDOW.
+ */
+size_t tb_select_workspace_bytes(int B, int Hq, int Lmax);
+tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *proj_len,
+                    int B, int Hq, int Lmax, int sink, int window, int budget, int radius,
+                    int mode, int32_t *idx, int32_t *count, int cap,
+                    void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Sparse decode attention ("Significance": attend over the retained cache
+ * reading only the selected tokens):
+ *     out[b, h] = sum_{t in F} softmax_t( scale * q[b,h] . k[b, h/g, t] ) v[b, h/g, t]
+ * with F = idx[b, h, 0:count[b, h]], plus, when ctx_len is not NULL and
+ * window > 0, the local window [w0, L) with L = ctx_len[b] and
+ * w0 = max(L - window, last list entry + 1, 0) ("Inference strategy": the
+ * circular buffer of the most recent tokens). Within a prediction interval the
+ * list (sink U important, see TB_SEL_OMIT_WINDOW) stays fixed and only
+ * ctx_len advances. fp32 softmax and accumulation; out = 0 for an empty F.
+ *   q       [B, Hq, D]        bf16
+ *   k_cache [B, Hkv, Lmax, D] bf16,  v_cache the same
+ *   idx     [B, Hq, cap] int32 ascending, entries in [0, Lmax) (clamped
+ *           otherwise); count [B, Hq] int32 (clamped to [0, cap])
+ *   ctx_len [B] int32, device, or NULL (ctx_len is clamped to [0, Lmax])
+ *   out     [B, Hq, D]        fp32
+ * Limits: D in {64, 128}; Hq % Hkv == 0; window >= 0.
+ * The workspace query takes the same window (pass 0 when ctx_len is NULL).
+ */
+size_t tb_attn_workspace_bytes(int B, int Hq, int cap, int window, int D);
+tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *idx, const int32_t *count, int cap,
+                                const int32_t *ctx_len, int window,
+                                int B, int Hq, int Hkv, int Lmax, int D, float scale,
+                                float *out, void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TB_H */

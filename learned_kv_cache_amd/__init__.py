@@ -1,0 +1,211 @@
+"""libtb: the TokenButler decode-time hot path on MI355X (gfx950).
+
+Thin ctypes binding over the C ABI declared in include/tb.h. Every function
+has the C name, takes torch tensors already resident on the GPU, checks
+dtype / device / shape / contiguity, and passes raw pointers plus the current
+HIP stream. All arithmetic happens in the HIP kernels of libtb.so; if the
+library is missing, loading fails loudly -- there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtb.so")
+
+TB_OK = 0
+TB_ERR_INVALID_ARGUMENT = 1
+TB_ERR_UNSUPPORTED_SHAPE = 2
+TB_ERR_WORKSPACE_TOO_SMALL = 3
+TB_ERR_HIP = 4
+TB_NF_FILL = 0
+TB_NF_DILATE = 1
+TB_SEL_OMIT_WINDOW = 0x100
+
+_lib = None
+_vp = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+
+
+class TBError(RuntimeError):
+    def __init__(self, status, detail):
+        super().__init__("libtb status %d (%s): %s" % (status, status_string(status), detail))
+        self.status = status
+
+
+def lib():
+    """Load libtb.so (built in-tree by learned_kv_cache_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libtb.so not built: run __graft_entry__.build() "
+                          "(or python -m learned_kv_cache_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.tb_status_string.restype = ctypes.c_char_p
+    L.tb_status_string.argtypes = [_i]
+    L.tb_last_error_detail.restype = ctypes.c_char_p
+    L.tb_last_error_detail.argtypes = []
+    L.tb_abi_version.restype = _i
+    L.tb_predict_workspace_bytes.restype = _sz
+    L.tb_predict_workspace_bytes.argtypes = [_i, _i, _i, _i]
+    L.tb_predict_queries.restype = _i
+    L.tb_predict_queries.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]
+    L.tb_project_keys.restype = _i
+    L.tb_project_keys.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+    L.tb_score.restype = _i
+    L.tb_score.argtypes = [_vp, _i, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+    L.tb_select_workspace_bytes.restype = _sz
+    L.tb_select_workspace_bytes.argtypes = [_i, _i, _i]
+    L.tb_select.restype = _i
+    L.tb_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
+                            _sz, _vp]
+    L.tb_attn_workspace_bytes.restype = _sz
+    L.tb_attn_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+    L.tb_sparse_decode_attn.restype = _i
+    L.tb_sparse_decode_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i,
+                                        ctypes.c_float, _vp, _vp, _sz, _vp]
+    _lib = L
+    return L
+
+
+def status_string(s):
+    return lib().tb_status_string(int(s)).decode()
+
+
+def _check(status):
+    if status != TB_OK:
+        raise TBError(status, lib().tb_last_error_detail().decode())
+
+
+def _ptr(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got shape %s" % (name, ndim, tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ws(workspace):
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
+def new_workspace(nbytes, device="cuda"):
+    """A zero-filled workspace of at least nbytes (the calls keep it zeroed)."""
+    return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- predictor
+
+def tb_predict_workspace_bytes(B, E, Eh, n_out):
+    return int(lib().tb_predict_workspace_bytes(B, E, Eh, n_out))
+
+
+def tb_predict_queries(x, w1, w2, qhat, workspace, stream=None):
+    """qhat[B, n_out] = bf16(SiLU(x w1^T)) w2^T. x [B,E] bf16, w1 [Eh,E] bf16,
+    w2 [n_out,Eh] bf16, qhat fp32 (any shape with B*n_out elements)."""
+    B, E = x.shape
+    Eh, n_out = w1.shape[0], w2.shape[0]
+    if tuple(w1.shape) != (Eh, E) or tuple(w2.shape) != (n_out, Eh) or qhat.numel() != B * n_out:
+        raise ValueError("tb_predict_queries: shape mismatch")
+    wp, wn = _ws(workspace)
+    _check(lib().tb_predict_queries(_ptr(x, torch.bfloat16, "x", 2), _ptr(w1, torch.bfloat16, "w1", 2),
+                                    _ptr(w2, torch.bfloat16, "w2", 2), _ptr(qhat, torch.float32, "qhat"),
+                                    B, E, Eh, n_out, wp, wn, _stream(stream)))
+    return qhat
+
+
+# ---------------------------------------------------------------- projection
+
+def tb_project_keys(k_cache, wk, kp, pos0, n_tokens, stream=None):
+    """kp[b, j, t] = fp16(k_cache[b, j, t] wk[j]^T) for t in [pos0[b], pos0[b] + n_tokens)."""
+    B, Hkv, Lmax, D = k_cache.shape
+    dp = wk.shape[1]
+    if tuple(wk.shape) != (Hkv, dp, D) or tuple(kp.shape) != (B, Hkv, Lmax, dp) or pos0.numel() != B:
+        raise ValueError("tb_project_keys: shape mismatch")
+    _check(lib().tb_project_keys(_ptr(k_cache, torch.bfloat16, "k_cache", 4),
+                                 _ptr(wk, torch.bfloat16, "wk", 3), _ptr(kp, torch.float16, "kp", 4),
+                                 _ptr(pos0, torch.int32, "pos0"), int(n_tokens), B, Hkv, Lmax, D, dp,
+                                 _stream(stream)))
+    return kp
+
+
+# ---------------------------------------------------------------- scoring
+
+def tb_score(qhat, kp, proj_len, scores, n_slots=1, slot=0, stream=None):
+    """scores[b, h, t] = qhat[b, slot, h] . kp[b, h // g, t] for t < proj_len[b]."""
+    B, Hkv, Lmax, dp = kp.shape
+    Hq = scores.shape[1]
+    if tuple(scores.shape) != (B, Hq, Lmax) or qhat.numel() != B * n_slots * Hq * dp:
+        raise ValueError("tb_score: shape mismatch")
+    _check(lib().tb_score(_ptr(qhat, torch.float32, "qhat"), int(n_slots), int(slot),
+                          _ptr(kp, torch.float16, "kp", 4), _ptr(proj_len, torch.int32, "proj_len"),
+                          _ptr(scores, torch.float32, "scores", 3), B, Hq, Hkv, Lmax, dp,
+                          _stream(stream)))
+    return scores
+
+
+# ---------------------------------------------------------------- selection
+
+def tb_select_workspace_bytes(B, Hq, Lmax):
+    return int(lib().tb_select_workspace_bytes(B, Hq, Lmax))
+
+
+def tb_select(scores, ctx_len, proj_len, sink, window, budget, radius, idx, count, workspace,
+              mode=TB_NF_FILL, stream=None):
+    """Sink U window U fixed-budget important tokens (neighbour fill), ascending.
+    mode: TB_NF_FILL, optionally | TB_SEL_OMIT_WINDOW."""
+    B, Hq, Lmax = scores.shape
+    cap = idx.shape[-1]
+    if tuple(idx.shape) != (B, Hq, cap) or tuple(count.shape) != (B, Hq):
+        raise ValueError("tb_select: shape mismatch")
+    wp, wn = _ws(workspace)
+    _check(lib().tb_select(_ptr(scores, torch.float32, "scores", 3), _ptr(ctx_len, torch.int32, "ctx_len"),
+                           _ptr(proj_len, torch.int32, "proj_len"), B, Hq, Lmax, int(sink), int(window),
+                           int(budget), int(radius), int(mode), _ptr(idx, torch.int32, "idx", 3),
+                           _ptr(count, torch.int32, "count", 2), cap, wp, wn, _stream(stream)))
+    return idx, count
+
+
+# ---------------------------------------------------------------- attention
+
+def tb_attn_workspace_bytes(B, Hq, cap, window, D):
+    return int(lib().tb_attn_workspace_bytes(B, Hq, cap, window, D))
+
+
+def tb_sparse_decode_attn(q, k_cache, v_cache, idx, count, out, workspace, scale=None,
+                          ctx_len=None, window=0, stream=None):
+    """out[b, h] = softmax-weighted sum of v over the positions idx[b, h, :count[b, h]]
+    plus, with ctx_len given, the local window of the last `window` positions."""
+    B, Hkv, Lmax, D = k_cache.shape
+    Hq = q.shape[1]
+    cap = idx.shape[-1]
+    if (tuple(q.shape) != (B, Hq, D) or tuple(v_cache.shape) != (B, Hkv, Lmax, D)
+            or tuple(idx.shape) != (B, Hq, cap) or tuple(out.shape) != (B, Hq, D)):
+        raise ValueError("tb_sparse_decode_attn: shape mismatch")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    ctx = None if ctx_len is None else _ptr(ctx_len, torch.int32, "ctx_len")
+    wp, wn = _ws(workspace)
+    _check(lib().tb_sparse_decode_attn(_ptr(q, torch.bfloat16, "q", 3), _ptr(k_cache, torch.bfloat16, "k_cache", 4),
+                                       _ptr(v_cache, torch.bfloat16, "v_cache", 4), _ptr(idx, torch.int32, "idx", 3),
+                                       _ptr(count, torch.int32, "count", 2), cap, ctx, int(window),
+                                       B, Hq, Hkv, Lmax, D, float(scale), _ptr(out, torch.float32, "out", 3),
+                                       wp, wn, _stream(stream)))
+    return out

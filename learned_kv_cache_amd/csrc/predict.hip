@@ -1,0 +1,170 @@
+// Query prediction: a two-layer MLP with SiLU on the producer layer's hidden
+// state ("TokenButler" summary, "Core architecture": query prediction).
+//
+//   h    = bf16_rne(SiLU(x w1^T))      mlp1: split over the reduction (E)
+//   qhat = h w2^T                      mlp2: SiLU + bf16 rounding applied to
+//                                      the summed mlp1 partials on load
+//
+// Both are MFMA 16x16x32 bf16 GEMMs with the weight rows as the A operand
+// (16 output features per tile) and the batch as the B operand (up to 16
+// sequences per tile), so the weights -- the only large operand -- stream from
+// HBM in 64-byte runs per lane. The reduction index is permuted identically
+// in A and B so that each lane reads 32 contiguous elements per 128-element
+// block; the result is the same sum. The four waves of a workgroup take
+// interleaved 128-element blocks and are reduced through LDS.
+#include "tb_common.h"
+
+namespace tb {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int BLK = 128;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Reduce the four waves' 16x16 tiles; thread tid gets (row tid/16, col tid%16).
+__device__ __forceinline__ float reduce_waves(const f32x4 &acc, float (*red)[64][4]) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][lane][i] = acc[i];
+    __syncthreads();
+    const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
+    const int src_lane = (row >> 2) * 16 + col, src_i = row & 3;
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += red[w][src_lane][src_i];
+    return s;
+}
+
+__global__ __launch_bounds__(kThreads) void mlp1_kernel(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ w1,
+                                                        float *__restrict__ part, int B, int E,
+                                                        int Eh, int bps) {
+    __shared__ float red[kWaves][64][4];
+    const int jt = blockIdx.x, sp = blockIdx.y, bt = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, kq = lane >> 4;
+    const int nblk = E / BLK;
+    const int blk0 = sp * bps;
+    const int blk1 = blk0 + bps < nblk ? blk0 + bps : nblk;
+    const int bb = bt * 16 + n;
+    const uint16_t *arow = w1 + (size_t)(jt * 16 + n) * E + kq * 32;
+    const uint16_t *brow = x + (size_t)bb * E + kq * 32;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int blk = blk0 + wave; blk < blk1; blk += kWaves) {
+        const uint4 *a = reinterpret_cast<const uint4 *>(arow + blk * BLK);
+        uint4 av[4], bv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = a[v];
+        if (bb < B) {
+            const uint4 *bp = reinterpret_cast<const uint4 *>(brow + blk * BLK);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) bv[v] = bp[v];
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) bv[v] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[v]), as_bf16x8(bv[v]), acc,
+                                                          0, 0, 0);
+    }
+    const float s = reduce_waves(acc, red);
+    const int j = jt * 16 + (threadIdx.x >> 4);
+    const int ob = bt * 16 + (threadIdx.x & 15);
+    if (ob < B) part[((size_t)sp * B + ob) * Eh + j] = s;
+}
+
+__device__ __forceinline__ uint32_t silu_bf16_pair(float z0, float z1) {
+    const float a0 = z0 / (1.f + expf(-z0));
+    const float a1 = z1 / (1.f + expf(-z1));
+    return f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
+}
+
+__global__ __launch_bounds__(kThreads) void mlp2_kernel(const float *__restrict__ part,
+                                                        const uint16_t *__restrict__ w2,
+                                                        float *__restrict__ qhat, int B, int Eh,
+                                                        int n_out, int nsplit) {
+    __shared__ float red[kWaves][64][4];
+    const int nt = blockIdx.x, bt = blockIdx.z;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, kq = lane >> 4;
+    const int nblk = Eh / BLK;
+    const int bb = bt * 16 + n;
+    const uint16_t *arow = w2 + (size_t)(nt * 16 + n) * Eh + kq * 32;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int blk = wave; blk < nblk; blk += kWaves) {
+        const uint4 *a = reinterpret_cast<const uint4 *>(arow + blk * BLK);
+        uint4 av[4], bv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = a[v];
+        if (bb < B) {
+            const int j0 = blk * BLK + kq * 32;
+            float z[32];
+#pragma unroll
+            for (int e = 0; e < 32; ++e) z[e] = 0.f;
+            for (int s = 0; s < nsplit; ++s) {
+                const float4 *p = reinterpret_cast<const float4 *>(part + ((size_t)s * B + bb) * Eh + j0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float4 f = p[e];
+                    z[4 * e] += f.x;
+                    z[4 * e + 1] += f.y;
+                    z[4 * e + 2] += f.z;
+                    z[4 * e + 3] += f.w;
+                }
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                bv[v] = make_uint4(silu_bf16_pair(z[8 * v], z[8 * v + 1]),
+                                   silu_bf16_pair(z[8 * v + 2], z[8 * v + 3]),
+                                   silu_bf16_pair(z[8 * v + 4], z[8 * v + 5]),
+                                   silu_bf16_pair(z[8 * v + 6], z[8 * v + 7]));
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) bv[v] = make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[v]), as_bf16x8(bv[v]), acc,
+                                                          0, 0, 0);
+    }
+    const float s = reduce_waves(acc, red);
+    const int o = nt * 16 + (threadIdx.x >> 4);
+    const int ob = bt * 16 + (threadIdx.x & 15);
+    if (ob < B) qhat[(size_t)ob * n_out + o] = s;
+}
+
+}  // namespace
+
+int predict_nsplit(int E, int Eh) {
+    const int nblk = E / BLK;
+    const int tiles = Eh / 16 > 0 ? Eh / 16 : 1;
+    int ns = (512 + tiles - 1) / tiles;
+    if (ns > nblk) ns = nblk;
+    if (ns < 1) ns = 1;
+    const int bps = (nblk + ns - 1) / ns;
+    return (nblk + bps - 1) / bps;  // no empty split
+}
+
+tb_status launch_predict(const void *x, const void *w1, const void *w2, float *qhat, int B, int E,
+                         int Eh, int n_out, void *ws, int nsplit, hipStream_t st) {
+    const int nblk = E / BLK;
+    const int bps = (nblk + nsplit - 1) / nsplit;
+    float *part = static_cast<float *>(ws);
+    const int bt = (B + 15) / 16;
+    hipLaunchKernelGGL(mlp1_kernel, dim3(Eh / 16, nsplit, bt), dim3(kThreads), 0, st,
+                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w1), part,
+                       B, E, Eh, bps);
+    tb_status e = check_launch("tb_predict_queries(mlp1)");
+    if (e) return e;
+    hipLaunchKernelGGL(mlp2_kernel, dim3(n_out / 16, 1, bt), dim3(kThreads), 0, st, part,
+                       static_cast<const uint16_t *>(w2), qhat, B, Eh, n_out, nsplit);
+    return check_launch("tb_predict_queries(mlp2)");
+}
+
+}  // namespace tb

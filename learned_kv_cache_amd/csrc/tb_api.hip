@@ -1,0 +1,184 @@
+// C ABI entry points of libtb: host-side argument validation, workspace
+// layout and kernel dispatch. Nothing here allocates or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "tb_common.h"
+
+namespace tb {
+
+static thread_local char g_detail[512] = "";
+
+void set_error(const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof g_detail, fmt, ap);
+    va_end(ap);
+}
+
+tb_status check_launch(const char *what) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+        set_error("%s: %s", what, hipGetErrorString(e));
+        return TB_ERR_HIP;
+    }
+    return TB_OK;
+}
+
+}  // namespace tb
+
+using tb::aligned16;
+using tb::aligned4;
+
+extern "C" {
+
+const char *tb_status_string(tb_status s) {
+    switch (s) {
+        case TB_OK: return "ok";
+        case TB_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case TB_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+        case TB_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case TB_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char *tb_last_error_detail(void) { return tb::g_detail; }
+
+int tb_abi_version(void) { return 1; }
+
+// ---------------------------------------------------------------- predictor
+size_t tb_predict_workspace_bytes(int B, int E, int Eh, int n_out) {
+    (void)n_out;
+    if (B <= 0 || E <= 0 || Eh <= 0 || E % 128 || Eh % 128) return 0;
+    return (size_t)tb::predict_nsplit(E, Eh) * B * Eh * sizeof(float);
+}
+
+tb_status tb_predict_queries(const void *x, const void *w1, const void *w2, float *qhat, int B,
+                             int E, int Eh, int n_out, void *workspace, size_t ws_bytes,
+                             void *stream) {
+    TB_REQUIRE(x && w1 && w2 && qhat && workspace, TB_ERR_INVALID_ARGUMENT,
+               "tb_predict_queries: null pointer");
+    TB_REQUIRE(aligned16(x) && aligned16(w1) && aligned16(w2) && aligned16(qhat) &&
+                   aligned16(workspace),
+               TB_ERR_INVALID_ARGUMENT, "tb_predict_queries: pointers must be 16-byte aligned");
+    TB_REQUIRE(B >= 1 && B <= 64 && E > 0 && Eh > 0 && n_out > 0, TB_ERR_INVALID_ARGUMENT,
+               "tb_predict_queries: bad sizes B=%d E=%d Eh=%d n_out=%d", B, E, Eh, n_out);
+    TB_REQUIRE(E % 128 == 0 && Eh % 128 == 0 && n_out % 16 == 0, TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_predict_queries: need E %% 128 == 0, Eh %% 128 == 0, n_out %% 16 == 0");
+    const size_t need = tb_predict_workspace_bytes(B, E, Eh, n_out);
+    TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
+               "tb_predict_queries: workspace %zu < %zu bytes", ws_bytes, need);
+    return tb::launch_predict(x, w1, w2, qhat, B, E, Eh, n_out, workspace,
+                              tb::predict_nsplit(E, Eh), static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- projection
+tb_status tb_project_keys(const void *k_cache, const void *wk, void *kp, const int32_t *pos0,
+                          int n_tokens, int B, int Hkv, int Lmax, int D, int dp, void *stream) {
+    TB_REQUIRE(k_cache && wk && kp && pos0, TB_ERR_INVALID_ARGUMENT,
+               "tb_project_keys: null pointer");
+    TB_REQUIRE(aligned16(k_cache) && aligned16(wk) && aligned16(kp) && aligned4(pos0),
+               TB_ERR_INVALID_ARGUMENT, "tb_project_keys: misaligned pointer");
+    TB_REQUIRE(B >= 1 && B <= 65535 && Hkv >= 1 && Hkv <= 65535 && Lmax >= 1 && n_tokens >= 0,
+               TB_ERR_INVALID_ARGUMENT, "tb_project_keys: bad sizes B=%d Hkv=%d Lmax=%d n=%d", B,
+               Hkv, Lmax, n_tokens);
+    TB_REQUIRE((D == 64 || D == 128) && (dp == 16 || dp == 32), TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_project_keys: D must be 64 or 128 and dp 16 or 32 (got %d, %d)", D, dp);
+    return tb::launch_project(k_cache, wk, kp, pos0, n_tokens, B, Hkv, Lmax, D, dp,
+                              static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- scoring
+tb_status tb_score(const float *qhat, int n_slots, int slot, const void *kp,
+                   const int32_t *proj_len, float *scores, int B, int Hq, int Hkv, int Lmax,
+                   int dp, void *stream) {
+    TB_REQUIRE(qhat && kp && proj_len && scores, TB_ERR_INVALID_ARGUMENT,
+               "tb_score: null pointer");
+    TB_REQUIRE(aligned4(qhat) && aligned16(kp) && aligned4(proj_len) && aligned4(scores),
+               TB_ERR_INVALID_ARGUMENT, "tb_score: misaligned pointer");
+    TB_REQUIRE(B >= 1 && B <= 65535 && Hkv >= 1 && Hq >= 1 && Lmax >= 1 && n_slots >= 1 &&
+                   slot >= 0 && slot < n_slots,
+               TB_ERR_INVALID_ARGUMENT, "tb_score: bad sizes");
+    TB_REQUIRE(Hq % Hkv == 0, TB_ERR_INVALID_ARGUMENT, "tb_score: Hq %% Hkv != 0");
+    TB_REQUIRE(Hq / Hkv <= 8 && Hkv <= 65535 && (dp == 16 || dp == 32), TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_score: need Hq/Hkv <= 8 and dp in {16, 32}");
+    return tb::launch_score(qhat, n_slots, slot, kp, proj_len, scores, B, Hq, Hkv, Lmax, dp,
+                            static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- selection
+size_t tb_select_workspace_bytes(int B, int Hq, int Lmax) {
+    if (B <= 0 || Hq <= 0 || Lmax <= 0) return 0;
+    return tb::select_ws_layout(B, Hq, Lmax, nullptr, nullptr);
+}
+
+tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *proj_len, int B,
+                    int Hq, int Lmax, int sink, int window, int budget, int radius, int mode,
+                    int32_t *idx, int32_t *count, int cap, void *workspace, size_t ws_bytes,
+                    void *stream) {
+    TB_REQUIRE(scores && ctx_len && proj_len && idx && count && workspace,
+               TB_ERR_INVALID_ARGUMENT, "tb_select: null pointer");
+    TB_REQUIRE(aligned4(scores) && aligned4(ctx_len) && aligned4(proj_len) && aligned4(idx) &&
+                   aligned4(count) && aligned16(workspace),
+               TB_ERR_INVALID_ARGUMENT, "tb_select: misaligned pointer");
+    TB_REQUIRE(B >= 1 && Hq >= 1 && (long long)B * Hq <= 65535 && Lmax >= 1,
+               TB_ERR_INVALID_ARGUMENT, "tb_select: bad sizes B=%d Hq=%d Lmax=%d", B, Hq, Lmax);
+    TB_REQUIRE(Lmax <= (1 << 24), TB_ERR_UNSUPPORTED_SHAPE, "tb_select: Lmax > 2^24");
+    TB_REQUIRE(sink >= 0 && window >= 0 && budget >= 0 && radius >= 0, TB_ERR_INVALID_ARGUMENT,
+               "tb_select: negative sink/window/budget/radius");
+    TB_REQUIRE(radius <= 64, TB_ERR_UNSUPPORTED_SHAPE, "tb_select: radius > 64");
+    TB_REQUIRE((mode & ~(0xff | TB_SEL_OMIT_WINDOW)) == 0, TB_ERR_INVALID_ARGUMENT,
+               "tb_select: unknown mode bits 0x%x", mode);
+    TB_REQUIRE((mode & 0xff) == TB_NF_FILL, TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_select: only TB_NF_FILL is implemented");
+    const bool omit = (mode & TB_SEL_OMIT_WINDOW) != 0;
+    const long long need_cap = (long long)sink + (omit ? 0 : window) + budget;
+    const long long min_cap = need_cap < Lmax ? need_cap : Lmax;
+    TB_REQUIRE(cap >= 1 && cap >= min_cap, TB_ERR_INVALID_ARGUMENT,
+               "tb_select: cap %d < min(Lmax, sink + budget (+ window unless omitted)) = %lld",
+               cap, min_cap);
+    const size_t need = tb_select_workspace_bytes(B, Hq, Lmax);
+    TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
+               "tb_select: workspace %zu < %zu bytes", ws_bytes, need);
+    tb::SelectWs ws;
+    tb::select_ws_layout(B, Hq, Lmax, workspace, &ws);
+    return tb::launch_select(scores, ctx_len, proj_len, B, Hq, Lmax, sink, window, budget, radius,
+                             omit, idx, count, cap, ws,
+                             static_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------- attention
+size_t tb_attn_workspace_bytes(int B, int Hq, int cap, int window, int D) {
+    if (B <= 0 || Hq <= 0 || cap <= 0 || window < 0 || D <= 0) return 0;
+    return tb::attn_ws_layout(B, Hq, cap + window, D, nullptr, nullptr, nullptr);
+}
+
+tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *v_cache,
+                                const int32_t *idx, const int32_t *count, int cap,
+                                const int32_t *ctx_len, int window, int B, int Hq, int Hkv,
+                                int Lmax, int D, float scale, float *out, void *workspace,
+                                size_t ws_bytes, void *stream) {
+    TB_REQUIRE(q && k_cache && v_cache && idx && count && out && workspace,
+               TB_ERR_INVALID_ARGUMENT, "tb_sparse_decode_attn: null pointer");
+    TB_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned4(idx) &&
+                   aligned4(count) && aligned4(out) && aligned16(workspace) && aligned4(ctx_len),
+               TB_ERR_INVALID_ARGUMENT, "tb_sparse_decode_attn: misaligned pointer");
+    TB_REQUIRE(B >= 1 && Hq >= 1 && Hkv >= 1 && Lmax >= 1 && cap >= 1 && window >= 0,
+               TB_ERR_INVALID_ARGUMENT, "tb_sparse_decode_attn: bad sizes");
+    TB_REQUIRE(Hq % Hkv == 0, TB_ERR_INVALID_ARGUMENT, "tb_sparse_decode_attn: Hq %% Hkv != 0");
+    TB_REQUIRE(D == 64 || D == 128, TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_sparse_decode_attn: D must be 64 or 128");
+    TB_REQUIRE(scale == scale, TB_ERR_INVALID_ARGUMENT, "tb_sparse_decode_attn: scale is NaN");
+    const int win = ctx_len ? window : 0;
+    const size_t need = tb_attn_workspace_bytes(B, Hq, cap, win, D);
+    TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
+               "tb_sparse_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
+    float *part;
+    uint32_t *ctr;
+    tb::attn_ws_layout(B, Hq, cap + win, D, workspace, &part, &ctr);
+    return tb::launch_attn(q, k_cache, v_cache, idx, count, cap, ctx_len, win, B, Hq, Hkv, Lmax,
+                           D, scale, out, part, ctr, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

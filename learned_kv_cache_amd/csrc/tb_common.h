@@ -1,0 +1,100 @@
+// Internal helpers shared by the libtb translation units (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tb.h"
+
+namespace tb {
+
+// ---- error reporting (tb_api.hip) ------------------------------------------
+void set_error(const char *fmt, ...);
+tb_status check_launch(const char *what);
+
+#define TB_REQUIRE(cond, code, ...)        \
+    do {                                    \
+        if (!(cond)) {                      \
+            ::tb::set_error(__VA_ARGS__);   \
+            return (code);                  \
+        }                                   \
+    } while (0)
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// ---- storage formats -------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// Round-to-nearest-even float -> bfloat16 bits (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t pair) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t pair) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(pair >> 16));
+}
+// Round-to-nearest-even float -> binary16 bits (hardware conversion).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+// ---- cross-lane sums within aligned groups of 4 / 8 / 16 lanes (DPP) --------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// quad_perm [1,0,3,2] = xor 1; [2,3,0,1] = xor 2; row_half_mirror; row_mirror
+template <int LANES>
+__device__ __forceinline__ float group_sum(float v) {
+    v += dpp_f<0xb1>(v);
+    v += dpp_f<0x4e>(v);
+    if constexpr (LANES >= 8) v += dpp_f<0x141>(v);
+    if constexpr (LANES >= 16) v += dpp_f<0x140>(v);
+    return v;
+}
+
+// IEEE totalOrder key of a finite float: larger key <=> larger in totalOrder
+// (so -0 sorts below +0).
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    return u ^ ((u >> 31) ? 0xffffffffu : 0x80000000u);
+}
+
+}  // namespace tb
+
+// ---- launchers (one per translation unit) ------------------------------------
+namespace tb {
+tb_status launch_predict(const void *x, const void *w1, const void *w2, float *qhat, int B, int E,
+                         int Eh, int n_out, void *ws, int nsplit, hipStream_t st);
+int predict_nsplit(int E, int Eh);
+tb_status launch_project(const void *kc, const void *wk, void *kp, const int32_t *pos0, int ntok,
+                         int B, int Hkv, int Lmax, int D, int dp, hipStream_t st);
+tb_status launch_score(const float *qhat, int n_slots, int slot, const void *kp,
+                       const int32_t *plen, float *scores, int B, int Hq, int Hkv, int Lmax,
+                       int dp, hipStream_t st);
+struct SelectWs {
+    uint32_t *hist;      // [nseg][4096], zero at rest
+    uint32_t *ncand;     // [nseg], zero at rest
+    uint32_t *bitmap;    // [nseg][nwords]
+    uint64_t *cand;      // [nseg][Lmax]
+    int nwords;
+};
+size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out);
+tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
+                        int Hq, int Lmax, int S, int W, int K, int r, bool omit_window,
+                        int32_t *idx, int32_t *count, int cap, const SelectWs &ws,
+                        hipStream_t st);
+int attn_nsplit(int rows);
+size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr);
+tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32_t *idx,
+                      const int32_t *count, int cap, const int32_t *ctx, int window, int B,
+                      int Hq, int Hkv, int Lmax, int D, float scale, float *out, float *part,
+                      uint32_t *ctr, hipStream_t st);
+}  // namespace tb

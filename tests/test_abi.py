@@ -1,0 +1,97 @@
+"""The C ABI library: it loads, exports every function include/tb.h declares,
+and its host-side validation rejects bad arguments before anything is
+enqueued (these calls never reach the GPU, so they run on the CPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tb.h")
+
+
+@pytest.fixture(scope="module")
+def tb():
+    import learned_kv_cache_amd as tb
+    if not os.path.exists(tb.LIB_PATH):
+        from learned_kv_cache_amd import build
+        build.build()
+    return tb
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tb_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(tb):
+    names = declared_functions()
+    assert len(names) == 11
+    lib = ctypes.CDLL(tb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version(tb):
+    L = tb.lib()
+    assert L.tb_abi_version() == 1
+    assert tb.status_string(0) == "ok"
+    assert tb.status_string(3) == "workspace too small"
+    assert tb.status_string(99) == "unknown status"
+
+
+def test_workspace_queries(tb):
+    assert tb.tb_predict_workspace_bytes(1, 4096, 1024, 1024) == 8 * 1 * 1024 * 4
+    assert tb.tb_predict_workspace_bytes(1, 100, 1024, 1024) == 0
+    s = tb.tb_select_workspace_bytes(1, 32, 65536)
+    assert s >= 32 * (4096 * 4 + 65536 * 8 + 65536 // 8)
+    a = tb.tb_attn_workspace_bytes(1, 32, 8192, 0, 128)
+    assert a >= 32 * 32 * 130 * 4 + 32 * 4
+
+
+FAKE = 0x10000          # aligned, never dereferenced: validation fails first
+MIS = 0x10002
+
+
+def test_validation_rejects_before_launch(tb):
+    L = tb.lib()
+    vp = ctypes.c_void_p
+    # null pointers
+    assert L.tb_predict_queries(None, vp(FAKE), vp(FAKE), vp(FAKE), 1, 512, 128, 128, vp(FAKE), 1 << 20, None) == 1
+    assert L.tb_score(None, 1, 0, vp(FAKE), vp(FAKE), vp(FAKE), 1, 8, 2, 300, 16, None) == 1
+    # misaligned
+    assert L.tb_project_keys(vp(MIS), vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 2, 300, 64, 16, None) == 1
+    assert b"aligned" in L.tb_last_error_detail()
+    # unsupported shapes
+    assert L.tb_project_keys(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 2, 300, 96, 16, None) == 2
+    assert L.tb_score(vp(FAKE), 1, 0, vp(FAKE), vp(FAKE), vp(FAKE), 1, 18, 2, 300, 16, None) == 2
+    assert L.tb_score(vp(FAKE), 1, 0, vp(FAKE), vp(FAKE), vp(FAKE), 1, 9, 2, 300, 16, None) == 1
+    assert L.tb_predict_queries(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 500, 128, 128, vp(FAKE), 1 << 20, None) == 2
+    # selection: negative budget, radius too large, cap too small, workspace too small, DILATE
+    ws = 1 << 30
+    args = lambda S, W, K, r, mode, cap, wsb: (vp(FAKE), vp(FAKE), vp(FAKE), 1, 8, 300, S, W, K, r, mode,
+                                               vp(FAKE), vp(FAKE), cap, vp(FAKE), wsb, None)
+    assert L.tb_select(*args(4, 16, -1, 1, 0, 52, ws)) == 1
+    assert L.tb_select(*args(4, 16, 32, 65, 0, 52, ws)) == 2
+    assert L.tb_select(*args(4, 16, 32, 1, 0, 51, ws)) == 1
+    assert L.tb_select(*args(4, 16, 32, 1, 0, 52, 100)) == 3
+    assert L.tb_select(*args(4, 16, 32, 1, 1, 52, ws)) == 2
+    # attention: D unsupported, workspace too small, Hq % Hkv
+    A = lambda Hq, D, wsb, win=0: (vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 64, None, win, 1, Hq,
+                                   2, 300, D, ctypes.c_float(0.1), vp(FAKE), vp(FAKE), wsb, None)
+    assert L.tb_sparse_decode_attn(*A(8, 96, ws)) == 2
+    assert L.tb_sparse_decode_attn(*A(8, 64, 16)) == 3
+    assert L.tb_sparse_decode_attn(*A(9, 64, ws)) == 1
+    assert L.tb_sparse_decode_attn(*A(8, 64, ws, -1)) == 1
+    assert L.tb_select(*args(4, 16, 32, 1, 0x200, 52, ws)) == 1
+
+
+def test_binding_rejects_cpu_tensors(tb):
+    import torch
+    x = torch.zeros(1, 512, dtype=torch.bfloat16)
+    w1 = torch.zeros(128, 512, dtype=torch.bfloat16)
+    w2 = torch.zeros(128, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        tb.tb_predict_queries(x, w1, w2, torch.zeros(1, 128), torch.zeros(16, dtype=torch.uint8))

@@ -1,0 +1,235 @@
+"""GPU parity: every libtb entry point against the oracle on the same seeded
+inputs, through the C ABI. Tolerances: projected keys, predicted queries and
+scores within 2e-3 relative (to max(|ref|, row rms)); selections bit-exact
+when both sides see the same scores; attention within 1e-2 abs + 2e-2 rel."""
+import numpy as np
+import pytest
+import torch
+
+from synthetic import (CONFIGS, bits_to_f32_bf16, bits_to_f32_f16, integer_scores, normal_bf16,
+                       normal_f16, rng_for, xavier_bf16)
+from synthetic.workload import make_layer
+from gpu_util import (assert_attn_close, assert_rel, bits, check_selection_band, dev, dev32, host,
+                      say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import learned_kv_cache_amd as tb
+    tb.lib()
+    return tb
+
+
+# ------------------------------------------------------------------ projection
+
+@pytest.mark.parametrize("B,Hkv,L,D,dp,pos0,ntok", [
+    (1, 2, 300, 64, 16, [0], 300),
+    (2, 2, 333, 64, 32, [5, 310], 40),         # second row runs past Lmax
+    (1, 8, 4099, 128, 32, [0], 4099),
+    (3, 4, 1000, 128, 16, [999, 17, 640], 16),
+    (1, 8, 64, 128, 32, [63], 1),
+])
+def test_project_keys(tb, orc, B, Hkv, L, D, dp, pos0, ntok):
+    say("project", B, Hkv, L, D, dp, pos0, ntok)
+    rng = rng_for(50, B, Hkv, L, D, dp)
+    kc = normal_bf16(rng, (B, Hkv, L, D))
+    wk = xavier_bf16(rng, dp, D, lead=(Hkv,))
+    ref = np.full((B, Hkv, L, dp), 0x7E00, np.uint16)
+    orc.project_keys(kc, wk, ref, np.array(pos0, np.int32), ntok)
+    kp = dev(np.full((B, Hkv, L, dp), 0x7E00, np.uint16), torch.float16)
+    tb.tb_project_keys(dev(kc, torch.bfloat16), dev(wk, torch.bfloat16), kp,
+                       dev32(np.array(pos0, np.int32)), ntok)
+    torch.cuda.synchronize()
+    got = bits(kp)
+    untouched = ref == 0x7E00
+    assert np.array_equal(got[untouched], ref[untouched])
+    for b in range(B):
+        lo, hi = pos0[b], min(L, pos0[b] + ntok)
+        assert_rel(bits_to_f32_f16(got[b, :, lo:hi]), bits_to_f32_f16(ref[b, :, lo:hi]), 2e-3,
+                   "project b=%d" % b)
+
+
+# ------------------------------------------------------------------ predictor
+
+@pytest.mark.parametrize("B,E,Eh,nout", [(1, 512, 128, 128), (3, 512, 128, 128),
+                                          (1, 4096, 1024, 1024), (8, 4096, 1024, 1024),
+                                          (4, 3584, 896, 896), (17, 1024, 256, 64)])
+def test_predict_queries(tb, orc, B, E, Eh, nout):
+    say("predict", B, E, Eh, nout)
+    rng = rng_for(51, B, E, Eh, nout)
+    x = normal_bf16(rng, (B, E))
+    w1 = xavier_bf16(rng, Eh, E)
+    w2 = xavier_bf16(rng, nout, Eh)
+    _, ref = orc.predict_queries(x, w1, w2)
+    q = torch.full((B, nout), float("nan"), device="cuda")
+    ws = tb.new_workspace(tb.tb_predict_workspace_bytes(B, E, Eh, nout))
+    tb.tb_predict_queries(dev(x, torch.bfloat16), dev(w1, torch.bfloat16), dev(w2, torch.bfloat16),
+                          q, ws)
+    torch.cuda.synchronize()
+    assert_rel(host(q), ref, 2e-3, "predict")
+
+
+# ------------------------------------------------------------------ scoring
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,dp,P,ns,slot", [
+    (1, 8, 2, 300, 16, [300], 1, 0),
+    (1, 32, 8, 65536, 32, [65536], 1, 0),
+    (2, 28, 4, 5000, 32, [5000, 1234], 2, 1),
+    (3, 8, 8, 777, 16, [1, 777, 513], 1, 0),
+    (1, 16, 2, 2048, 32, [0], 1, 0),
+])
+def test_score(tb, orc, B, Hq, Hkv, L, dp, P, ns, slot):
+    say("score", B, Hq, Hkv, L, dp, P, ns, slot)
+    rng = rng_for(52, B, Hq, L, dp)
+    kp = normal_f16(rng, (B, Hkv, L, dp), std=0.5)
+    qh = rng.standard_normal((B, ns * Hq * dp)).astype(np.float32)
+    Pn = np.array(P, np.int32)
+    ref = orc.score(qh, kp, Pn, Hq, n_slots=ns, slot=slot)
+    s = torch.full((B, Hq, L), float("nan"), device="cuda")
+    tb.tb_score(dev32(qh), dev(kp, torch.float16), dev32(Pn), s, n_slots=ns, slot=slot)
+    torch.cuda.synchronize()
+    got = host(s)
+    for b in range(B):
+        assert np.isnan(got[b, :, P[b]:]).all()
+        if P[b]:
+            assert_rel(got[b, :, :P[b]], ref[b, :, :P[b]], 2e-3, "score b=%d" % b)
+
+
+# ------------------------------------------------------------------ selection
+
+def run_select(tb, scores, L, P, S, W, K, r, cap=None, ws=None):
+    B, Hq, Lmax = scores.shape
+    cap = cap or min(Lmax, S + W + K)
+    idx = torch.full((B, Hq, cap), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, Hq), -7, dtype=torch.int32, device="cuda")
+    if ws is None:
+        ws = tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax))
+    tb.tb_select(dev32(scores), dev32(np.asarray(L, np.int32)), dev32(np.asarray(P, np.int32)),
+                 S, W, K, r, idx, cnt, ws)
+    torch.cuda.synchronize()
+    return host(idx), host(cnt), ws
+
+
+def assert_same_selection(orc, tb, scores, L, P, S, W, K, r, what, ws=None):
+    say("select", what, scores.shape, S, W, K, r)
+    cap = min(scores.shape[-1], S + W + K)
+    ri, rc = orc.select(scores, np.asarray(L, np.int32), np.asarray(P, np.int32), S, W, K, r, cap)
+    gi, gc, ws = run_select(tb, scores, L, P, S, W, K, r, cap, ws)
+    assert np.array_equal(gc, rc), what
+    for b in range(rc.shape[0]):
+        for h in range(rc.shape[1]):
+            n = rc[b, h]
+            assert np.array_equal(gi[b, h, :n], ri[b, h, :n]), (what, b, h)
+    return ws
+
+
+@pytest.mark.parametrize("r", [0, 1, 2])
+def test_select_c1_shapes(tb, orc, r):
+    rng = rng_for(53, r)
+    s = rng.standard_normal((1, 8, 300)).astype(np.float32)
+    assert_same_selection(orc, tb, s, [300], [300], 4, 16, 32, r, "c1 r=%d" % r)
+
+
+@pytest.mark.parametrize("r", [1, 2])
+def test_select_c2_shapes(tb, orc, r):
+    rng = rng_for(54, r)
+    s = rng.standard_normal((1, 32, 65536)).astype(np.float32)
+    assert_same_selection(orc, tb, s, [65536], [65536], 64, 256, 7872, r, "c2 r=%d" % r)
+
+
+def test_select_tie_heavy_and_large_candidate_groups(tb, orc):
+    rng = rng_for(55)
+    # integer scores: few distinct values, boundary bins hold thousands of tokens
+    s = integer_scores(rng, (2, 4, 20000), -3, 4)
+    s[:, :, ::7] = -0.0
+    assert_same_selection(orc, tb, s, [20000, 15001], [20000, 14900], 16, 64, 3000, 1, "ints r1")
+    assert_same_selection(orc, tb, s, [20000, 15001], [20000, 14900], 16, 64, 3000, 2, "ints r2")
+    # all equal: one bin holds all of E (candidate list beyond LDS)
+    z = np.zeros((1, 2, 30000), np.float32)
+    assert_same_selection(orc, tb, z, [30000], [30000], 8, 32, 12000, 1, "all-equal")
+
+
+def test_select_edge_cases(tb, orc):
+    rng = rng_for(56)
+    s = rng.standard_normal((3, 4, 1000)).astype(np.float32)
+    L = [1000, 400, 60]
+    assert_same_selection(orc, tb, s, L, L, 8, 32, 10000, 1, "budget >= |E|")
+    assert_same_selection(orc, tb, s, L, L, 8, 32, 0, 1, "budget 0")
+    assert_same_selection(orc, tb, s, [30, 40, 39], [30, 40, 39], 8, 32, 5, 1, "L <= S + W")
+    assert_same_selection(orc, tb, s, L, [500, 100, 60], 8, 32, 100, 2, "projection lag")
+    assert_same_selection(orc, tb, s, [1, 1, 2], [1, 1, 2], 0, 0, 1, 0, "tiny")
+    pm = np.full((1, 1, 12), -0.0, np.float32)
+    pm[0, 0, 5] = 0.0
+    assert_same_selection(orc, tb, pm, [12], [12], 2, 2, 1, 0, "+0 above -0")
+
+
+def test_select_bad_lengths_flagged(tb, orc):
+    s = np.zeros((2, 2, 100), np.float32)
+    gi, gc, _ = run_select(tb, s, [100, 101], [100, 50], 4, 8, 10, 1)
+    assert (gc[1] == -1).all() and (gc[0] == 22).all()
+
+
+def test_select_workspace_reuse(tb, orc):
+    rng = rng_for(57)
+    ws = None
+    for i in range(3):
+        s = rng.standard_normal((2, 8, 9000)).astype(np.float32)
+        ws = assert_same_selection(orc, tb, s, [9000, 7777], [9000, 7700], 16, 64, 900, 1,
+                                   "reuse %d" % i, ws)
+    assert int(ws[: 2 * 8 * 4096 * 4].count_nonzero()) == 0   # histograms back to zero
+
+
+# ------------------------------------------------------------------ attention
+
+@pytest.mark.parametrize("B,Hq,Hkv,L,D,cap", [(1, 8, 2, 300, 64, 52), (2, 32, 8, 5000, 128, 700),
+                                              (1, 28, 4, 3000, 128, 3000), (1, 4, 1, 600, 64, 513)])
+def test_attention_random_sets(tb, orc, B, Hq, Hkv, L, D, cap):
+    say("attn", B, Hq, Hkv, L, D, cap)
+    rng = rng_for(58, B, Hq, L, D, cap)
+    q = normal_bf16(rng, (B, Hq, D))
+    kc = normal_bf16(rng, (B, Hkv, L, D))
+    vc = normal_bf16(rng, (B, Hkv, L, D))
+    idx = np.zeros((B, Hq, cap), np.int32)
+    cnt = np.zeros((B, Hq), np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            n = int(rng.integers(0, cap + 1)) if (b + h) % 5 else cap
+            if (b + h) % 11 == 3:
+                n = 0
+            sel = np.sort(rng.choice(L, n, replace=False)).astype(np.int32)
+            idx[b, h, :n] = sel
+            cnt[b, h] = n
+    ref = orc.sparse_attention(q, kc, vc, idx, cnt)
+    out = torch.full((B, Hq, D), float("nan"), device="cuda")
+    ws = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, 0, D))
+    for rep in range(2):                        # the arrival counters reset themselves
+        tb.tb_sparse_decode_attn(dev(q, torch.bfloat16), dev(kc, torch.bfloat16),
+                                 dev(vc, torch.bfloat16), dev32(idx), dev32(cnt), out, ws)
+        torch.cuda.synchronize()
+        assert_attn_close(host(out), ref, "attn rep %d" % rep)
+
+
+def test_attention_dense_equals_full_budget(tb, orc):
+    say("attn dense")
+    rng = rng_for(59)
+    B, Hq, Hkv, L, D = 1, 8, 2, 4000, 128
+    q = normal_bf16(rng, (B, Hq, D))
+    kc = normal_bf16(rng, (B, Hkv, L, D))
+    vc = normal_bf16(rng, (B, Hkv, L, D))
+    idx = np.broadcast_to(np.arange(L, dtype=np.int32), (B, Hq, L)).copy()
+    cnt = np.full((B, Hq), L, np.int32)
+    out = torch.zeros((B, Hq, D), device="cuda")
+    ws = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, L, 0, D))
+    tb.tb_sparse_decode_attn(dev(q, torch.bfloat16), dev(kc, torch.bfloat16),
+                             dev(vc, torch.bfloat16), dev32(idx), dev32(cnt), out, ws)
+    torch.cuda.synchronize()
+    # dense causal attention, last query row, fp64 CPU library routine
+    kk = torch.from_numpy(np.repeat(bits_to_f32_bf16(kc), 4, axis=1)).double()
+    vv = torch.from_numpy(np.repeat(bits_to_f32_bf16(vc), 4, axis=1)).double()
+    qq = torch.from_numpy(bits_to_f32_bf16(q)).double()[:, :, None]
+    dense = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[:, :, 0].numpy()
+    assert_attn_close(host(out), dense, "dense")
