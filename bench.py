@@ -1,0 +1,296 @@
+"""Decode-step throughput of the TokenButler hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: predict the importance
+queries (producer MLP), project the newest token's key, score every cached
+token, select sink + window + fixed budget with neighbour fill, and run
+sparse decode attention. Workload: Llama-3.1-8B-shaped single consumer layer,
+B=1, L=65536, 32 query / 8 KV heads, head dim 128, E=4096, Eh=1024, d'=32,
+sink 64, window 256, budget 7872, radius 1, 64 planted 8-token spans.
+
+Inputs are resident in HBM before the timed region; R replicas of every
+per-step input are rotated so that each step reads cold memory (the working
+set of one step fits in the 256 MiB MALL). The dominant kernel (sparse
+attention gather) is timed live with HIP events on its launch stream.
+
+Prints one JSON line. Run with --gpus 1 only.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+METRIC = "sparse decode steps/s at 64K ctx, 8K budget; achieved HBM GB/s vs peak"
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_gather_c2_traffic.txt")
+ATTN_SRC = os.path.join(ROOT, "learned_kv_cache_amd", "csrc", "attn.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def planting_direction(inp, cfg):
+    """Key direction that raises head h's score fastest (Wk^T q_hat_h), from a
+    float64 numpy evaluation of the predictor on the host; only used to build
+    the planted spans of the synthetic workload."""
+    from synthetic import bits_to_f32_bf16
+    x = bits_to_f32_bf16(inp["x"]).astype(np.float64)
+    w1 = bits_to_f32_bf16(inp["w1"]).astype(np.float64)
+    w2 = bits_to_f32_bf16(inp["w2"]).astype(np.float64)
+    z = x @ w1.T
+    h = z / (1.0 + np.exp(-z))
+    qh = (h @ w2.T).reshape(x.shape[0], cfg.Hq, cfg.dp)
+    wk = np.repeat(bits_to_f32_bf16(inp["wk"]).astype(np.float64), cfg.g, axis=0)
+    return np.einsum("bhc,hcd->bhd", qh, wk)
+
+
+def traffic_record():
+    """HBM bytes per attention launch from the committed rocprofv3 PMC
+    summary, if it was taken on the current attention source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
+    if rec.get("attn_source_sha256_16") != src_hash or "traffic_bytes_per_launch" not in rec:
+        return None
+    return float(rec["traffic_bytes_per_launch"])
+
+
+def cpu_baseline(inp, cfg, seconds):
+    """The oracle (plain C, fp64, single thread) on full decode steps of the
+    same workload, repeated for about `seconds` of CPU time."""
+    import oracle as orc
+    B, L = 1, cfg.L
+    kp = np.zeros((B, cfg.Hkv, L, cfg.dp), np.uint16)
+    orc.project_keys(inp["kc"], inp["wk"], kp, np.zeros(B, np.int32), L - 1)   # setup, untimed
+    ctx = inp["ctx_len"]
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        orc.decode_step(inp["x"], inp["w1"], inp["w2"], inp["kc"], inp["vc"], inp["wk"], kp,
+                        inp["q"], ctx, ctx, (ctx - 1).astype(np.int32), 1, cfg.S, cfg.W, cfg.K,
+                        cfg.r, cap=cfg.cap)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full decode steps of the same workload (predict, project 1 token, "
+                      "score 65536 tokens x 32 heads, select, attend), single-threaded C, "
+                      "%.1f s" % (n, el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--replicas", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stages", action="store_true", help="also time each stage")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a 1 GiB device copy (for PMC byte-counter calibration) and exit")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only; --gpus %d is not supported (this path does not "
+              "shard across GPUs)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import learned_kv_cache_amd as tb
+    from synthetic import CONFIGS
+    from synthetic.workload import make_layer
+
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+        return
+
+    cfg = CONFIGS[2]
+    B, L, R = 1, cfg.L, max(1, args.replicas)
+    log("generating inputs (%s)" % cfg.name)
+    inp = make_layer(cfg, seed=0, direction_fn=lambda d: planting_direction(d, cfg))
+
+    def dev16(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(dt).cuda()
+
+    log("uploading %d replicas" % R)
+    reps = []
+    base = {k: dev16(inp[k], torch.bfloat16) for k in ("x", "w1", "w2", "kc", "vc", "wk", "q")}
+    zeros = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for i in range(R):
+        r = {k: (v if i == 0 else v.clone()) for k, v in base.items()}
+        r["kp"] = torch.zeros((B, cfg.Hkv, L, cfg.dp), dtype=torch.float16, device="cuda")
+        tb.tb_project_keys(r["kc"], r["wk"], r["kp"], zeros, L - 1)   # the cache before this step
+        reps.append(r)
+    torch.cuda.synchronize()
+
+    ctx = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    pos_new = torch.full((B,), L - 1, dtype=torch.int32, device="cuda")
+    qhat = torch.empty((B, cfg.n_out), device="cuda")
+    scores = torch.empty((B, cfg.Hq, L), device="cuda")
+    cap = cfg.cap
+    idx = torch.zeros((B, cfg.Hq, cap), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((B, cfg.Hq), dtype=torch.int32, device="cuda")
+    out = torch.zeros((B, cfg.Hq, cfg.D), device="cuda")
+    ws_p = tb.new_workspace(tb.tb_predict_workspace_bytes(B, cfg.E, cfg.Eh, cfg.n_out))
+    ws_s = tb.new_workspace(tb.tb_select_workspace_bytes(B, cfg.Hq, L))
+    ws_a = tb.new_workspace(tb.tb_attn_workspace_bytes(B, cfg.Hq, cap, 0, cfg.D))
+
+    # Pre-marshalled C ABI calls (same entry points as the binding, without
+    # per-call Python argument checks, so the host keeps ahead of the GPU).
+    # Validate every argument set once through the checked binding first.
+    tb.tb_predict_queries(reps[0]["x"], reps[0]["w1"], reps[0]["w2"], qhat, ws_p)
+    tb.tb_score(qhat, reps[0]["kp"], ctx, scores)
+    tb.tb_select(scores, ctx, ctx, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt, ws_s)
+    tb.tb_sparse_decode_attn(reps[0]["q"], reps[0]["kc"], reps[0]["vc"], idx, cnt, out, ws_a)
+    torch.cuda.synchronize()
+
+    L_ = tb.lib()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    nb = lambda w: w.numel()
+    calls = []
+    for r in reps:
+        calls.append([
+            (L_.tb_predict_queries, (P(r["x"]), P(r["w1"]), P(r["w2"]), P(qhat), B, cfg.E, cfg.Eh,
+                                     cfg.n_out, P(ws_p), nb(ws_p), sp)),
+            (L_.tb_project_keys, (P(r["kc"]), P(r["wk"]), P(r["kp"]), P(pos_new), 1, B, cfg.Hkv, L,
+                                  cfg.D, cfg.dp, sp)),
+            (L_.tb_score, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(scores), B, cfg.Hq, cfg.Hkv, L,
+                           cfg.dp, sp)),
+            (L_.tb_select, (P(scores), P(ctx), P(ctx), B, cfg.Hq, L, cfg.S, cfg.W, cfg.K, cfg.r,
+                            tb.TB_NF_FILL, P(idx), P(cnt), cap, P(ws_s), nb(ws_s), sp)),
+            (L_.tb_sparse_decode_attn, (P(r["q"]), P(r["kc"]), P(r["vc"]), P(idx), P(cnt), cap,
+                                        None, 0, B, cfg.Hq, cfg.Hkv, L, cfg.D,
+                                        ctypes.c_float(1.0 / np.sqrt(cfg.D)), P(out), P(ws_a),
+                                        nb(ws_a), sp)),
+        ])
+
+    def run_step(i, ev=None):
+        c = calls[i % R]
+        for j, (fn, a) in enumerate(c):
+            if ev is not None and j == 4:
+                ev[0].record(stream)
+            st = fn(*a)
+            if st:
+                raise RuntimeError("libtb call failed: %s" % L_.tb_last_error_detail().decode())
+        if ev is not None:
+            ev[1].record(stream)
+
+    log("warmup %d" % args.warmup)
+    for i in range(args.warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(K)]
+    log("timing %d steps" % K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        run_step(i, evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    attn_ms = [a.elapsed_time(b) for a, b in evs]
+    attn_avg_s = float(np.mean(attn_ms)) / 1e3
+
+    # algorithmic bytes of one attention launch: each distinct (kv head, token)
+    # row of the g heads' attended sets, K and V, bf16 -- counted from idx
+    gi = idx.cpu().numpy()
+    gc = cnt.cpu().numpy()
+    union_rows = 0
+    per_head_rows = int(gc.sum())
+    for kvh in range(cfg.Hkv):
+        s = set()
+        for h in range(kvh * cfg.g, (kvh + 1) * cfg.g):
+            s.update(gi[0, h, :gc[0, h]].tolist())
+        union_rows += len(s)
+    row_bytes = 2 * cfg.D * 2
+    attn_bytes = union_rows * row_bytes + cfg.Hq * cfg.D * (2 + 4) + gc.size * 4 + per_head_rows * 4
+    achieved = attn_bytes / attn_avg_s / 1e9
+
+    # compulsory bytes of the whole step (for the step-level GB/s)
+    kp_bytes = L * cfg.Hkv * cfg.dp * 2
+    mlp_bytes = (cfg.E * cfg.Eh + cfg.Eh * cfg.n_out) * 2
+    proj_bytes = cfg.Hkv * (cfg.D * 2 + cfg.dp * cfg.D * 2 + cfg.dp * 2)
+    step_bytes = union_rows * row_bytes + kp_bytes + mlp_bytes + proj_bytes
+    step_s = elapsed / K
+
+    stages = None
+    if args.stages:
+        names = ["predict", "project", "score", "select", "attention"]
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(200)]
+        for i in range(200):
+            c = calls[i % R]
+            for j, (fn, a) in enumerate(c):
+                sev[i][j].record(stream)
+                fn(*a)
+            sev[i][5].record(stream)
+        torch.cuda.synchronize()
+        stages = {n: round(float(np.median([e[j].elapsed_time(e[j + 1]) for e in sev])) * 1e3, 2)
+                  for j, n in enumerate(names)}
+
+    traffic = traffic_record()
+    res = {
+        "metric": METRIC,
+        "value": K / elapsed,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: B=%d L=%d Hq=%d Hkv=%d D=%d E=%d Eh=%d d'=%d sink=%d "
+                               "window=%d budget=%d radius=%d, predictor every step, %d planted "
+                               "8-token spans, %d rotated input replicas"
+                               % (cfg.name, B, L, cfg.Hq, cfg.Hkv, cfg.D, cfg.E, cfg.Eh, cfg.dp,
+                                  cfg.S, cfg.W, cfg.K, cfg.r, cfg.n_spans, R),
+                   "global_batch": B, "seq_len": L},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "sparse decode attention gather (attn_kernel<128>)",
+                     "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6},
+        "step_gbps": step_bytes / step_s / 1e9,
+        "step_compulsory_bytes": step_bytes,
+        "attended_rows": {"union": union_rows, "per_head": per_head_rows},
+    }
+    if stages:
+        res["stages_us"] = stages
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

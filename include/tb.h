@@ -71,7 +71,7 @@ int tb_abi_version(void);
  *   w1    [Eh, E]                bf16  (out x in)
  *   w2    [n_out, Eh]            bf16  (out x in); n_out = n_slots * Hq * dp
  *   qhat  [B, n_out]             fp32  (read as [B, n_slots, Hq, dp])
- * Limits: E % 128 == 0, Eh % 128 == 0, n_out % 16 == 0, 1 <= B <= 64.
+ * Limits: E % 128 == 0, Eh % 128 == 0, Eh <= 1536, n_out % 16 == 0, 1 <= B <= 64.
  * The workspace holds the split partial sums of x w1^T.
  */
 size_t tb_predict_workspace_bytes(int B, int E, int Eh, int n_out);

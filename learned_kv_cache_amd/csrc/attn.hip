@@ -7,9 +7,10 @@
 // lane), so a wave gathers 64/(D/8) rows per 16-byte load and keeps U rows of
 // K and V in flight per lane. Logits are reduced with DPP, the softmax runs
 // online in registers (base-2, fp32), and the workgroup writes one partial
-// (max, sum, o[D]). The last workgroup of a head (atomic arrival counter)
-// merges the partials by log-sum-exp and writes the fp32 output, then resets
-// the counter, so no second launch is needed.
+// (max, sum, o[D]). A second, small launch merges each head's partials by
+// log-sum-exp into the fp32 output; the kernel boundary is the only
+// synchronization between workgroups (no device-scope fences, which on this
+// chip would write back and invalidate the XCD's L2).
 //
 // Launch order is XCD-aware: dispatch sends workgroup i to XCD i % 8, and the
 // block index is decoded so that each XCD receives a contiguous run of work
@@ -32,8 +33,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ count, int cap, const int32_t *__restrict__ ctx, int window,
     int Hq, int Hkv, int Lmax, float scale_log2,
-    int nsplit, int n_items, float *__restrict__ part, uint32_t *__restrict__ ctr,
-    float *__restrict__ out) {
+    int nsplit, int n_items, float *__restrict__ part) {
     constexpr int LPR = D / 8;          // lanes per row
     constexpr int RPW = 64 / LPR;       // row groups per wave
     constexpr int NG = kWaves * RPW;    // row groups per workgroup
@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
 
     __shared__ float sm_o[NG][D];
     __shared__ float sm_m[NG], sm_l[NG];
-    __shared__ int sm_last;
+    __shared__ int sm_tok[CH];
 
     const int nb = gridDim.x;
     const int bid = blockIdx.x;
@@ -73,6 +73,13 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     const int total = n + nwin;
     const int lo = split * CH;
     const int hi = (lo + CH < total) ? lo + CH : total;
+    // this workgroup's positions, clamped to the cache
+    for (int i = threadIdx.x; i < CH; i += kThreads) {
+        const int r = lo + i;
+        int t = r < hi ? (r < n ? ib[r] : wstart + (r - n)) : 0;
+        sm_tok[i] = t < 0 ? 0 : (t >= Lmax ? Lmax - 1 : t);
+    }
+    __syncthreads();
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rg = lane / LPR, cl = lane % LPR;
@@ -104,8 +111,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
         for (int u = 0; u < U; ++u) {
             const int r = r0 + u * STRIDE;
             ok[u] = r < hi;
-            int t = ok[u] ? (r < n ? ib[r] : wstart + (r - n)) : 0;
-            tk[u] = t < 0 ? 0 : (t >= Lmax ? Lmax - 1 : t);
+            tk[u] = sm_tok[ok[u] ? r - lo : 0];
         }
         uint4 kr[U], vr[U];
 #pragma unroll
@@ -157,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
         m = mx;
     }
 
-    // merge the row groups of this workgroup
+    // merge the row groups of this workgroup into one partial
 #pragma unroll
     for (int c = 0; c < 8; ++c) sm_o[grp][cl * 8 + c] = acc[c];
     if (cl == 0) {
@@ -183,54 +189,68 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
             pp[1] = Ls;
         }
     }
+}
 
-    // arrival: the last workgroup of this head merges every split
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(ctr + bh, 1u, __ATOMIC_ACQ_REL,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        sm_last = (prev == (uint32_t)(nsplit - 1));
-    }
-    __syncthreads();
-    if (!sm_last) return;
-    __threadfence();
-    if (threadIdx.x < D) {
-        const float *base = part + (size_t)bh * nsplit * (D + 2);
-        float M = -1e30f;
-        for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[(size_t)s * (D + 2)]);
-        float den = 0.f, num = 0.f;
-        for (int s = 0; s < nsplit; ++s) {
-            const float *ps = base + (size_t)s * (D + 2);
-            const float w = exp2f(ps[0] - M);
-            den += ps[1] * w;
-            num += ps[2 + threadIdx.x] * w;
+// One workgroup per (b, h): log-sum-exp merge of the split partials. Up to
+// 32 partials at a time are staged in LDS with independent loads, and the
+// running (max, sum, numerator) is rescaled from one stage to the next.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restrict__ part,
+                                                           int nsplit, float *__restrict__ out) {
+    constexpr int CS = 32;
+    constexpr int PW = D + 2;
+    __shared__ float sm[CS * PW];
+    const int bh = blockIdx.x;
+    const float *base = part + (size_t)bh * nsplit * PW;
+    constexpr int PER = (CS * PW + 255) / 256;
+    float M = -1e30f, den = 0.f, num = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += CS) {
+        const int ns = nsplit - s0 < CS ? nsplit - s0 : CS;
+        const float *src = base + (size_t)s0 * PW;
+        float v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = threadIdx.x + k * 256;
+            v[k] = i < ns * PW ? src[i] : 0.f;
         }
-        out[(size_t)bh * D + threadIdx.x] = den > 0.f ? num / den : 0.f;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = threadIdx.x + k * 256;
+            if (i < ns * PW) sm[i] = v[k];
+        }
+        __syncthreads();
+        float Mc = M;
+        for (int s = 0; s < ns; ++s) Mc = fmaxf(Mc, sm[s * PW]);
+        const float r = exp2f(M - Mc);
+        den *= r;
+        num *= r;
+        for (int s = 0; s < ns; ++s) {
+            const float w = exp2f(sm[s * PW] - Mc);
+            den += sm[s * PW + 1] * w;
+            if (threadIdx.x < D) num += sm[s * PW + 2 + threadIdx.x] * w;
+        }
+        M = Mc;
     }
-    if (threadIdx.x == 0) ctr[bh] = 0u;
+    if (threadIdx.x < D) out[(size_t)bh * D + threadIdx.x] = den > 0.f ? num / den : 0.f;
 }
 
 }  // namespace
 
 int attn_nsplit(int rows) { return (rows + CH - 1) / CH > 0 ? (rows + CH - 1) / CH : 1; }
 
-size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr) {
+size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part) {
     const size_t nbh = (size_t)B * Hq;
     size_t part_bytes = nbh * attn_nsplit(rows) * (D + 2) * sizeof(float);
     part_bytes = (part_bytes + 255) & ~(size_t)255;
-    const size_t total = part_bytes + nbh * sizeof(uint32_t);
-    if (base) {
-        *part = static_cast<float *>(base);
-        *ctr = reinterpret_cast<uint32_t *>(static_cast<char *>(base) + part_bytes);
-    }
-    return total;
+    if (base) *part = static_cast<float *>(base);
+    return part_bytes;
 }
 
 tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32_t *idx,
                       const int32_t *count, int cap, const int32_t *ctx, int window, int B,
                       int Hq, int Hkv, int Lmax, int D, float scale, float *out, float *part,
-                      uint32_t *ctr, hipStream_t st) {
+                      hipStream_t st) {
     if (ctx == nullptr) window = 0;
     const int nsplit = attn_nsplit(cap + window);
     const long long items = (long long)B * Hq * nsplit;
@@ -246,12 +266,20 @@ tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32
     if (D == 128)
         hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)nb), dim3(kThreads), 0, st, qq, kk, vv,
                            idx, count, cap, ctx, window, Hq, Hkv, Lmax, scale_log2, nsplit,
-                           (int)items, part, ctr, out);
+                           (int)items, part);
     else
         hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)nb), dim3(kThreads), 0, st, qq, kk, vv,
                            idx, count, cap, ctx, window, Hq, Hkv, Lmax, scale_log2, nsplit,
-                           (int)items, part, ctr, out);
-    return check_launch("tb_sparse_decode_attn");
+                           (int)items, part);
+    tb_status e = check_launch("tb_sparse_decode_attn(split)");
+    if (e) return e;
+    if (D == 128)
+        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(B * Hq), dim3(256), 0, st, part, nsplit,
+                           out);
+    else
+        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(B * Hq), dim3(256), 0, st, part, nsplit,
+                           out);
+    return check_launch("tb_sparse_decode_attn(combine)");
 }
 
 }  // namespace tb

@@ -2,8 +2,9 @@
 // state ("TokenButler" summary, "Core architecture": query prediction).
 //
 //   h    = bf16_rne(SiLU(x w1^T))      mlp1: split over the reduction (E)
-//   qhat = h w2^T                      mlp2: SiLU + bf16 rounding applied to
-//                                      the summed mlp1 partials on load
+//   qhat = h w2^T                      mlp2: each workgroup first builds h
+//                                      (sum of the mlp1 partials, SiLU, bf16)
+//                                      for its batch tile in LDS
 //
 // Both are MFMA 16x16x32 bf16 GEMMs with the weight rows as the A operand
 // (16 output features per tile) and the batch as the B operand (up to 16
@@ -23,6 +24,8 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int BLK = 128;
+constexpr int kMaxSplit = 16;
+constexpr int kMaxBlkPerWave = 3;   // Eh <= 1536 = 3 blocks per wave
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -79,59 +82,76 @@ __global__ __launch_bounds__(kThreads) void mlp1_kernel(const uint16_t *__restri
     if (ob < B) part[((size_t)sp * B + ob) * Eh + j] = s;
 }
 
-__device__ __forceinline__ uint32_t silu_bf16_pair(float z0, float z1) {
-    const float a0 = z0 / (1.f + expf(-z0));
-    const float a1 = z1 / (1.f + expf(-z1));
-    return f32_to_bf16_rne(a0) | (f32_to_bf16_rne(a1) << 16);
+__device__ __forceinline__ uint32_t silu_bf16(float z) {
+    return f32_to_bf16_rne(z / (1.f + expf(-z)));
 }
 
+// h for the batch tile is built once per workgroup in LDS: the mlp1 split
+// partials are summed in a fixed order, passed through SiLU and rounded to
+// bf16; the MFMA B operand is then read from LDS.
 __global__ __launch_bounds__(kThreads) void mlp2_kernel(const float *__restrict__ part,
                                                         const uint16_t *__restrict__ w2,
                                                         float *__restrict__ qhat, int B, int Eh,
                                                         int n_out, int nsplit) {
     __shared__ float red[kWaves][64][4];
+    extern __shared__ uint16_t s_h[];   // [16][Eh]
     const int nt = blockIdx.x, bt = blockIdx.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, kq = lane >> 4;
+    const int nb = B - bt * 16 < 16 ? B - bt * 16 : 16;
     const int nblk = Eh / BLK;
-    const int bb = bt * 16 + n;
     const uint16_t *arow = w2 + (size_t)(nt * 16 + n) * Eh + kq * 32;
+    // this wave's W2 tiles are requested before h is built
+    uint4 av[kMaxBlkPerWave][4];
+#pragma unroll
+    for (int i = 0; i < kMaxBlkPerWave; ++i) {
+        const int blk = wave + i * kWaves;
+        if (blk < nblk) {
+            const uint4 *a = reinterpret_cast<const uint4 *>(arow + blk * BLK);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) av[i][v] = a[v];
+        }
+    }
+    // rows of the tile beyond B are zero
+    for (int i = threadIdx.x; i < (16 - nb) * Eh; i += kThreads) s_h[nb * Eh + i] = 0;
+    const int q4 = Eh / 4;
+    for (int it = threadIdx.x; it < nb * q4; it += kThreads) {
+        const int bl = it / q4, j = (it - bl * q4) * 4;
+        const float *p0 = part + (size_t)(bt * 16 + bl) * Eh + j;
+        const size_t sstride = (size_t)B * Eh;
+        float4 f[kMaxSplit];
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp)
+            f[sp] = sp < nsplit ? *reinterpret_cast<const float4 *>(p0 + sp * sstride)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp) {
+            z.x += f[sp].x;
+            z.y += f[sp].y;
+            z.z += f[sp].z;
+            z.w += f[sp].w;
+        }
+        uint2 hv;
+        hv.x = silu_bf16(z.x) | (silu_bf16(z.y) << 16);
+        hv.y = silu_bf16(z.z) | (silu_bf16(z.w) << 16);
+        *reinterpret_cast<uint2 *>(s_h + bl * Eh + j) = hv;
+    }
+    __syncthreads();
+    const uint4 *hrow = reinterpret_cast<const uint4 *>(s_h + n * Eh + kq * 32);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int blk = wave; blk < nblk; blk += kWaves) {
-        const uint4 *a = reinterpret_cast<const uint4 *>(arow + blk * BLK);
-        uint4 av[4], bv[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) av[v] = a[v];
-        if (bb < B) {
-            const int j0 = blk * BLK + kq * 32;
-            float z[32];
+    for (int i = 0; i < kMaxBlkPerWave; ++i) {
+        const int blk = wave + i * kWaves;
+        if (blk < nblk) {
+            uint4 bv[4];
 #pragma unroll
-            for (int e = 0; e < 32; ++e) z[e] = 0.f;
-            for (int s = 0; s < nsplit; ++s) {
-                const float4 *p = reinterpret_cast<const float4 *>(part + ((size_t)s * B + bb) * Eh + j0);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float4 f = p[e];
-                    z[4 * e] += f.x;
-                    z[4 * e + 1] += f.y;
-                    z[4 * e + 2] += f.z;
-                    z[4 * e + 3] += f.w;
-                }
-            }
+            for (int v = 0; v < 4; ++v) bv[v] = hrow[blk * (BLK / 8) + v];
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-                bv[v] = make_uint4(silu_bf16_pair(z[8 * v], z[8 * v + 1]),
-                                   silu_bf16_pair(z[8 * v + 2], z[8 * v + 3]),
-                                   silu_bf16_pair(z[8 * v + 4], z[8 * v + 5]),
-                                   silu_bf16_pair(z[8 * v + 6], z[8 * v + 7]));
-        } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) bv[v] = make_uint4(0, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[i][v]),
+                                                              as_bf16x8(bv[v]), acc, 0, 0, 0);
         }
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[v]), as_bf16x8(bv[v]), acc,
-                                                          0, 0, 0);
     }
     const float s = reduce_waves(acc, red);
     const int o = nt * 16 + (threadIdx.x >> 4);
@@ -146,6 +166,7 @@ int predict_nsplit(int E, int Eh) {
     const int tiles = Eh / 16 > 0 ? Eh / 16 : 1;
     int ns = (512 + tiles - 1) / tiles;
     if (ns > nblk) ns = nblk;
+    if (ns > kMaxSplit) ns = kMaxSplit;
     if (ns < 1) ns = 1;
     const int bps = (nblk + ns - 1) / ns;
     return (nblk + bps - 1) / bps;  // no empty split
@@ -162,7 +183,8 @@ tb_status launch_predict(const void *x, const void *w1, const void *w2, float *q
                        B, E, Eh, bps);
     tb_status e = check_launch("tb_predict_queries(mlp1)");
     if (e) return e;
-    hipLaunchKernelGGL(mlp2_kernel, dim3(n_out / 16, 1, bt), dim3(kThreads), 0, st, part,
+    hipLaunchKernelGGL(mlp2_kernel, dim3(n_out / 16, 1, bt), dim3(kThreads),
+                       (size_t)16 * Eh * sizeof(uint16_t), st, part,
                        static_cast<const uint16_t *>(w2), qhat, B, Eh, n_out, nsplit);
     return check_launch("tb_predict_queries(mlp2)");
 }

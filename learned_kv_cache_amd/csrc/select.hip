@@ -16,14 +16,17 @@
 //            scores; 4096-bin LDS histogram of the top 12 key bits, merged
 //            into a per-segment global histogram with atomics;
 //   classify same grid: find the boundary bin; tokens above it go straight
-//            into a selection bitmap (wave ballots), tokens in it are appended
-//            to a per-segment candidate list (wave-aggregated atomics);
-//   finalize one 1024-thread workgroup per segment: exact radix select of the
-//            remaining quota among the candidates (LDS when they fit), then
-//            OR sink / window / chosen candidates into 32768-token bitmap
-//            tiles and compact them with a block prefix sum into the
-//            ascending index list. It also returns the histogram and the
-//            candidate counter to zero for the next call.
+//            into a selection bitmap (wave ballots), tokens in it are gathered
+//            in LDS and appended to a per-segment candidate list with one
+//            atomic per workgroup;
+//   finalize one 1024-thread workgroup per segment: exact select of the
+//            remaining quota among the candidates (LDS when they fit): 10-bit
+//            radix passes narrow the boundary group until it holds at most 64
+//            keys, which are then ranked directly. Sink / window / chosen
+//            candidates are ORed into 32768-token bitmap tiles that a block
+//            prefix sum compacts into the ascending index list. It also
+//            returns the histogram and the candidate counter to zero for the
+//            next call.
 #include "tb_common.h"
 
 namespace tb {
@@ -37,8 +40,9 @@ constexpr int MAXR = 64;
 constexpr int T3 = 1024;             // threads of finalize
 constexpr int TILE_WORDS = T3;       // bitmap words per compaction tile
 constexpr int LDS_CAND = 8192;       // candidates held in LDS by finalize
-constexpr int RBITS = 11;            // radix digit of the exact select
+constexpr int RBITS = 10;            // radix digit of the exact select
 constexpr int RBINS = 1 << RBITS;
+constexpr int GMAX = 64;             // boundary group size ranked directly
 
 struct Region {
     int L, P, e0, e1, need;
@@ -60,12 +64,23 @@ __device__ __forceinline__ Region region(const int32_t *ctx, const int32_t *plen
 }
 
 // Stage order keys of scores for positions [lo, hi) (clipped to [e0, e1))
-// into LDS; slot i holds position lo + i.
+// into LDS; slot i holds position lo + i. All loads of a thread are issued
+// before any is consumed.
+template <int NT>
 __device__ __forceinline__ void stage_keys(uint32_t *sk, const float *s, int lo, int hi, int e0,
                                            int e1) {
-    for (int i = threadIdx.x; i < hi - lo; i += blockDim.x) {
+    constexpr int PER = (CHUNK + 2 * MAXR + NT - 1) / NT;
+    float v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int t = lo + (int)threadIdx.x + k * NT;
+        v[k] = (t < hi && t >= e0 && t < e1) ? s[t] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = (int)threadIdx.x + k * NT;
         const int t = lo + i;
-        sk[i] = (t >= e0 && t < e1) ? order_key(s[t]) : 0u;
+        if (t < hi) sk[i] = (t >= e0 && t < e1) ? order_key(v[k]) : 0u;
     }
 }
 
@@ -96,40 +111,70 @@ __device__ __forceinline__ int key_token(uint64_t key) {
     return (low & 1u) ? c - d : c + d;
 }
 
-// Boundary of the top `need` among a 4096-bin histogram (bin 4095 highest):
-// bin B1 with above(B1) < need <= above(B1) + hist[B1]; returns need1 =
-// need - above(B1). Block-wide; result in *bin / *need1 (LDS).
+// Inclusive prefix sum over the threads of the block (thread order). s_w
+// holds NT / 64 slots. Two barriers; s_w may be reused after return.
 template <int NT>
-__device__ void find_boundary(const uint32_t *hist, int need, int *s_bin, int *s_need,
-                              uint32_t *s_scan) {
-    constexpr int PER = NBINS / NT;
-    const int tid = threadIdx.x;
-    uint32_t local[PER];
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *s_w, uint32_t *total) {
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_w[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const uint32_t t = s_w[w];
+        before += w < wave ? t : 0u;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + x;
+}
+
+// Boundary of the top `need` among a 4096-bin histogram (bin 4095 highest):
+// bin B1 with above(B1) < need <= above(B1) + hist[B1]; need1 = need -
+// above(B1). Thread t owns the t-th group of PER bins counted from the top.
+// Block-wide; the result lands in *s_bin / *s_need (LDS, left unchanged when
+// the histogram holds fewer than `need` entries).
+template <int NT>
+struct HistSlice {
+    static constexpr int PER = NBINS / NT;
+    uint32_t v[PER];
+    // thread t owns the t-th group of PER bins counted from the top
+    __device__ __forceinline__ void load(const uint32_t *hist) {
+        const int top = NBINS - ((int)threadIdx.x + 1) * PER;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[i] = hist[top + i];
+    }
+};
+
+template <int NT>
+__device__ void find_boundary(const HistSlice<NT> &hs, int need, int *s_bin, int *s_need,
+                              uint32_t *s_w) {
+    constexpr int PER = HistSlice<NT>::PER;
+    const int top = NBINS - ((int)threadIdx.x + 1) * PER;
     uint32_t sum = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        local[i] = hist[tid * PER + i];
-        sum += local[i];
-    }
-    // inclusive suffix sum over threads: s_scan[tid] = sum of threads >= tid
-    s_scan[tid] = sum;
-    __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
-        const uint32_t v = tid + off < NT ? s_scan[tid + off] : 0u;
-        __syncthreads();
-        s_scan[tid] += v;
-        __syncthreads();
-    }
-    const uint32_t above = tid + 1 < NT ? s_scan[tid + 1] : 0u;
-    if (above < (uint32_t)need && (uint32_t)need <= s_scan[tid]) {
+    for (int i = 0; i < PER; ++i) sum += hs.v[i];
+    uint32_t total;
+    const uint32_t incl = block_incl_scan<NT>(sum, s_w, &total);
+    const uint32_t above = incl - sum;
+    if (above < (uint32_t)need && (uint32_t)need <= incl) {
         uint32_t acc = above;
+#pragma unroll
         for (int i = PER - 1; i >= 0; --i) {
-            if (acc + local[i] >= (uint32_t)need) {
-                *s_bin = tid * PER + i;
+            if (acc + hs.v[i] >= (uint32_t)need) {
+                *s_bin = top + i;
                 *s_need = need - (int)acc;
                 break;
             }
-            acc += local[i];
+            acc += hs.v[i];
         }
     }
     __syncthreads();
@@ -151,7 +196,7 @@ __global__ __launch_bounds__(T1) void hist_kernel(const float *__restrict__ scor
     if (a >= z) return;
     const int lo = a - r, hi = z + r;
     const float *s = scores + (size_t)seg * Lmax;
-    stage_keys(sk, s, lo, hi, g.e0, g.e1);
+    stage_keys<T1>(sk, s, lo, hi, g.e0, g.e1);
     for (int i = threadIdx.x; i < NBINS; i += T1) lh[i] = 0u;
     __syncthreads();
     for (int t = a + threadIdx.x; t < z; t += T1) {
@@ -170,8 +215,10 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     const uint32_t *__restrict__ ghist, uint32_t *__restrict__ ncand,
     uint64_t *__restrict__ cand, uint32_t *__restrict__ bitmap, int nwords) {
     __shared__ uint32_t sk[CHUNK + 2 * MAXR];
-    __shared__ uint32_t s_scan[T1];
+    __shared__ uint64_t s_cand[CHUNK];
+    __shared__ uint32_t s_w[T1 / 64];
     __shared__ int s_bin, s_need;
+    __shared__ uint32_t s_nc, s_off;
     const int seg = blockIdx.y, b = seg / Hq;
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
     const int c0 = blockIdx.x * CHUNK;
@@ -186,14 +233,17 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     int B1 = NBINS;
     const int lo = a - r, hi = z + r;
     if (touch) {
-        s_bin = NBINS;
-        s_need = 0;
-        find_boundary<T1>(ghist + (size_t)seg * NBINS, g.need, &s_bin, &s_need, s_scan);
+        if (threadIdx.x == 0) {
+            s_bin = NBINS;
+            s_need = 0;
+            s_nc = 0;
+        }
+        HistSlice<T1> hs;
+        hs.load(ghist + (size_t)seg * NBINS);
+        stage_keys<T1>(sk, scores + (size_t)seg * Lmax, lo, hi, g.e0, g.e1);
+        find_boundary<T1>(hs, g.need, &s_bin, &s_need, s_w);
         B1 = s_bin;
-        stage_keys(sk, scores + (size_t)seg * Lmax, lo, hi, g.e0, g.e1);
-        __syncthreads();
     }
-    uint64_t *cl = cand + (size_t)seg * Lmax;
     // every word of this chunk is written: 64 tokens per wave per step
     for (int base = c0 + wave * 64; base < c0 + CHUNK; base += T1) {
         if (base >= nwords * 32) break;
@@ -219,41 +269,25 @@ __global__ __launch_bounds__(T1) void classify_kernel(
         const uint64_t cm = __ballot(isc);
         if (cm) {
             uint32_t off = 0;
-            if (lane == 0) off = atomicAdd(&ncand[seg], (uint32_t)__popcll(cm));
+            if (lane == 0) off = atomicAdd(&s_nc, (uint32_t)__popcll(cm));
             off = __shfl(off, 0);
-            if (isc) {
-                const uint32_t rank = __popcll(cm & ((1ull << lane) - 1ull));
-                if (off + rank < (uint32_t)Lmax) cl[off + rank] = key;
-            }
+            if (isc) s_cand[off + __popcll(cm & ((1ull << lane) - 1ull))] = key;
         }
     }
+    if (!touch) return;
+    __syncthreads();
+    const uint32_t nc = s_nc;
+    if (nc == 0) return;
+    if (threadIdx.x == 0) s_off = atomicAdd(&ncand[seg], nc);
+    __syncthreads();
+    uint64_t *cl = cand + (size_t)seg * Lmax;
+    const uint32_t off = s_off;
+    for (uint32_t i = threadIdx.x; i < nc; i += T1)
+        if (off + i < (uint32_t)Lmax) cl[off + i] = s_cand[i];
 }
 
-__device__ __forceinline__ uint32_t block_excl_scan_1024(uint32_t v, uint32_t *s_w,
-                                                         uint32_t *total) {
-    // wave-level inclusive scan, then across the 16 waves
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) s_w[wave] = x;
-    __syncthreads();
-    if (threadIdx.x < 16) {
-        uint32_t w = s_w[threadIdx.x];
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const uint32_t y = __shfl_up(w, off, 16);
-            if (threadIdx.x >= off) w += y;
-        }
-        s_w[16 + threadIdx.x] = w;
-    }
-    __syncthreads();
-    const uint32_t before = wave ? s_w[16 + wave - 1] : 0u;
-    *total = s_w[31];
-    return before + x - v;
+__device__ __forceinline__ uint32_t bits_below(int n) {
+    return n <= 0 ? 0u : (n >= 32 ? 0xffffffffu : ((1u << n) - 1u));
 }
 
 __global__ __launch_bounds__(T3) void finalize_kernel(
@@ -262,13 +296,12 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
     const uint64_t *__restrict__ cand, const uint32_t *__restrict__ bitmap, int nwords,
     int32_t *__restrict__ idx, int32_t *__restrict__ count, int cap) {
     __shared__ uint64_t s_cand[LDS_CAND];
-    __shared__ uint32_t s_hist[RBINS];
     __shared__ uint32_t s_tile[TILE_WORDS];
-    __shared__ uint32_t s_scan[T3];
-    __shared__ uint32_t s_w[32];
-    __shared__ int s_bin, s_need;
+    __shared__ uint64_t s_grp[GMAX];
+    __shared__ uint32_t s_w[T3 / 64];
+    __shared__ int s_bin, s_need, s_cnt;
+    __shared__ uint32_t s_ng;
     __shared__ uint64_t s_thr;
-    __shared__ int s_found;
 
     const int seg = blockIdx.x, b = seg / Hq;
     const int tid = threadIdx.x;
@@ -282,64 +315,88 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
     int nc = 0;
     uint64_t thr = 0;  // candidates with key >= thr are chosen
     const uint64_t *cl = cand + (size_t)seg * Lmax;
+    bool lds = true;
     if (partial) {
-        s_bin = NBINS;
-        s_need = 0;
-        find_boundary<T3>(ghist + (size_t)seg * NBINS, g.need, &s_bin, &s_need, s_scan);
-        const int need1 = s_need;
+        if (tid == 0) {
+            s_bin = NBINS;
+            s_need = 0;
+        }
         nc = (int)ncand[seg];
+        HistSlice<T3> hs;
+        hs.load(ghist + (size_t)seg * NBINS);
         nc = nc < 0 ? 0 : (nc > Lmax ? Lmax : nc);
-        const bool lds = nc <= LDS_CAND;
-        if (lds)
-            for (int i = tid; i < nc; i += T3) s_cand[i] = cl[i];
-        __syncthreads();
-        if (need1 < nc) {
-            // exact select of the need1-th largest key among the candidates
+        lds = nc <= LDS_CAND;
+        if (lds) {
+            constexpr int PER = LDS_CAND / T3;
+            uint64_t v[PER];
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int i = tid + k * T3;
+                v[k] = i < nc ? cl[i] : 0ull;
+            }
+#pragma unroll
+            for (int k = 0; k < PER; ++k) {
+                const int i = tid + k * T3;
+                if (i < nc) s_cand[i] = v[k];
+            }
+        }
+        find_boundary<T3>(hs, g.need, &s_bin, &s_need, s_w);
+        int k = s_need;
+        if (k < nc) {
+            // the k-th largest key (all keys are distinct) among the candidates
             uint64_t prefix = (uint64_t)s_bin << (64 - HBITS);
             uint64_t mask = (uint64_t)(NBINS - 1) << (64 - HBITS);
-            int k = need1;
+            int grp = nc;
             int shift = 64 - HBITS;
-            bool done = false;
-            while (!done && shift > 0) {
+            while (grp > GMAX && shift > 0) {
                 const int width = shift < RBITS ? shift : RBITS;
                 shift -= width;
                 const uint32_t dmask = (1u << width) - 1u;
-                for (int i = tid; i < RBINS; i += T3) s_hist[i] = 0u;
+                // thread t counts digit (RBINS - 1 - t): thread order = descending digit
+                s_tile[tid] = 0u;
                 __syncthreads();
                 for (int i = tid; i < nc; i += T3) {
                     const uint64_t key = lds ? s_cand[i] : cl[i];
-                    if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & dmask], 1u);
+                    if ((key & mask) == prefix)
+                        atomicAdd(&s_tile[RBINS - 1 - (int)((key >> shift) & dmask)], 1u);
                 }
                 __syncthreads();
-                if (tid == 0) {
-                    uint32_t acc = 0;
-                    for (int d = (int)dmask; d >= 0; --d) {
-                        if (acc + s_hist[d] >= (uint32_t)k) {
-                            s_bin = d;
-                            s_need = k - (int)acc;
-                            s_found = (int)s_hist[d];
-                            break;
-                        }
-                        acc += s_hist[d];
-                    }
+                const uint32_t c = s_tile[tid];
+                uint32_t total;
+                const uint32_t incl = block_incl_scan<T3>(c, s_w, &total);
+                const uint32_t above = incl - c;
+                if (c > 0 && above < (uint32_t)k && (uint32_t)k <= incl) {
+                    s_bin = RBINS - 1 - tid;
+                    s_need = k - (int)above;
+                    s_cnt = (int)c;
                 }
                 __syncthreads();
                 prefix |= (uint64_t)s_bin << shift;
                 mask |= (uint64_t)dmask << shift;
                 k = s_need;
-                if (s_found == 1 && shift > 0) {
-                    // a single key carries this prefix: it is the threshold
-                    for (int i = tid; i < nc; i += T3) {
-                        const uint64_t key = lds ? s_cand[i] : cl[i];
-                        if ((key & mask) == prefix) s_thr = key;
-                    }
-                    __syncthreads();
-                    prefix = s_thr;
-                    done = true;
-                }
+                grp = s_cnt;
                 __syncthreads();
             }
-            thr = prefix;
+            // rank the (at most GMAX) keys that carry the prefix
+            if (tid == 0) s_ng = 0;
+            __syncthreads();
+            for (int i = tid; i < nc; i += T3) {
+                const uint64_t key = lds ? s_cand[i] : cl[i];
+                if ((key & mask) == prefix) {
+                    const uint32_t slot = atomicAdd(&s_ng, 1u);
+                    if (slot < (uint32_t)GMAX) s_grp[slot] = key;
+                }
+            }
+            __syncthreads();
+            const int ng = s_ng < (uint32_t)GMAX ? (int)s_ng : GMAX;
+            if (tid < ng) {
+                const uint64_t mine = s_grp[tid];
+                int rank = 0;
+                for (int j = 0; j < ng; ++j) rank += s_grp[j] > mine ? 1 : 0;
+                if (rank == k - 1) s_thr = mine;
+            }
+            __syncthreads();
+            thr = s_thr;
         }
         // leave the workspace zero-filled for the next call
         for (int i = tid; i < NBINS; i += T3) ghist[(size_t)seg * NBINS + i] = 0u;
@@ -351,7 +408,6 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
     const int nw = (L + 31) >> 5;
     const uint32_t *bm = bitmap + (size_t)seg * nwords;
     int32_t *dst = idx + (size_t)seg * cap;
-    const bool lds = nc <= LDS_CAND;
     const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
     const int slo = S < L ? S : L;
     uint32_t running = 0;
@@ -359,14 +415,11 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
         const int w = w0 + tid;
         uint32_t bits = 0;
         if (w < nw) {
-            bits = (g.need > 0) ? bm[w] : 0u;
             const int t0 = w << 5;
-            // sink [0, slo) and window [wlo, L) bits of this word
-            for (int j = 0; j < 32; ++j) {
-                const int t = t0 + j;
-                if (t < L && (t < slo || t >= wlo)) bits |= 1u << j;
-            }
-            if (t0 + 32 > L) bits &= (L - t0 >= 32) ? ~0u : ((1u << (L - t0)) - 1u);
+            bits = (g.need > 0) ? bm[w] : 0u;
+            bits |= bits_below(slo - t0);                                  // sink
+            bits |= bits_below(L - t0) & ~bits_below(wlo - t0);            // window
+            bits &= bits_below(L - t0);
         }
         s_tile[tid] = bits;
         __syncthreads();
@@ -383,8 +436,8 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
         }
         const uint32_t mine = s_tile[tid];
         uint32_t total;
-        const uint32_t off = block_excl_scan_1024((uint32_t)__popc(mine), s_w, &total);
-        uint32_t pos = running + off;
+        const uint32_t incl = block_incl_scan<T3>((uint32_t)__popc(mine), s_w, &total);
+        uint32_t pos = running + incl - (uint32_t)__popc(mine);
         uint32_t v = mine;
         while (v) {
             const int j = __ffs(v) - 1;
@@ -393,7 +446,6 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
             ++pos;
         }
         running += total;
-        __syncthreads();
     }
     if (tid == 0) count[seg] = (int32_t)running;
 }

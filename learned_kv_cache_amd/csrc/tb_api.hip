@@ -64,8 +64,9 @@ tb_status tb_predict_queries(const void *x, const void *w1, const void *w2, floa
                TB_ERR_INVALID_ARGUMENT, "tb_predict_queries: pointers must be 16-byte aligned");
     TB_REQUIRE(B >= 1 && B <= 64 && E > 0 && Eh > 0 && n_out > 0, TB_ERR_INVALID_ARGUMENT,
                "tb_predict_queries: bad sizes B=%d E=%d Eh=%d n_out=%d", B, E, Eh, n_out);
-    TB_REQUIRE(E % 128 == 0 && Eh % 128 == 0 && n_out % 16 == 0, TB_ERR_UNSUPPORTED_SHAPE,
-               "tb_predict_queries: need E %% 128 == 0, Eh %% 128 == 0, n_out %% 16 == 0");
+    TB_REQUIRE(E % 128 == 0 && Eh % 128 == 0 && n_out % 16 == 0 && Eh <= 1536,
+               TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_predict_queries: need E %% 128 == 0, Eh %% 128 == 0, Eh <= 1536, n_out %% 16 == 0");
     const size_t need = tb_predict_workspace_bytes(B, E, Eh, n_out);
     TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
                "tb_predict_queries: workspace %zu < %zu bytes", ws_bytes, need);
@@ -151,7 +152,7 @@ tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *
 // ---------------------------------------------------------------- attention
 size_t tb_attn_workspace_bytes(int B, int Hq, int cap, int window, int D) {
     if (B <= 0 || Hq <= 0 || cap <= 0 || window < 0 || D <= 0) return 0;
-    return tb::attn_ws_layout(B, Hq, cap + window, D, nullptr, nullptr, nullptr);
+    return tb::attn_ws_layout(B, Hq, cap + window, D, nullptr, nullptr);
 }
 
 tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *v_cache,
@@ -175,10 +176,9 @@ tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *
     TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
                "tb_sparse_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
     float *part;
-    uint32_t *ctr;
-    tb::attn_ws_layout(B, Hq, cap + win, D, workspace, &part, &ctr);
+    tb::attn_ws_layout(B, Hq, cap + win, D, workspace, &part);
     return tb::launch_attn(q, k_cache, v_cache, idx, count, cap, ctx_len, win, B, Hq, Hkv, Lmax,
-                           D, scale, out, part, ctr, static_cast<hipStream_t>(stream));
+                           D, scale, out, part, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

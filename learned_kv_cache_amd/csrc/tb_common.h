@@ -92,9 +92,9 @@ tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *
                         int32_t *idx, int32_t *count, int cap, const SelectWs &ws,
                         hipStream_t st);
 int attn_nsplit(int rows);
-size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr);
+size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part);
 tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32_t *idx,
                       const int32_t *count, int cap, const int32_t *ctx, int window, int B,
                       int Hq, int Hkv, int Lmax, int D, float scale, float *out, float *part,
-                      uint32_t *ctr, hipStream_t st);
+                      hipStream_t st);
 }  // namespace tb

@@ -48,7 +48,8 @@ def test_workspace_queries(tb):
     s = tb.tb_select_workspace_bytes(1, 32, 65536)
     assert s >= 32 * (4096 * 4 + 65536 * 8 + 65536 // 8)
     a = tb.tb_attn_workspace_bytes(1, 32, 8192, 0, 128)
-    assert a >= 32 * 32 * 130 * 4 + 32 * 4
+    assert a >= 32 * 32 * 130 * 4
+    assert tb.tb_attn_workspace_bytes(1, 32, 8192, 256, 128) > a
 
 
 FAKE = 0x10000          # aligned, never dereferenced: validation fails first
