@@ -157,7 +157,7 @@ tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *
  *           otherwise); count [B, Hq] int32 (clamped to [0, cap])
  *   ctx_len [B] int32, device, or NULL (ctx_len is clamped to [0, Lmax])
  *   out     [B, Hq, D]        fp32
- * Limits: D in {64, 128}; Hq % Hkv == 0; window >= 0.
+ * Limits: D in {64, 128}; Hq % Hkv == 0; window >= 0; Lmax * D * 2 < 2^31.
  * The workspace query takes the same window (pass 0 when ctx_len is NULL).
  */
 size_t tb_attn_workspace_bytes(int B, int Hq, int cap, int window, int D);

@@ -3,14 +3,21 @@
 // only the most relevant tokens).
 //
 // Split-K gather: a workgroup owns CH consecutive entries of one query head's
-// ascending index list. D/8 lanes share one K/V row (16 bytes = 8 channels per
-// lane), so a wave gathers 64/(D/8) rows per 16-byte load and keeps U rows of
-// K and V in flight per lane. Logits are reduced with DPP, the softmax runs
-// online in registers (base-2, fp32), and the workgroup writes one partial
-// (max, sum, o[D]). A second, small launch merges each head's partials by
-// log-sum-exp into the fp32 output; the kernel boundary is the only
-// synchronization between workgroups (no device-scope fences, which on this
-// chip would write back and invalidate the XCD's L2).
+// ascending index list, staged in LDS. D/8 lanes share one K/V row (16 bytes
+// = 8 channels per lane), so a wave gathers 64/(D/8) rows per 16-byte load;
+// each lane group requests all of its CH/16 (D = 128) K rows at once, then
+// all of its V rows into the same registers, so a workgroup waits on memory
+// twice and stays small enough for the whole grid to be resident. Logits are reduced with
+// DPP, the softmax is fp32 base-2 in registers, and the workgroup writes one partial
+// (max, sum, o[D]). The last workgroup of a head to arrive merges the
+// partials by log-sum-exp into the fp32 output.
+//
+// Cross-workgroup handoff without device-scope fences (on this chip a fence at
+// agent scope writes back, and on acquire invalidates, the XCD's whole L2):
+// wave 0 alone writes the partial with agent-scope atomic stores (coherent
+// across XCDs by themselves), waits for them to complete, then increments an
+// agent-scope arrival counter; the workgroup that sees the last arrival reads
+// every partial with agent-scope atomic loads and resets the counter.
 //
 // Launch order is XCD-aware: dispatch sends workgroup i to XCD i % 8, and the
 // block index is decoded so that each XCD receives a contiguous run of work
@@ -25,7 +32,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int CH = 256;  // index-list entries per workgroup
-constexpr int U = 4;     // rows in flight per row group per iteration
+// word 3 of a raw (untyped) buffer resource on gfx9-family parts
+constexpr int kRsrcWord3 = 0x00020000;
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_kernel(
@@ -33,15 +41,19 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     const uint16_t *__restrict__ vc, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ count, int cap, const int32_t *__restrict__ ctx, int window,
     int Hq, int Hkv, int Lmax, float scale_log2,
-    int nsplit, int n_items, float *__restrict__ part) {
+    int nsplit, int n_items, float *__restrict__ part, uint32_t *__restrict__ ctr,
+    float *__restrict__ out) {
     constexpr int LPR = D / 8;          // lanes per row
     constexpr int RPW = 64 / LPR;       // row groups per wave
     constexpr int NG = kWaves * RPW;    // row groups per workgroup
     constexpr int STRIDE = NG;          // rows per workgroup pass
+    constexpr int RPG = CH / NG;        // rows per row group
 
     __shared__ float sm_o[NG][D];
     __shared__ float sm_m[NG], sm_l[NG];
     __shared__ int sm_tok[CH];
+    __shared__ float sm_p[32 * (D + 2)];
+    __shared__ int sm_last;
 
     const int nb = gridDim.x;
     const int bid = blockIdx.x;
@@ -95,75 +107,75 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
             qf[2 * e + 1] = bf16_hi(w[e]) * scale_log2;
         }
     }
-    const size_t head_off = (size_t)(b * Hkv + kvh) * Lmax * D + cl * 8;
-    const uint16_t *kbase = kc + head_off;
-    const uint16_t *vbase = vc + head_off;
+    // buffer resources over this (b, kv head)'s K and V rows: 32-bit row
+    // offsets, and the hardware range check returns zeros past the head
+    const size_t head_off = (size_t)(b * Hkv + kvh) * Lmax * D;
+    const int head_bytes = Lmax * D * 2;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kc + head_off), (short)0, head_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vc + head_off), (short)0, head_bytes, kRsrcWord3);
+    const int lane_off = cl * 16;
 
     float m = -1e30f, l = 0.f;
     float acc[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = 0.f;
 
-    for (int r0 = lo + grp; r0 < hi; r0 += STRIDE * U) {
-        int tk[U];
-        bool ok[U];
+    // all K rows of this row group are requested at once; their registers are
+    // then reused for the V rows, which are requested as soon as the logits
+    // are formed
+    uint4 kv[RPG];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int r = r0 + u * STRIDE;
-            ok[u] = r < hi;
-            tk[u] = sm_tok[ok[u] ? r - lo : 0];
+    for (int u = 0; u < RPG; ++u) {
+        const int t = sm_tok[grp + u * STRIDE];
+        kv[u] = (lo + grp + u * STRIDE < hi)
+                    ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    krs, t * (D * 2) + lane_off, 0, 0))
+                    : make_uint4(0, 0, 0, 0);
+    }
+    float s[RPG];
+#pragma unroll
+    for (int u = 0; u < RPG; ++u) {
+        const uint32_t w[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            d = __builtin_fmaf(bf16_lo(w[e]), qf[2 * e], d);
+            d = __builtin_fmaf(bf16_hi(w[e]), qf[2 * e + 1], d);
         }
-        uint4 kr[U], vr[U];
+        s[u] = d;
+    }
+    // the logits are formed (and the K registers freed) before V is requested
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (ok[u]) {
-                kr[u] = *reinterpret_cast<const uint4 *>(kbase + (size_t)tk[u] * D);
-                vr[u] = *reinterpret_cast<const uint4 *>(vbase + (size_t)tk[u] * D);
-            } else {
-                kr[u] = make_uint4(0, 0, 0, 0);
-                vr[u] = make_uint4(0, 0, 0, 0);
-            }
+    for (int u = 0; u < RPG; ++u) asm volatile("" ::"v"(s[u]));
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < RPG; ++u) {
+        const int t = sm_tok[grp + u * STRIDE];
+        kv[u] = (lo + grp + u * STRIDE < hi)
+                    ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    vrs, t * (D * 2) + lane_off, 0, 0))
+                    : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < RPG; ++u) s[u] = group_sum<LPR>(s[u]);
+#pragma unroll
+    for (int u = 0; u < RPG; ++u)
+        if (lo + grp + u * STRIDE < hi) m = fmaxf(m, s[u]);
+#pragma unroll
+    for (int u = 0; u < RPG; ++u) {
+        const float p = (lo + grp + u * STRIDE < hi) ? exp2f(s[u] - m) : 0.f;
+        l += p;
+        const uint32_t w[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            acc[2 * e] = __builtin_fmaf(p, bf16_lo(w[e]), acc[2 * e]);
+            acc[2 * e + 1] = __builtin_fmaf(p, bf16_hi(w[e]), acc[2 * e + 1]);
         }
-        float s[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t w[4] = {kr[u].x, kr[u].y, kr[u].z, kr[u].w};
-            float d = 0.f;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                d = __builtin_fmaf(bf16_lo(w[e]), qf[2 * e], d);
-                d = __builtin_fmaf(bf16_hi(w[e]), qf[2 * e + 1], d);
-            }
-            s[u] = group_sum<LPR>(d);
-        }
-        float mx = m;
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (ok[u]) mx = fmaxf(mx, s[u]);
-        const float alpha = exp2f(m - mx);
-        float p[U];
-        float psum = 0.f;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            p[u] = ok[u] ? exp2f(s[u] - mx) : 0.f;
-            psum += p[u];
-        }
-        l = l * alpha + psum;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[c] *= alpha;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t w[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc[2 * e] = __builtin_fmaf(p[u], bf16_lo(w[e]), acc[2 * e]);
-                acc[2 * e + 1] = __builtin_fmaf(p[u], bf16_hi(w[e]), acc[2 * e + 1]);
-            }
-        }
-        m = mx;
     }
 
-    // merge the row groups of this workgroup into one partial
+    // merge the row groups of this workgroup into one partial (wave 0 only)
 #pragma unroll
     for (int c = 0; c < 8; ++c) sm_o[grp][cl * 8 + c] = acc[c];
     if (cl == 0) {
@@ -172,37 +184,45 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     }
     __syncthreads();
     float *pp = part + ((size_t)bh * nsplit + split) * (D + 2);
-    if (threadIdx.x < D) {
+    if (wave == 0) {
         float M = -1e30f;
 #pragma unroll
         for (int i = 0; i < NG; ++i) M = fmaxf(M, sm_m[i]);
-        float Ls = 0.f, O = 0.f;
+        float Ls = 0.f;
+        float O[D / 64];
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) O[j] = 0.f;
 #pragma unroll
         for (int i = 0; i < NG; ++i) {
             const float w = exp2f(sm_m[i] - M);
             Ls += sm_l[i] * w;
-            O += sm_o[i][threadIdx.x] * w;
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) O[j] += sm_o[i][lane + 64 * j] * w;
         }
-        pp[2 + threadIdx.x] = O;
-        if (threadIdx.x == 0) {
-            pp[0] = M;
-            pp[1] = Ls;
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j)
+            __hip_atomic_store(pp + 2 + lane + 64 * j, O[j], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+            __hip_atomic_store(pp, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pp + 1, Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // the partial's stores complete before the arrival is counted
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(ctr + bh, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            sm_last = prev == (uint32_t)(nsplit - 1);
         }
     }
-}
+    __syncthreads();
+    if (!sm_last) return;
 
-// One workgroup per (b, h): log-sum-exp merge of the split partials. Up to
-// 32 partials at a time are staged in LDS with independent loads, and the
-// running (max, sum, numerator) is rescaled from one stage to the next.
-template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restrict__ part,
-                                                           int nsplit, float *__restrict__ out) {
-    constexpr int CS = 32;
+    // last arrival: merge all partials of this head (32 at a time through LDS)
     constexpr int PW = D + 2;
-    __shared__ float sm[CS * PW];
-    const int bh = blockIdx.x;
+    constexpr int CS = 32;
+    constexpr int PER = (CS * PW + kThreads - 1) / kThreads;
     const float *base = part + (size_t)bh * nsplit * PW;
-    constexpr int PER = (CS * PW + 255) / 256;
     float M = -1e30f, den = 0.f, num = 0.f;
     for (int s0 = 0; s0 < nsplit; s0 += CS) {
         const int ns = nsplit - s0 < CS ? nsplit - s0 : CS;
@@ -210,47 +230,53 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
         float v[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int i = threadIdx.x + k * 256;
-            v[k] = i < ns * PW ? src[i] : 0.f;
+            const int i = threadIdx.x + k * kThreads;
+            v[k] = i < ns * PW ? __hip_atomic_load(src + i, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.f;
         }
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const int i = threadIdx.x + k * 256;
-            if (i < ns * PW) sm[i] = v[k];
+            const int i = threadIdx.x + k * kThreads;
+            if (i < ns * PW) sm_p[i] = v[k];
         }
         __syncthreads();
         float Mc = M;
-        for (int s = 0; s < ns; ++s) Mc = fmaxf(Mc, sm[s * PW]);
+        for (int s = 0; s < ns; ++s) Mc = fmaxf(Mc, sm_p[s * PW]);
         const float r = exp2f(M - Mc);
         den *= r;
         num *= r;
         for (int s = 0; s < ns; ++s) {
-            const float w = exp2f(sm[s * PW] - Mc);
-            den += sm[s * PW + 1] * w;
-            if (threadIdx.x < D) num += sm[s * PW + 2 + threadIdx.x] * w;
+            const float w = exp2f(sm_p[s * PW] - Mc);
+            den += sm_p[s * PW + 1] * w;
+            if (threadIdx.x < D) num += sm_p[s * PW + 2 + threadIdx.x] * w;
         }
         M = Mc;
     }
     if (threadIdx.x < D) out[(size_t)bh * D + threadIdx.x] = den > 0.f ? num / den : 0.f;
+    if (threadIdx.x == 0) __hip_atomic_store(ctr + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
 int attn_nsplit(int rows) { return (rows + CH - 1) / CH > 0 ? (rows + CH - 1) / CH : 1; }
 
-size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part) {
+size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr) {
     const size_t nbh = (size_t)B * Hq;
     size_t part_bytes = nbh * attn_nsplit(rows) * (D + 2) * sizeof(float);
     part_bytes = (part_bytes + 255) & ~(size_t)255;
-    if (base) *part = static_cast<float *>(base);
-    return part_bytes;
+    if (base) {
+        *part = static_cast<float *>(base);
+        *ctr = reinterpret_cast<uint32_t *>(static_cast<char *>(base) + part_bytes);
+    }
+    return part_bytes + nbh * sizeof(uint32_t);
 }
 
 tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32_t *idx,
                       const int32_t *count, int cap, const int32_t *ctx, int window, int B,
                       int Hq, int Hkv, int Lmax, int D, float scale, float *out, float *part,
-                      hipStream_t st) {
+                      uint32_t *ctr, hipStream_t st) {
     if (ctx == nullptr) window = 0;
     const int nsplit = attn_nsplit(cap + window);
     const long long items = (long long)B * Hq * nsplit;
@@ -266,20 +292,12 @@ tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32
     if (D == 128)
         hipLaunchKernelGGL(attn_kernel<128>, dim3((unsigned)nb), dim3(kThreads), 0, st, qq, kk, vv,
                            idx, count, cap, ctx, window, Hq, Hkv, Lmax, scale_log2, nsplit,
-                           (int)items, part);
+                           (int)items, part, ctr, out);
     else
         hipLaunchKernelGGL(attn_kernel<64>, dim3((unsigned)nb), dim3(kThreads), 0, st, qq, kk, vv,
                            idx, count, cap, ctx, window, Hq, Hkv, Lmax, scale_log2, nsplit,
-                           (int)items, part);
-    tb_status e = check_launch("tb_sparse_decode_attn(split)");
-    if (e) return e;
-    if (D == 128)
-        hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(B * Hq), dim3(256), 0, st, part, nsplit,
-                           out);
-    else
-        hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(B * Hq), dim3(256), 0, st, part, nsplit,
-                           out);
-    return check_launch("tb_sparse_decode_attn(combine)");
+                           (int)items, part, ctr, out);
+    return check_launch("tb_sparse_decode_attn");
 }
 
 }  // namespace tb

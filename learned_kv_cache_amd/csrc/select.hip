@@ -11,22 +11,22 @@
 // position on ties). The greedy order is exactly descending key order, the
 // keys are distinct, and the important buffer is the min(K, |E|) largest keys.
 //
-// Three launches, all integer work:
-//   hist     per (segment, 4096-token chunk): pooled keys from LDS-staged
-//            scores; 4096-bin LDS histogram of the top 12 key bits, merged
-//            into a per-segment global histogram with atomics;
-//   classify same grid: find the boundary bin; tokens above it go straight
-//            into a selection bitmap (wave ballots), tokens in it are gathered
-//            in LDS and appended to a per-segment candidate list with one
-//            atomic per workgroup;
-//   finalize one 1024-thread workgroup per segment: exact select of the
-//            remaining quota among the candidates (LDS when they fit): 10-bit
-//            radix passes narrow the boundary group until it holds at most 64
-//            keys, which are then ranked directly. Sink / window / chosen
-//            candidates are ORed into 32768-token bitmap tiles that a block
-//            prefix sum compacts into the ascending index list. It also
-//            returns the histogram and the candidate counter to zero for the
-//            next call.
+// Four launches, all integer work:
+//   hist     per (segment, 2048-token chunk): pooled keys from LDS-staged
+//            scores; 4096-bin LDS histogram of the top 12 key bits (runs of
+//            equal bins in neighbouring lanes are added once), merged into a
+//            per-segment global histogram with atomics;
+//   boundary one workgroup per segment finds the boundary bin once and
+//            returns the histogram to zero;
+//   classify same grid: tokens above the boundary bin go straight into a
+//            selection bitmap (wave ballots); tokens in it are gathered in LDS
+//            and written to the chunk's own slots of the candidate list;
+//   finalize one 1024-thread workgroup per segment: gathers the chunks'
+//            candidates, exact select of the remaining quota among them (10-bit
+//            radix passes narrow the boundary group to at most 64 keys, which
+//            are ranked directly). Sink / window / chosen candidates are ORed
+//            into 32768-token bitmap tiles that a block prefix sum compacts
+//            into the ascending index list.
 #include "tb_common.h"
 
 namespace tb {
@@ -34,7 +34,7 @@ namespace {
 
 constexpr int HBITS = 12;
 constexpr int NBINS = 1 << HBITS;
-constexpr int CHUNK = 4096;          // tokens per hist/classify workgroup
+constexpr int CHUNK = 2048;          // tokens per hist/classify workgroup
 constexpr int T1 = 256;              // threads of hist/classify
 constexpr int MAXR = 64;
 constexpr int T3 = 1024;             // threads of finalize
@@ -43,6 +43,8 @@ constexpr int LDS_CAND = 8192;       // candidates held in LDS by finalize
 constexpr int RBITS = 10;            // radix digit of the exact select
 constexpr int RBINS = 1 << RBITS;
 constexpr int GMAX = 64;             // boundary group size ranked directly
+constexpr int PRE_TILES = 8;         // bitmap tiles prefetched (262144 tokens)
+constexpr int MAX_CHUNKS = (1 << 24) / CHUNK;   // chunks of the largest Lmax
 
 struct Region {
     int L, P, e0, e1, need;
@@ -199,9 +201,21 @@ __global__ __launch_bounds__(T1) void hist_kernel(const float *__restrict__ scor
     stage_keys<T1>(sk, s, lo, hi, g.e0, g.e1);
     for (int i = threadIdx.x; i < NBINS; i += T1) lh[i] = 0u;
     __syncthreads();
-    for (int t = a + threadIdx.x; t < z; t += T1) {
-        const uint64_t k = pooled_key(sk, lo, t, g.e0, g.e1, r);
-        atomicAdd(&lh[(uint32_t)(k >> (64 - HBITS))], 1u);
+    const int lane = threadIdx.x & 63;
+    for (int base = a + (int)(threadIdx.x & ~63); base < z; base += T1) {
+        const int t = base + lane;
+        const bool valid = t < z;
+        const uint32_t bin = valid ? (uint32_t)(pooled_key(sk, lo, t, g.e0, g.e1, r) >> (64 - HBITS))
+                                   : 0xffffffffu;
+        // valid lanes are a prefix of the wave; add each run of equal bins once
+        const uint32_t prev = __shfl_up(bin, 1);
+        const bool start = valid && (lane == 0 || prev != bin);
+        const uint64_t edges = __ballot(start || !valid);
+        if (start) {
+            const uint64_t after = lane == 63 ? 0ull : edges & (~0ull << (lane + 1));
+            const int end = after ? __ffsll((long long)after) - 1 : 64;
+            atomicAdd(&lh[bin], (uint32_t)(end - lane));
+        }
     }
     __syncthreads();
     uint32_t *gh = ghist + (size_t)seg * NBINS;
@@ -209,16 +223,43 @@ __global__ __launch_bounds__(T1) void hist_kernel(const float *__restrict__ scor
         if (lh[i]) atomicAdd(&gh[i], lh[i]);
 }
 
+// One workgroup per segment: the boundary bin of the complete histogram
+// (written to info), then the histogram is returned to zero for the next call.
+__global__ __launch_bounds__(T1) void boundary_kernel(const int32_t *__restrict__ ctx,
+                                                      const int32_t *__restrict__ plen, int Hq,
+                                                      int Lmax, int S, int W, int K,
+                                                      uint32_t *__restrict__ ghist,
+                                                      int32_t *__restrict__ info) {
+    __shared__ uint32_t s_w[T1 / 64];
+    __shared__ int s_bin, s_need;
+    const int seg = blockIdx.x, b = seg / Hq;
+    const Region g = region(ctx, plen, b, Lmax, S, W, K);
+    if (g.bad || g.need == 0 || g.need == g.e1 - g.e0) return;
+    uint32_t *gh = ghist + (size_t)seg * NBINS;
+    HistSlice<T1> hs;
+    hs.load(gh);
+    if (threadIdx.x == 0) {
+        s_bin = NBINS;
+        s_need = 0;
+    }
+    find_boundary<T1>(hs, g.need, &s_bin, &s_need, s_w);
+    if (threadIdx.x == 0) {
+        info[2 * seg] = s_bin;
+        info[2 * seg + 1] = s_need;
+    }
+    const int top = NBINS - ((int)threadIdx.x + 1) * HistSlice<T1>::PER;
+#pragma unroll
+    for (int i = 0; i < HistSlice<T1>::PER; ++i) gh[top + i] = 0u;
+}
+
 __global__ __launch_bounds__(T1) void classify_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx,
     const int32_t *__restrict__ plen, int Hq, int Lmax, int S, int W, int K, int r,
-    const uint32_t *__restrict__ ghist, uint32_t *__restrict__ ncand,
+    const int32_t *__restrict__ info, uint32_t *__restrict__ ccount, int nchunks,
     uint64_t *__restrict__ cand, uint32_t *__restrict__ bitmap, int nwords) {
     __shared__ uint32_t sk[CHUNK + 2 * MAXR];
     __shared__ uint64_t s_cand[CHUNK];
-    __shared__ uint32_t s_w[T1 / 64];
-    __shared__ int s_bin, s_need;
-    __shared__ uint32_t s_nc, s_off;
+    __shared__ uint32_t s_nc;
     const int seg = blockIdx.y, b = seg / Hq;
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
     const int c0 = blockIdx.x * CHUNK;
@@ -230,20 +271,14 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     const int a = c0 > g.e0 ? c0 : g.e0;
     const int z = c0 + CHUNK < g.e1 ? c0 + CHUNK : g.e1;
     const bool touch = partial && a < z;
-    int B1 = NBINS;
     const int lo = a - r, hi = z + r;
+    int B1 = NBINS;
+    if (threadIdx.x == 0) s_nc = 0;
     if (touch) {
-        if (threadIdx.x == 0) {
-            s_bin = NBINS;
-            s_need = 0;
-            s_nc = 0;
-        }
-        HistSlice<T1> hs;
-        hs.load(ghist + (size_t)seg * NBINS);
+        B1 = info[2 * seg];
         stage_keys<T1>(sk, scores + (size_t)seg * Lmax, lo, hi, g.e0, g.e1);
-        find_boundary<T1>(hs, g.need, &s_bin, &s_need, s_w);
-        B1 = s_bin;
     }
+    __syncthreads();
     // every word of this chunk is written: 64 tokens per wave per step
     for (int base = c0 + wave * 64; base < c0 + CHUNK; base += T1) {
         if (base >= nwords * 32) break;
@@ -274,28 +309,55 @@ __global__ __launch_bounds__(T1) void classify_kernel(
             if (isc) s_cand[off + __popcll(cm & ((1ull << lane) - 1ull))] = key;
         }
     }
-    if (!touch) return;
     __syncthreads();
     const uint32_t nc = s_nc;
-    if (nc == 0) return;
-    if (threadIdx.x == 0) s_off = atomicAdd(&ncand[seg], nc);
-    __syncthreads();
-    uint64_t *cl = cand + (size_t)seg * Lmax;
-    const uint32_t off = s_off;
+    if (threadIdx.x == 0 && (int)blockIdx.x < nchunks) ccount[(size_t)seg * nchunks + blockIdx.x] = nc;
+    // the chunk owns candidate slots [c0, c0 + CHUNK) of its segment
+    uint64_t *cl = cand + (size_t)seg * Lmax + c0;
     for (uint32_t i = threadIdx.x; i < nc; i += T1)
-        if (off + i < (uint32_t)Lmax) cl[off + i] = s_cand[i];
+        if (c0 + (int)i < Lmax) cl[i] = s_cand[i];
+}
+
+// Position of the k-th (0-based) set bit of v; requires k < popcount(v).
+__device__ __forceinline__ int select_bit(uint32_t v, uint32_t k) {
+    int pos = 0;
+    uint32_t c = (uint32_t)__popc(v & 0xffffu);
+    if (k >= c) { k -= c; pos += 16; v >>= 16; }
+    c = (uint32_t)__popc(v & 0xffu);
+    if (k >= c) { k -= c; pos += 8; v >>= 8; }
+    c = (uint32_t)__popc(v & 0xfu);
+    if (k >= c) { k -= c; pos += 4; v >>= 4; }
+    c = (uint32_t)__popc(v & 0x3u);
+    if (k >= c) { k -= c; pos += 2; v >>= 2; }
+    if (k >= (v & 1u)) pos += 1;
+    return pos;
 }
 
 __device__ __forceinline__ uint32_t bits_below(int n) {
     return n <= 0 ? 0u : (n >= 32 ? 0xffffffffu : ((1u << n) - 1u));
 }
 
+// Candidate i of the segment (chunk-major order): chunk c holds entries
+// [off[c], off[c+1]) in its slots starting at c * CHUNK.
+__device__ __forceinline__ uint64_t cand_at(const uint64_t *cl, const uint32_t *s_off, int nchunks,
+                                            uint32_t i) {
+    int lo = 0, hi = nchunks - 1;   // last chunk with off[c] <= i
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= i) lo = mid;
+        else hi = mid - 1;
+    }
+    return cl[(size_t)lo * CHUNK + (i - s_off[lo])];
+}
+
 __global__ __launch_bounds__(T3) void finalize_kernel(
     const int32_t *__restrict__ ctx, const int32_t *__restrict__ plen, int Hq, int Lmax, int S,
-    int W, int K, int omit_window, uint32_t *__restrict__ ghist, uint32_t *__restrict__ ncand,
-    const uint64_t *__restrict__ cand, const uint32_t *__restrict__ bitmap, int nwords,
-    int32_t *__restrict__ idx, int32_t *__restrict__ count, int cap) {
+    int W, int K, int omit_window, const int32_t *__restrict__ info,
+    const uint32_t *__restrict__ ccount, int nchunks, const uint64_t *__restrict__ cand,
+    const uint32_t *__restrict__ bitmap, int nwords, int32_t *__restrict__ idx,
+    int32_t *__restrict__ count, int cap) {
     __shared__ uint64_t s_cand[LDS_CAND];
+    __shared__ uint32_t s_off[MAX_CHUNKS];
     __shared__ uint32_t s_tile[TILE_WORDS];
     __shared__ uint64_t s_grp[GMAX];
     __shared__ uint32_t s_w[T3 / 64];
@@ -312,39 +374,66 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
     }
     const int nE = g.e1 - g.e0;
     const bool partial = g.need > 0 && g.need < nE;
+    // bitmap words of the first tiles, requested before anything else
+    const int L = g.L;
+    const int nw = (L + 31) >> 5;
+    const uint32_t *bm = bitmap + (size_t)seg * nwords;
+    uint32_t pre[PRE_TILES];
+#pragma unroll
+    for (int k = 0; k < PRE_TILES; ++k) {
+        const int w = k * TILE_WORDS + tid;
+        pre[k] = (g.need > 0 && w < nw) ? bm[w] : 0u;
+    }
     int nc = 0;
     uint64_t thr = 0;  // candidates with key >= thr are chosen
     const uint64_t *cl = cand + (size_t)seg * Lmax;
     bool lds = true;
     if (partial) {
-        if (tid == 0) {
-            s_bin = NBINS;
-            s_need = 0;
+        const int B1 = info[2 * seg];
+        int k = info[2 * seg + 1];
+        // per-chunk candidate counts -> chunk offsets (block scan)
+        constexpr int PC = MAX_CHUNKS / T3;
+        uint32_t cc[PC];
+        uint32_t csum = 0;
+#pragma unroll
+        for (int j = 0; j < PC; ++j) {
+            const int c = tid * PC + j;
+            cc[j] = c < nchunks ? ccount[(size_t)seg * nchunks + c] : 0u;
+            csum += cc[j];
         }
-        nc = (int)ncand[seg];
-        HistSlice<T3> hs;
-        hs.load(ghist + (size_t)seg * NBINS);
-        nc = nc < 0 ? 0 : (nc > Lmax ? Lmax : nc);
+        // the prefetched bitmap words are materialized here, overlapped with
+        // the loads above
+#pragma unroll
+        for (int j = 0; j < PRE_TILES; ++j) asm volatile("" ::"v"(pre[j]));
+        uint32_t total;
+        uint32_t run = block_incl_scan<T3>(csum, s_w, &total) - csum;
+#pragma unroll
+        for (int j = 0; j < PC; ++j) {
+            const int c = tid * PC + j;
+            if (c < nchunks) s_off[c] = run;
+            run += cc[j];
+        }
+        nc = (int)total;
         lds = nc <= LDS_CAND;
+        __syncthreads();
         if (lds) {
             constexpr int PER = LDS_CAND / T3;
             uint64_t v[PER];
 #pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int i = tid + k * T3;
-                v[k] = i < nc ? cl[i] : 0ull;
+            for (int j = 0; j < PER; ++j) {
+                const int i = tid + j * T3;
+                v[j] = i < nc ? cand_at(cl, s_off, nchunks, (uint32_t)i) : 0ull;
             }
 #pragma unroll
-            for (int k = 0; k < PER; ++k) {
-                const int i = tid + k * T3;
-                if (i < nc) s_cand[i] = v[k];
+            for (int j = 0; j < PER; ++j) {
+                const int i = tid + j * T3;
+                if (i < nc) s_cand[i] = v[j];
             }
+            __syncthreads();
         }
-        find_boundary<T3>(hs, g.need, &s_bin, &s_need, s_w);
-        int k = s_need;
         if (k < nc) {
             // the k-th largest key (all keys are distinct) among the candidates
-            uint64_t prefix = (uint64_t)s_bin << (64 - HBITS);
+            uint64_t prefix = (uint64_t)B1 << (64 - HBITS);
             uint64_t mask = (uint64_t)(NBINS - 1) << (64 - HBITS);
             int grp = nc;
             int shift = 64 - HBITS;
@@ -356,14 +445,14 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
                 s_tile[tid] = 0u;
                 __syncthreads();
                 for (int i = tid; i < nc; i += T3) {
-                    const uint64_t key = lds ? s_cand[i] : cl[i];
+                    const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
                     if ((key & mask) == prefix)
                         atomicAdd(&s_tile[RBINS - 1 - (int)((key >> shift) & dmask)], 1u);
                 }
                 __syncthreads();
                 const uint32_t c = s_tile[tid];
-                uint32_t total;
-                const uint32_t incl = block_incl_scan<T3>(c, s_w, &total);
+                uint32_t tot;
+                const uint32_t incl = block_incl_scan<T3>(c, s_w, &tot);
                 const uint32_t above = incl - c;
                 if (c > 0 && above < (uint32_t)k && (uint32_t)k <= incl) {
                     s_bin = RBINS - 1 - tid;
@@ -381,7 +470,7 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
             if (tid == 0) s_ng = 0;
             __syncthreads();
             for (int i = tid; i < nc; i += T3) {
-                const uint64_t key = lds ? s_cand[i] : cl[i];
+                const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
                 if ((key & mask) == prefix) {
                     const uint32_t slot = atomicAdd(&s_ng, 1u);
                     if (slot < (uint32_t)GMAX) s_grp[slot] = key;
@@ -398,15 +487,9 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
             __syncthreads();
             thr = s_thr;
         }
-        // leave the workspace zero-filled for the next call
-        for (int i = tid; i < NBINS; i += T3) ghist[(size_t)seg * NBINS + i] = 0u;
-        if (tid == 0) ncand[seg] = 0u;
     }
 
     // compaction of sink | window | above-boundary bits | chosen candidates
-    const int L = g.L;
-    const int nw = (L + 31) >> 5;
-    const uint32_t *bm = bitmap + (size_t)seg * nwords;
     int32_t *dst = idx + (size_t)seg * cap;
     const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
     const int slo = S < L ? S : L;
@@ -416,7 +499,11 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
         uint32_t bits = 0;
         if (w < nw) {
             const int t0 = w << 5;
-            bits = (g.need > 0) ? bm[w] : 0u;
+            const int tile = w0 / TILE_WORDS;
+            uint32_t pb = 0;
+#pragma unroll
+            for (int j = 0; j < PRE_TILES; ++j) pb = tile == j ? pre[j] : pb;
+            bits = (g.need > 0) ? (tile < PRE_TILES ? pb : bm[w]) : 0u;
             bits |= bits_below(slo - t0);                                  // sink
             bits |= bits_below(L - t0) & ~bits_below(wlo - t0);            // window
             bits &= bits_below(L - t0);
@@ -426,7 +513,7 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
         if (partial) {
             const int tlo = w0 << 5, thi = (w0 + TILE_WORDS) << 5;
             for (int i = tid; i < nc; i += T3) {
-                const uint64_t key = lds ? s_cand[i] : cl[i];
+                const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
                 if (key >= thr) {
                     const int t = key_token(key);
                     if (t >= tlo && t < thi) atomicOr(&s_tile[(t - tlo) >> 5], 1u << (t & 31));
@@ -437,13 +524,27 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
         const uint32_t mine = s_tile[tid];
         uint32_t total;
         const uint32_t incl = block_incl_scan<T3>((uint32_t)__popc(mine), s_w, &total);
-        uint32_t pos = running + incl - (uint32_t)__popc(mine);
-        uint32_t v = mine;
-        while (v) {
-            const int j = __ffs(v) - 1;
-            v &= v - 1;
-            if (pos < (uint32_t)cap) dst[pos] = ((w0 + tid) << 5) + j;
-            ++pos;
+        const uint32_t pop = (uint32_t)__popc(mine);
+        const uint32_t first = incl - pop;   // list position of this word's first entry
+        // each wave emits its 64 words' positions 64 at a time: lane l takes
+        // output slot s, finds the owning word by binary search over the
+        // wave's prefix counts, and picks the bit; stores are coalesced
+        const int lane = tid & 63;
+        const uint32_t wfirst = __shfl(first, 0);
+        const uint32_t wend = __shfl(first + pop, 63);
+        for (uint32_t s0 = wfirst; s0 < wend; s0 += 64) {
+            const uint32_t sl = s0 + (uint32_t)lane;
+            int lo2 = 0;
+#pragma unroll
+            for (int step = 32; step >= 1; step >>= 1) {
+                const uint32_t f = __shfl(first, lo2 + step);
+                if (f <= sl) lo2 += step;
+            }
+            const uint32_t wbits = __shfl(mine, lo2);
+            const uint32_t k = sl - __shfl(first, lo2);
+            const uint32_t p = running + sl;
+            if (sl < wend && p < (uint32_t)cap)
+                dst[p] = ((w0 + (tid & ~63) + lo2) << 5) + select_bit(wbits, k);
         }
         running += total;
     }
@@ -455,20 +556,28 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
 size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
     const size_t nseg = (size_t)B * Hq;
     const int nwords = (Lmax + 31) / 32 + 1;
+    const int nchunks = (Lmax + CHUNK - 1) / CHUNK;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t hist_b = up(nseg * NBINS * 4);
-    const size_t nc_b = up(nseg * 4);
+    const size_t info_b = up(nseg * 8);
+    const size_t cc_b = up(nseg * (size_t)nchunks * 4);
     const size_t bm_b = up(nseg * (size_t)nwords * 4);
     const size_t cand_b = up(nseg * (size_t)Lmax * 8);
     if (base && out) {
         char *p = static_cast<char *>(base);
         out->hist = reinterpret_cast<uint32_t *>(p);
-        out->ncand = reinterpret_cast<uint32_t *>(p + hist_b);
-        out->bitmap = reinterpret_cast<uint32_t *>(p + hist_b + nc_b);
-        out->cand = reinterpret_cast<uint64_t *>(p + hist_b + nc_b + bm_b);
+        p += hist_b;
+        out->info = reinterpret_cast<int32_t *>(p);
+        p += info_b;
+        out->ccount = reinterpret_cast<uint32_t *>(p);
+        p += cc_b;
+        out->bitmap = reinterpret_cast<uint32_t *>(p);
+        p += bm_b;
+        out->cand = reinterpret_cast<uint64_t *>(p);
         out->nwords = nwords;
+        out->nchunks = nchunks;
     }
-    return hist_b + nc_b + bm_b + cand_b;
+    return hist_b + info_b + cc_b + bm_b + cand_b;
 }
 
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
@@ -476,17 +585,22 @@ tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *
                         int32_t *idx, int32_t *count, int cap, const SelectWs &ws,
                         hipStream_t st) {
     const int nseg = B * Hq;
-    dim3 grid((Lmax + CHUNK - 1) / CHUNK, nseg);
+    dim3 grid(ws.nchunks, nseg);
     hipLaunchKernelGGL(hist_kernel, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W, K,
                        r, ws.hist);
     tb_status e = check_launch("tb_select(hist)");
     if (e) return e;
+    hipLaunchKernelGGL(boundary_kernel, dim3(nseg), dim3(T1), 0, st, ctx, plen, Hq, Lmax, S, W, K,
+                       ws.hist, ws.info);
+    e = check_launch("tb_select(boundary)");
+    if (e) return e;
     hipLaunchKernelGGL(classify_kernel, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
-                       K, r, ws.hist, ws.ncand, ws.cand, ws.bitmap, ws.nwords);
+                       K, r, ws.info, ws.ccount, ws.nchunks, ws.cand, ws.bitmap, ws.nwords);
     e = check_launch("tb_select(classify)");
     if (e) return e;
     hipLaunchKernelGGL(finalize_kernel, dim3(nseg), dim3(T3), 0, st, ctx, plen, Hq, Lmax, S, W, K,
-                       omit_window ? 1 : 0, ws.hist, ws.ncand, ws.cand, ws.bitmap, ws.nwords, idx, count, cap);
+                       omit_window ? 1 : 0, ws.info, ws.ccount, ws.nchunks, ws.cand, ws.bitmap,
+                       ws.nwords, idx, count, cap);
     return check_launch("tb_select(finalize)");
 }
 

@@ -152,7 +152,7 @@ tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *
 // ---------------------------------------------------------------- attention
 size_t tb_attn_workspace_bytes(int B, int Hq, int cap, int window, int D) {
     if (B <= 0 || Hq <= 0 || cap <= 0 || window < 0 || D <= 0) return 0;
-    return tb::attn_ws_layout(B, Hq, cap + window, D, nullptr, nullptr);
+    return tb::attn_ws_layout(B, Hq, cap + window, D, nullptr, nullptr, nullptr);
 }
 
 tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *v_cache,
@@ -170,15 +170,18 @@ tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *
     TB_REQUIRE(Hq % Hkv == 0, TB_ERR_INVALID_ARGUMENT, "tb_sparse_decode_attn: Hq %% Hkv != 0");
     TB_REQUIRE(D == 64 || D == 128, TB_ERR_UNSUPPORTED_SHAPE,
                "tb_sparse_decode_attn: D must be 64 or 128");
+    TB_REQUIRE((long long)Lmax * D * 2 <= 0x7fffffffLL, TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_sparse_decode_attn: one head's cache must be below 2 GiB (Lmax * D * 2)");
     TB_REQUIRE(scale == scale, TB_ERR_INVALID_ARGUMENT, "tb_sparse_decode_attn: scale is NaN");
     const int win = ctx_len ? window : 0;
     const size_t need = tb_attn_workspace_bytes(B, Hq, cap, win, D);
     TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
                "tb_sparse_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
     float *part;
-    tb::attn_ws_layout(B, Hq, cap + win, D, workspace, &part);
+    uint32_t *ctr;
+    tb::attn_ws_layout(B, Hq, cap + win, D, workspace, &part, &ctr);
     return tb::launch_attn(q, k_cache, v_cache, idx, count, cap, ctx_len, win, B, Hq, Hkv, Lmax,
-                           D, scale, out, part, static_cast<hipStream_t>(stream));
+                           D, scale, out, part, ctr, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

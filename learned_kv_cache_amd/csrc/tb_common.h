@@ -81,10 +81,12 @@ tb_status launch_score(const float *qhat, int n_slots, int slot, const void *kp,
                        int dp, hipStream_t st);
 struct SelectWs {
     uint32_t *hist;      // [nseg][4096], zero at rest
-    uint32_t *ncand;     // [nseg], zero at rest
+    int32_t *info;       // [nseg][2] boundary bin, quota inside it
+    uint32_t *ccount;    // [nseg][nchunks] candidates per chunk
     uint32_t *bitmap;    // [nseg][nwords]
-    uint64_t *cand;      // [nseg][Lmax]
+    uint64_t *cand;      // [nseg][Lmax], chunk c owns slots [c * CHUNK, ...)
     int nwords;
+    int nchunks;
 };
 size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out);
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
@@ -92,9 +94,9 @@ tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *
                         int32_t *idx, int32_t *count, int cap, const SelectWs &ws,
                         hipStream_t st);
 int attn_nsplit(int rows);
-size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part);
+size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr);
 tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32_t *idx,
                       const int32_t *count, int cap, const int32_t *ctx, int window, int B,
                       int Hq, int Hkv, int Lmax, int D, float scale, float *out, float *part,
-                      hipStream_t st);
+                      uint32_t *ctr, hipStream_t st);
 }  // namespace tb

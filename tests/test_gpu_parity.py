@@ -233,3 +233,38 @@ def test_attention_dense_equals_full_budget(tb, orc):
     qq = torch.from_numpy(bits_to_f32_bf16(q)).double()[:, :, None]
     dense = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv)[:, :, 0].numpy()
     assert_attn_close(host(out), dense, "dense")
+
+
+def test_attention_repeatable_bitwise_at_c2_shape(tb, orc):
+    """The split partials are handed between workgroups through agent-scope
+    atomics and an arrival counter; repeated launches must give bitwise
+    identical outputs (the merge order is fixed), and match the oracle."""
+    say("attn repeat c2 shape")
+    rng = rng_for(60)
+    B, Hq, Hkv, L, D, cap = 1, 32, 8, 65536, 128, 8192
+    q = normal_bf16(rng, (B, Hq, D))
+    kc = normal_bf16(rng, (B, Hkv, L, D))
+    vc = normal_bf16(rng, (B, Hkv, L, D))
+    idx = np.zeros((B, Hq, cap), np.int32)
+    for h in range(Hq):
+        idx[0, h] = np.sort(rng.choice(L, cap, replace=False))
+    cnt = np.full((B, Hq), cap, np.int32)
+    cnt[0, 5] = 1000
+    ref = orc.sparse_attention(q, kc, vc, idx, cnt)
+    dq, dk, dv = dev(q, torch.bfloat16), dev(kc, torch.bfloat16), dev(vc, torch.bfloat16)
+    di, dc = dev32(idx), dev32(cnt)
+    ws = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, 0, D))
+    outs = []
+    for rep in range(20):
+        out = torch.full((B, Hq, D), float("nan"), device="cuda")
+        tb.tb_sparse_decode_attn(dq, dk, dv, di, dc, out, ws)
+        outs.append(out)
+    torch.cuda.synchronize()
+    first = host(outs[0])
+    assert_attn_close(first, ref, "attn c2 shape")
+    for rep, o in enumerate(outs[1:], 1):
+        assert np.array_equal(host(o).view(np.uint32), first.view(np.uint32)), rep
+    # the arrival counters are back to zero
+    nsplit = (cap + 255) // 256
+    ctr_off = (B * Hq * nsplit * (D + 2) * 4 + 255) // 256 * 256
+    assert int(ws[ctr_off:ctr_off + B * Hq * 4].count_nonzero()) == 0
