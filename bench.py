@@ -93,6 +93,145 @@ def cpu_baseline(inp, cfg, seconds):
                       "%.1f s" % (n, el)}
 
 
+def run_interval(cfg, args):
+    """Prediction-interval pipeline over all layers of a multi-layer workload:
+    once per interval, project the pending N_p tokens of every layer, run every
+    producer's predictor, score and select every consumer layer (the window
+    left out of the list); then I decode steps, each appending one token per
+    sequence and running sparse attention on every layer with the sliding
+    window. steps/s = I / interval time. The caches are generated on the GPU
+    (torch.randn, bf16): they are far larger than the 256 MiB MALL."""
+    import torch
+    import learned_kv_cache_amd as tb
+    from synthetic import rng_for
+    from synthetic.workload import T_LEN
+
+    B, Hq, Hkv, D, dp, E, Eh = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.dp, cfg.E, cfg.Eh
+    I, Np, nl = cfg.interval, cfg.n_proj, cfg.layers
+    npro = (nl + cfg.producer_stride - 1) // cfg.producer_stride
+    Lmax = cfg.L + I
+    if cfg.ragged:
+        L0 = (cfg.L // 2 + rng_for(cfg.cid, T_LEN).integers(0, cfg.L // 2 + 1, size=B)).astype(np.int32)
+    else:
+        L0 = np.full(B, cfg.L, np.int32)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260101 + cfg.cid)
+    log("allocating %d layers of K/V [%d, %d, %d, %d] bf16 on the GPU" % (nl, B, Hkv, Lmax, D))
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=gen, device="cuda") * std).to(torch.bfloat16)
+
+    def xavier(o, i, lead=()):
+        bnd = (6.0 / (i + o)) ** 0.5
+        return ((torch.rand(*lead, o, i, generator=gen, device="cuda") * 2 - 1) * bnd).to(torch.bfloat16)
+
+    K = [randn(B, Hkv, Lmax, D) for _ in range(nl)]
+    V = [randn(B, Hkv, Lmax, D) for _ in range(nl)]
+    Wk = [xavier(dp, D, (Hkv,)) for _ in range(nl)]
+    Q = [randn(B, Hq, D) for _ in range(nl)]
+    X = [randn(B, E) for _ in range(npro)]
+    W1 = [xavier(Eh, E) for _ in range(npro)]
+    W2 = [xavier(Hq * dp, Eh) for _ in range(npro)]
+    ws_p = tb.new_workspace(tb.tb_predict_workspace_bytes(B, E, Eh, Hq * dp))
+    qhat = [torch.empty(B, Hq * dp, device="cuda") for _ in range(npro)]
+    ctx0 = torch.from_numpy(L0).cuda()
+    if cfg.heavy_frac > 0:
+        # heavy tail: a fraction of positions per query head gets keys moved
+        # along that head's predicted-query direction by heavy_shift score std
+        for p in range(npro):
+            tb.tb_predict_queries(X[p], W1[p], W2[p], qhat[p], ws_p)
+        for l in range(nl):
+            qh = qhat[l // cfg.producer_stride].view(B, Hq, dp)
+            wk = Wk[l].float().repeat_interleave(cfg.g, 0)                 # [Hq, dp, D]
+            v = torch.einsum("bhc,hcd->bhd", qh, wk)
+            v = v / v.norm(dim=-1, keepdim=True)
+            for b in range(B):
+                n = int(cfg.heavy_frac * (int(L0[b]) - cfg.W - cfg.S))
+                for h in range(Hq):
+                    pos = torch.randint(cfg.S, int(L0[b]) - cfg.W, (n,), generator=gen, device="cuda")
+                    kv = h // cfg.g
+                    K[l][b, kv, pos] = (K[l][b, kv, pos].float() + cfg.heavy_shift * v[b, h]).to(torch.bfloat16)
+    # projected keys of everything but the pending batch
+    Kp = [torch.zeros(B, Hkv, Lmax, dp, dtype=torch.float16, device="cuda") for _ in range(nl)]
+    pend = torch.from_numpy(L0 - Np).cuda()
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for l in range(nl):
+        tb.tb_project_keys(K[l], Wk[l], Kp[l], zero, int(L0.max()) - Np)
+    torch.cuda.synchronize()
+    scores = torch.empty(B, Hq, Lmax, device="cuda")
+    cap = cfg.S + cfg.K
+    idx = [torch.zeros(B, Hq, cap, dtype=torch.int32, device="cuda") for _ in range(nl)]
+    cnt = [torch.zeros(B, Hq, dtype=torch.int32, device="cuda") for _ in range(nl)]
+    out = torch.empty(B, Hq, D, device="cuda")
+    ws_s = tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax))
+    ws_a = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, cfg.W, D))
+    step_ctx = [torch.from_numpy(L0 + 1 + j).cuda() for j in range(I)]
+    mode = tb.TB_NF_FILL | tb.TB_SEL_OMIT_WINDOW
+    stream = torch.cuda.current_stream()
+
+    def interval(attn_ev=None):
+        for l in range(nl):
+            tb.tb_project_keys(K[l], Wk[l], Kp[l], pend, Np)
+        for p in range(npro):
+            tb.tb_predict_queries(X[p], W1[p], W2[p], qhat[p], ws_p)
+        for l in range(nl):
+            tb.tb_score(qhat[l // cfg.producer_stride], Kp[l], ctx0, scores)
+            tb.tb_select(scores, ctx0, ctx0, cfg.S, cfg.W, cfg.K, cfg.r, idx[l], cnt[l], ws_s, mode=mode)
+        for j in range(I):
+            for l in range(nl):
+                if attn_ev is not None and l == 0:
+                    attn_ev[j][0].record(stream)
+                tb.tb_sparse_decode_attn(Q[l], K[l], V[l], idx[l], cnt[l], out, ws_a,
+                                         ctx_len=step_ctx[j], window=cfg.W)
+            if attn_ev is not None:
+                attn_ev[j][1].record(stream)
+
+    log("warmup interval")
+    interval()
+    torch.cuda.synchronize()
+    n_int = max(1, args.intervals)
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(I)] for _ in range(n_int)]
+    log("timing %d intervals of %d steps" % (n_int, I))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(n_int):
+        interval(evs[k])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    attn_us = float(np.mean([a.elapsed_time(b) for row in evs for a, b in row])) * 1e3 / nl
+    # compulsory gather bytes of one layer's attention launch at the first step
+    gi, gc = idx[0].cpu().numpy(), cnt[0].cpu().numpy()
+    rows = 0
+    for b in range(B):
+        Lb = int(L0[b]) + 1
+        win = set(range(max(0, Lb - cfg.W), Lb))
+        for kvh in range(Hkv):
+            u = set(win)
+            for h in range(kvh * cfg.g, (kvh + 1) * cfg.g):
+                u.update(gi[b, h, :gc[b, h]].tolist())
+            rows += len(u)
+    attn_bytes = rows * 2 * D * 2
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    steps = n_int * I
+    res = {
+        "metric": METRIC, "value": steps / el, "unit": "steps/s", "n_gpus": 1, "steps": steps,
+        "warmup": I, "ms_per_step": el / steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (device-generated)",
+        "config": {"workload": "%s: B=%d L=%s layers=%d Hq=%d Hkv=%d D=%d E=%d Eh=%d d'=%d sink=%d "
+                               "window=%d budget=%d radius=%d interval=%d projection batch=%d"
+                               % (cfg.name, B, "ragged %d..%d" % (L0.min(), L0.max()) if cfg.ragged
+                                  else str(cfg.L), nl, Hq, Hkv, D, E, Eh, dp, cfg.S, cfg.W, cfg.K,
+                                  cfg.r, I, Np),
+                   "global_batch": B, "seq_len": int(L0.max())},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "kernel": "sparse decode attention gather (one layer, one step)",
+                     "bytes_per_launch": attn_bytes, "avg_launch_us": attn_us},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +241,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also time each stage")
+    ap.add_argument("--config", type=int, default=2,
+                    help="2: the single-layer decode step (default); 3, 4, 5: the multi-layer "
+                         "prediction-interval workloads")
+    ap.add_argument("--intervals", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy (for PMC byte-counter calibration) and exit")
     args = ap.parse_args()
@@ -129,6 +272,9 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
         return
 
+    if args.config != 2:
+        run_interval(CONFIGS[args.config], args)
+        return
     cfg = CONFIGS[2]
     B, L, R = 1, cfg.L, max(1, args.replicas)
     log("generating inputs (%s)" % cfg.name)
@@ -163,7 +309,8 @@ def main():
     # Pre-marshalled C ABI calls (same entry points as the binding, without
     # per-call Python argument checks, so the host keeps ahead of the GPU).
     # Validate every argument set once through the checked binding first.
-    tb.tb_predict_queries(reps[0]["x"], reps[0]["w1"], reps[0]["w2"], qhat, ws_p)
+    tb.tb_predict_project(reps[0]["x"], reps[0]["w1"], reps[0]["w2"], qhat, ws_p, reps[0]["kc"],
+                          reps[0]["wk"], reps[0]["kp"], pos_new, 1)
     tb.tb_score(qhat, reps[0]["kp"], ctx, scores)
     tb.tb_select(scores, ctx, ctx, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt, ws_s)
     tb.tb_sparse_decode_attn(reps[0]["q"], reps[0]["kc"], reps[0]["vc"], idx, cnt, out, ws_a)
@@ -177,10 +324,9 @@ def main():
     calls = []
     for r in reps:
         calls.append([
-            (L_.tb_predict_queries, (P(r["x"]), P(r["w1"]), P(r["w2"]), P(qhat), B, cfg.E, cfg.Eh,
-                                     cfg.n_out, P(ws_p), nb(ws_p), sp)),
-            (L_.tb_project_keys, (P(r["kc"]), P(r["wk"]), P(r["kp"]), P(pos_new), 1, B, cfg.Hkv, L,
-                                  cfg.D, cfg.dp, sp)),
+            (L_.tb_predict_project, (P(r["x"]), P(r["w1"]), P(r["w2"]), P(qhat), B, cfg.E, cfg.Eh,
+                                     cfg.n_out, P(ws_p), nb(ws_p), P(r["kc"]), P(r["wk"]),
+                                     P(r["kp"]), P(pos_new), 1, cfg.Hkv, L, cfg.D, cfg.dp, sp)),
             (L_.tb_score, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(scores), B, cfg.Hq, cfg.Hkv, L,
                            cfg.dp, sp)),
             (L_.tb_select, (P(scores), P(ctx), P(ctx), B, cfg.Hq, L, cfg.S, cfg.W, cfg.K, cfg.r,
@@ -194,7 +340,7 @@ def main():
     def run_step(i, ev=None):
         c = calls[i % R]
         for j, (fn, a) in enumerate(c):
-            if ev is not None and j == 4:
+            if ev is not None and j == 3:
                 ev[0].record(stream)
             st = fn(*a)
             if st:
@@ -244,14 +390,14 @@ def main():
 
     stages = None
     if args.stages:
-        names = ["predict", "project", "score", "select", "attention"]
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(200)]
+        names = ["predict+project", "score", "select", "attention"]
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(200)]
         for i in range(200):
             c = calls[i % R]
             for j, (fn, a) in enumerate(c):
                 sev[i][j].record(stream)
                 fn(*a)
-            sev[i][5].record(stream)
+            sev[i][4].record(stream)
         torch.cuda.synchronize()
         stages = {n: round(float(np.median([e[j].elapsed_time(e[j + 1]) for e in sev])) * 1e3, 2)
                   for j, n in enumerate(names)}

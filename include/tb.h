@@ -80,6 +80,20 @@ tb_status tb_predict_queries(const void *x, const void *w1, const void *w2, floa
                              void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * tb_predict_queries and tb_project_keys fused: the two steps are independent
+ * (the predictor reads the producer layer's state, the projection the consumer
+ * layer's newest keys), so the projection runs as extra workgroups of the
+ * predictor's first launch; one launch less per decode step. Arguments,
+ * limits and results are exactly those of the two calls (same B for both).
+ */
+tb_status tb_predict_project(const void *x, const void *w1, const void *w2, float *qhat,
+                             int B, int E, int Eh, int n_out,
+                             void *workspace, size_t ws_bytes,
+                             const void *k_cache, const void *wk, void *kp,
+                             const int32_t *pos0, int n_tokens,
+                             int Hkv, int Lmax, int D, int dp, void *stream);
+
+/*
  * Key-cache projection ("Core architecture", key projection; "Inference
  * strategy", batching: run once per batch of new tokens, not every step):
  *     kp[b, j, t, :] = fp16_rne( k_cache[b, j, t, :] wk[j]^T )   fp32 accumulation

@@ -53,6 +53,9 @@ def lib():
     L.tb_predict_workspace_bytes.argtypes = [_i, _i, _i, _i]
     L.tb_predict_queries.restype = _i
     L.tb_predict_queries.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]
+    L.tb_predict_project.restype = _i
+    L.tb_predict_project.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp, _vp, _vp,
+                                     _vp, _i, _i, _i, _i, _i, _vp]
     L.tb_project_keys.restype = _i
     L.tb_project_keys.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
     L.tb_score.restype = _i
@@ -129,6 +132,26 @@ def tb_predict_queries(x, w1, w2, qhat, workspace, stream=None):
                                     _ptr(w2, torch.bfloat16, "w2", 2), _ptr(qhat, torch.float32, "qhat"),
                                     B, E, Eh, n_out, wp, wn, _stream(stream)))
     return qhat
+
+
+def tb_predict_project(x, w1, w2, qhat, workspace, k_cache, wk, kp, pos0, n_tokens, stream=None):
+    """tb_predict_queries and tb_project_keys in one call (one launch fewer)."""
+    B, E = x.shape
+    Eh, n_out = w1.shape[0], w2.shape[0]
+    Bk, Hkv, Lmax, D = k_cache.shape
+    dp = wk.shape[1]
+    if (tuple(w1.shape) != (Eh, E) or tuple(w2.shape) != (n_out, Eh) or qhat.numel() != B * n_out
+            or Bk != B or tuple(wk.shape) != (Hkv, dp, D) or tuple(kp.shape) != (B, Hkv, Lmax, dp)
+            or pos0.numel() != B):
+        raise ValueError("tb_predict_project: shape mismatch")
+    wp, wn = _ws(workspace)
+    _check(lib().tb_predict_project(_ptr(x, torch.bfloat16, "x", 2), _ptr(w1, torch.bfloat16, "w1", 2),
+                                    _ptr(w2, torch.bfloat16, "w2", 2), _ptr(qhat, torch.float32, "qhat"),
+                                    B, E, Eh, n_out, wp, wn, _ptr(k_cache, torch.bfloat16, "k_cache", 4),
+                                    _ptr(wk, torch.bfloat16, "wk", 3), _ptr(kp, torch.float16, "kp", 4),
+                                    _ptr(pos0, torch.int32, "pos0"), int(n_tokens), Hkv, Lmax, D, dp,
+                                    _stream(stream)))
+    return qhat, kp
 
 
 # ---------------------------------------------------------------- projection

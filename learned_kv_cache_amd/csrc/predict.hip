@@ -13,13 +13,13 @@
 // in A and B so that each lane reads 32 contiguous elements per 128-element
 // block; the result is the same sum. The four waves of a workgroup take
 // interleaved 128-element blocks and are reduced through LDS.
-#include "tb_common.h"
+#include "project_impl.h"
 
 namespace tb {
 namespace {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef bf16x8_t bf16x8;
+typedef f32x4_t f32x4;
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -43,12 +43,10 @@ __device__ __forceinline__ float reduce_waves(const f32x4 &acc, float (*red)[64]
     return s;
 }
 
-__global__ __launch_bounds__(kThreads) void mlp1_kernel(const uint16_t *__restrict__ x,
-                                                        const uint16_t *__restrict__ w1,
-                                                        float *__restrict__ part, int B, int E,
-                                                        int Eh, int bps) {
-    __shared__ float red[kWaves][64][4];
-    const int jt = blockIdx.x, sp = blockIdx.y, bt = blockIdx.z;
+__device__ __forceinline__ void mlp1_block(const uint16_t *__restrict__ x,
+                                           const uint16_t *__restrict__ w1,
+                                           float *__restrict__ part, int B, int E, int Eh, int bps,
+                                           int jt, int sp, int bt, float (*red)[64][4]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, kq = lane >> 4;
     const int nblk = E / BLK;
@@ -80,6 +78,36 @@ __global__ __launch_bounds__(kThreads) void mlp1_kernel(const uint16_t *__restri
     const int j = jt * 16 + (threadIdx.x >> 4);
     const int ob = bt * 16 + (threadIdx.x & 15);
     if (ob < B) part[((size_t)sp * B + ob) * Eh + j] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void mlp1_kernel(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ w1,
+                                                        float *__restrict__ part, int B, int E,
+                                                        int Eh, int bps) {
+    __shared__ float red[kWaves][64][4];
+    mlp1_block(x, w1, part, B, E, Eh, bps, blockIdx.x, blockIdx.y, blockIdx.z, red);
+}
+
+// mlp1 and an independent key projection in one launch: the first n1
+// workgroups are mlp1 tiles, the rest projection workgroups.
+template <int D, int DP>
+__global__ __launch_bounds__(kThreads) void mlp1_project_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ w1, float *__restrict__ part,
+    int B, int E, int Eh, int bps, int nsplit, int n1, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ wk, uint16_t *__restrict__ kp, const int32_t *__restrict__ pos0,
+    int ntok, int Hkv, int Lmax, int nproj) {
+    __shared__ float red[kWaves][64][4];
+    const int bid = blockIdx.x;
+    if (bid < n1) {
+        const int jt = bid % (Eh / 16);
+        const int rest = bid / (Eh / 16);
+        mlp1_block(x, w1, part, B, E, Eh, bps, jt, rest % nsplit, rest / nsplit, red);
+    } else {
+        const int q = bid - n1;
+        const int blk = q % nproj;
+        const int rest = q / nproj;
+        project_block<D, DP>(kc, wk, kp, pos0, ntok, Hkv, Lmax, blk, rest % Hkv, rest / Hkv);
+    }
 }
 
 __device__ __forceinline__ uint32_t silu_bf16(float z) {
@@ -187,6 +215,50 @@ tb_status launch_predict(const void *x, const void *w1, const void *w2, float *q
                        (size_t)16 * Eh * sizeof(uint16_t), st, part,
                        static_cast<const uint16_t *>(w2), qhat, B, Eh, n_out, nsplit);
     return check_launch("tb_predict_queries(mlp2)");
+}
+
+tb_status launch_predict_project(const void *x, const void *w1, const void *w2, float *qhat,
+                                 int B, int E, int Eh, int n_out, void *ws, int nsplit,
+                                 const void *kc, const void *wk, void *kp, const int32_t *pos0,
+                                 int ntok, int Hkv, int Lmax, int D, int dp, hipStream_t st) {
+    if (ntok == 0)
+        return launch_predict(x, w1, w2, qhat, B, E, Eh, n_out, ws, nsplit, st);
+    const int nblk = E / BLK;
+    const int bps = (nblk + nsplit - 1) / nsplit;
+    float *part = static_cast<float *>(ws);
+    const int bt = (B + 15) / 16;
+    const int n1 = (Eh / 16) * nsplit * bt;
+    const int nproj = (ntok + kProjTokPerBlock - 1) / kProjTokPerBlock;
+    const long long nb = (long long)n1 + (long long)nproj * Hkv * B;
+    if (nb > 0x7fffffffLL) {
+        set_error("tb_predict_project: grid too large");
+        return TB_ERR_UNSUPPORTED_SHAPE;
+    }
+    const uint16_t *xx = static_cast<const uint16_t *>(x);
+    const uint16_t *ww1 = static_cast<const uint16_t *>(w1);
+    const uint16_t *k = static_cast<const uint16_t *>(kc);
+    const uint16_t *w = static_cast<const uint16_t *>(wk);
+    uint16_t *o = static_cast<uint16_t *>(kp);
+    bool launched = false;
+#define TB_PP(DD, PP)                                                                          \
+    if (!launched && D == DD && dp == PP) {                                                    \
+        hipLaunchKernelGGL((mlp1_project_kernel<DD, PP>), dim3((unsigned)nb), dim3(kThreads), 0, \
+                           st, xx, ww1, part, B, E, Eh, bps, nsplit, n1, k, w, o, pos0, ntok,  \
+                           Hkv, Lmax, nproj);                                                  \
+        launched = true;                                                                       \
+    }
+    TB_PP(128, 32) TB_PP(128, 16) TB_PP(64, 32) TB_PP(64, 16)
+#undef TB_PP
+    if (!launched) {
+        set_error("tb_predict_project: unsupported D=%d dp=%d", D, dp);
+        return TB_ERR_UNSUPPORTED_SHAPE;
+    }
+    tb_status e = check_launch("tb_predict_project(mlp1+project)");
+    if (e) return e;
+    hipLaunchKernelGGL(mlp2_kernel, dim3(n_out / 16, 1, bt), dim3(kThreads),
+                       (size_t)16 * Eh * sizeof(uint16_t), st, part,
+                       static_cast<const uint16_t *>(w2), qhat, B, Eh, n_out, nsplit);
+    return check_launch("tb_predict_project(mlp2)");
 }
 
 }  // namespace tb

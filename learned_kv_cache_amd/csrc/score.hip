@@ -12,7 +12,7 @@ namespace tb {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kRowsPerThread = 2;
+constexpr int kRowsPerThread = 1;
 constexpr int kTokPerBlock = kThreads * kRowsPerThread;
 
 template <int G, int DP>

@@ -11,7 +11,7 @@
 // position on ties). The greedy order is exactly descending key order, the
 // keys are distinct, and the important buffer is the min(K, |E|) largest keys.
 //
-// Four launches, all integer work:
+// Five launches, all integer work:
 //   hist     per (segment, 2048-token chunk): pooled keys from LDS-staged
 //            scores; 4096-bin LDS histogram of the top 12 key bits (runs of
 //            equal bins in neighbouring lanes are added once), merged into a
@@ -21,12 +21,13 @@
 //   classify same grid: tokens above the boundary bin go straight into a
 //            selection bitmap (wave ballots); tokens in it are gathered in LDS
 //            and written to the chunk's own slots of the candidate list;
-//   finalize one 1024-thread workgroup per segment: gathers the chunks'
+//   thr      one 1024-thread workgroup per segment: gathers the chunks'
 //            candidates, exact select of the remaining quota among them (10-bit
 //            radix passes narrow the boundary group to at most 64 keys, which
-//            are ranked directly). Sink / window / chosen candidates are ORed
-//            into 32768-token bitmap tiles that a block prefix sum compacts
-//            into the ascending index list.
+//            are ranked directly), then each chunk's offset in the output list;
+//   compact  one wave per chunk: bitmap words ORed with the chunk's chosen
+//            candidates and the sink / window bits, emitted as ascending
+//            positions with coalesced stores.
 #include "tb_common.h"
 
 namespace tb {
@@ -38,12 +39,10 @@ constexpr int CHUNK = 2048;          // tokens per hist/classify workgroup
 constexpr int T1 = 256;              // threads of hist/classify
 constexpr int MAXR = 64;
 constexpr int T3 = 1024;             // threads of finalize
-constexpr int TILE_WORDS = T3;       // bitmap words per compaction tile
 constexpr int LDS_CAND = 8192;       // candidates held in LDS by finalize
 constexpr int RBITS = 10;            // radix digit of the exact select
 constexpr int RBINS = 1 << RBITS;
 constexpr int GMAX = 64;             // boundary group size ranked directly
-constexpr int PRE_TILES = 8;         // bitmap tiles prefetched (262144 tokens)
 constexpr int MAX_CHUNKS = (1 << 24) / CHUNK;   // chunks of the largest Lmax
 
 struct Region {
@@ -255,11 +254,12 @@ __global__ __launch_bounds__(T1) void boundary_kernel(const int32_t *__restrict_
 __global__ __launch_bounds__(T1) void classify_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx,
     const int32_t *__restrict__ plen, int Hq, int Lmax, int S, int W, int K, int r,
-    const int32_t *__restrict__ info, uint32_t *__restrict__ ccount, int nchunks,
-    uint64_t *__restrict__ cand, uint32_t *__restrict__ bitmap, int nwords) {
+    const int32_t *__restrict__ info, uint32_t *__restrict__ ccount,
+    uint32_t *__restrict__ acount, int nchunks, uint64_t *__restrict__ cand,
+    uint32_t *__restrict__ bitmap, int nwords) {
     __shared__ uint32_t sk[CHUNK + 2 * MAXR];
     __shared__ uint64_t s_cand[CHUNK];
-    __shared__ uint32_t s_nc;
+    __shared__ uint32_t s_nc, s_na;
     const int seg = blockIdx.y, b = seg / Hq;
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
     const int c0 = blockIdx.x * CHUNK;
@@ -273,7 +273,10 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     const bool touch = partial && a < z;
     const int lo = a - r, hi = z + r;
     int B1 = NBINS;
-    if (threadIdx.x == 0) s_nc = 0;
+    if (threadIdx.x == 0) {
+        s_nc = 0;
+        s_na = 0;
+    }
     if (touch) {
         B1 = info[2 * seg];
         stage_keys<T1>(sk, scores + (size_t)seg * Lmax, lo, hi, g.e0, g.e1);
@@ -300,6 +303,7 @@ __global__ __launch_bounds__(T1) void classify_kernel(
             const int w = base >> 5;
             bm[w] = (uint32_t)m;
             if (w + 1 < nwords) bm[w + 1] = (uint32_t)(m >> 32);
+            if (m) atomicAdd(&s_na, (uint32_t)__popcll(m));
         }
         const uint64_t cm = __ballot(isc);
         if (cm) {
@@ -311,7 +315,10 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     }
     __syncthreads();
     const uint32_t nc = s_nc;
-    if (threadIdx.x == 0 && (int)blockIdx.x < nchunks) ccount[(size_t)seg * nchunks + blockIdx.x] = nc;
+    if (threadIdx.x == 0 && (int)blockIdx.x < nchunks) {
+        ccount[(size_t)seg * nchunks + blockIdx.x] = nc;
+        acount[(size_t)seg * nchunks + blockIdx.x] = s_na;
+    }
     // the chunk owns candidate slots [c0, c0 + CHUNK) of its segment
     uint64_t *cl = cand + (size_t)seg * Lmax + c0;
     for (uint32_t i = threadIdx.x; i < nc; i += T1)
@@ -337,28 +344,51 @@ __device__ __forceinline__ uint32_t bits_below(int n) {
     return n <= 0 ? 0u : (n >= 32 ? 0xffffffffu : ((1u << n) - 1u));
 }
 
-// Candidate i of the segment (chunk-major order): chunk c holds entries
-// [off[c], off[c+1]) in its slots starting at c * CHUNK.
-__device__ __forceinline__ uint64_t cand_at(const uint64_t *cl, const uint32_t *s_off, int nchunks,
-                                            uint32_t i) {
-    int lo = 0, hi = nchunks - 1;   // last chunk with off[c] <= i
+// Chunk holding candidate i of the segment (chunk-major order): the last
+// chunk c with off[c] <= i; chunk c holds entries [off[c], off[c+1]).
+__device__ __forceinline__ int chunk_of(const uint32_t *s_off, int nchunks, uint32_t i) {
+    int lo = 0, hi = nchunks - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (s_off[mid] <= i) lo = mid;
         else hi = mid - 1;
     }
-    return cl[(size_t)lo * CHUNK + (i - s_off[lo])];
+    return lo;
 }
 
-__global__ __launch_bounds__(T3) void finalize_kernel(
+// Candidate i of the segment, read from its chunk's slots.
+__device__ __forceinline__ uint64_t cand_at(const uint64_t *cl, const uint32_t *s_off, int nchunks,
+                                            uint32_t i) {
+    const int c = chunk_of(s_off, nchunks, i);
+    return cl[(size_t)c * CHUNK + (i - s_off[c])];
+}
+
+// How many of the tokens [t0, t1) lie in sink [0, slo) U window [wlo, L)
+// (the two ranges may overlap in short contexts).
+__device__ __forceinline__ int fixed_in(int t0, int t1, int slo, int wlo, int L) {
+    const int e = t1 < L ? t1 : L;
+    int n = 0;
+    if (t0 < slo) n += (e < slo ? e : slo) - t0;
+    int w0 = wlo > slo ? wlo : slo;
+    w0 = w0 > t0 ? w0 : t0;
+    if (e > w0) n += e - w0;
+    return n > 0 ? n : 0;
+}
+
+// One workgroup per segment: gather the chunks' candidates, find the exact
+// threshold key among them, then every chunk's output offset (above-boundary
+// tokens + chosen candidates + sink / window positions in the chunk, scanned).
+__global__ __launch_bounds__(T3) void thr_kernel(
     const int32_t *__restrict__ ctx, const int32_t *__restrict__ plen, int Hq, int Lmax, int S,
     int W, int K, int omit_window, const int32_t *__restrict__ info,
-    const uint32_t *__restrict__ ccount, int nchunks, const uint64_t *__restrict__ cand,
-    const uint32_t *__restrict__ bitmap, int nwords, int32_t *__restrict__ idx,
-    int32_t *__restrict__ count, int cap) {
+    const uint32_t *__restrict__ ccount, const uint32_t *__restrict__ acount, int nchunks,
+    const uint64_t *__restrict__ cand, uint64_t *__restrict__ thr_out,
+    uint32_t *__restrict__ coff, int32_t *__restrict__ count) {
     __shared__ uint64_t s_cand[LDS_CAND];
+    __shared__ uint16_t s_cc[LDS_CAND];          // chunk of each LDS candidate
     __shared__ uint32_t s_off[MAX_CHUNKS];
-    __shared__ uint32_t s_tile[TILE_WORDS];
+    __shared__ uint32_t s_chosen[MAX_CHUNKS];
+    __shared__ uint32_t s_tile[RBINS];
     __shared__ uint64_t s_grp[GMAX];
     __shared__ uint32_t s_w[T3 / 64];
     __shared__ int s_bin, s_need, s_cnt;
@@ -374,37 +404,28 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
     }
     const int nE = g.e1 - g.e0;
     const bool partial = g.need > 0 && g.need < nE;
-    // bitmap words of the first tiles, requested before anything else
     const int L = g.L;
-    const int nw = (L + 31) >> 5;
-    const uint32_t *bm = bitmap + (size_t)seg * nwords;
-    uint32_t pre[PRE_TILES];
+    const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
+    const int slo = S < L ? S : L;
+    constexpr int PC = MAX_CHUNKS / T3;
+    uint32_t cc[PC], ac[PC];
+    uint32_t csum = 0;
 #pragma unroll
-    for (int k = 0; k < PRE_TILES; ++k) {
-        const int w = k * TILE_WORDS + tid;
-        pre[k] = (g.need > 0 && w < nw) ? bm[w] : 0u;
+    for (int j = 0; j < PC; ++j) {
+        const int c = tid * PC + j;
+        const bool in = c < nchunks && g.need > 0;
+        cc[j] = in && partial ? ccount[(size_t)seg * nchunks + c] : 0u;
+        ac[j] = in ? acount[(size_t)seg * nchunks + c] : 0u;
+        csum += cc[j];
+        if (c < nchunks) s_chosen[c] = 0u;
     }
     int nc = 0;
-    uint64_t thr = 0;  // candidates with key >= thr are chosen
+    uint64_t thr = ~0ull;   // candidates with key >= thr are chosen (none by default)
     const uint64_t *cl = cand + (size_t)seg * Lmax;
     bool lds = true;
     if (partial) {
-        const int B1 = info[2 * seg];
         int k = info[2 * seg + 1];
-        // per-chunk candidate counts -> chunk offsets (block scan)
-        constexpr int PC = MAX_CHUNKS / T3;
-        uint32_t cc[PC];
-        uint32_t csum = 0;
-#pragma unroll
-        for (int j = 0; j < PC; ++j) {
-            const int c = tid * PC + j;
-            cc[j] = c < nchunks ? ccount[(size_t)seg * nchunks + c] : 0u;
-            csum += cc[j];
-        }
-        // the prefetched bitmap words are materialized here, overlapped with
-        // the loads above
-#pragma unroll
-        for (int j = 0; j < PRE_TILES; ++j) asm volatile("" ::"v"(pre[j]));
+        const int B1 = info[2 * seg];
         uint32_t total;
         uint32_t run = block_incl_scan<T3>(csum, s_w, &total) - csum;
 #pragma unroll
@@ -419,19 +440,30 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
         if (lds) {
             constexpr int PER = LDS_CAND / T3;
             uint64_t v[PER];
+            int vc[PER];
 #pragma unroll
             for (int j = 0; j < PER; ++j) {
                 const int i = tid + j * T3;
-                v[j] = i < nc ? cand_at(cl, s_off, nchunks, (uint32_t)i) : 0ull;
+                vc[j] = 0;
+                v[j] = 0ull;
+                if (i < nc) {
+                    vc[j] = chunk_of(s_off, nchunks, (uint32_t)i);
+                    v[j] = cl[(size_t)vc[j] * CHUNK + ((uint32_t)i - s_off[vc[j]])];
+                }
             }
 #pragma unroll
             for (int j = 0; j < PER; ++j) {
                 const int i = tid + j * T3;
-                if (i < nc) s_cand[i] = v[j];
+                if (i < nc) {
+                    s_cand[i] = v[j];
+                    s_cc[i] = (uint16_t)vc[j];
+                }
             }
             __syncthreads();
         }
-        if (k < nc) {
+        if (k >= nc) {
+            thr = 0ull;   // every candidate is chosen
+        } else {
             // the k-th largest key (all keys are distinct) among the candidates
             uint64_t prefix = (uint64_t)B1 << (64 - HBITS);
             uint64_t mask = (uint64_t)(NBINS - 1) << (64 - HBITS);
@@ -487,68 +519,107 @@ __global__ __launch_bounds__(T3) void finalize_kernel(
             __syncthreads();
             thr = s_thr;
         }
+        // chosen candidates per chunk
+        for (int i = tid; i < nc; i += T3) {
+            const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
+            if (key >= thr)
+                atomicAdd(&s_chosen[lds ? (int)s_cc[i] : chunk_of(s_off, nchunks, i)], 1u);
+        }
     }
+    __syncthreads();
+    // chunk offsets of the output list
+    uint32_t tot_c[PC];
+    uint32_t lsum = 0;
+#pragma unroll
+    for (int j = 0; j < PC; ++j) {
+        const int c = tid * PC + j;
+        tot_c[j] = 0u;
+        if (c < nchunks)
+            tot_c[j] = ac[j] + s_chosen[c] + (uint32_t)fixed_in(c * CHUNK, (c + 1) * CHUNK, slo, wlo, L);
+        lsum += tot_c[j];
+    }
+    uint32_t total;
+    uint32_t run = block_incl_scan<T3>(lsum, s_w, &total) - lsum;
+#pragma unroll
+    for (int j = 0; j < PC; ++j) {
+        const int c = tid * PC + j;
+        if (c < nchunks) coff[(size_t)seg * nchunks + c] = run;
+        run += tot_c[j];
+    }
+    if (tid == 0) {
+        count[seg] = (int32_t)total;
+        thr_out[seg] = thr;
+    }
+}
 
-    // compaction of sink | window | above-boundary bits | chosen candidates
-    int32_t *dst = idx + (size_t)seg * cap;
+// One wave per (chunk, segment): the chunk's 64 bitmap words, ORed with its
+// chosen candidates and the sink / window bits, are emitted as ascending
+// positions at the chunk's offset with coalesced stores.
+__global__ __launch_bounds__(64) void compact_kernel(
+    const int32_t *__restrict__ ctx, const int32_t *__restrict__ plen, int Hq, int Lmax, int S,
+    int W, int K, int omit_window, const uint32_t *__restrict__ ccount, int nchunks,
+    const uint64_t *__restrict__ cand, const uint32_t *__restrict__ bitmap, int nwords,
+    const uint64_t *__restrict__ thr_in, const uint32_t *__restrict__ coff,
+    int32_t *__restrict__ idx, int cap) {
+    __shared__ uint32_t s_word[64];
+    const int c = blockIdx.x, seg = blockIdx.y, b = seg / Hq;
+    const int lane = threadIdx.x;
+    const Region g = region(ctx, plen, b, Lmax, S, W, K);
+    const int L = g.L;
+    if (g.bad || c * CHUNK >= L) return;
+    const int nE = g.e1 - g.e0;
+    const bool partial = g.need > 0 && g.need < nE;
+    const int w = c * (CHUNK / 32) + lane;
+    const int t0 = w << 5;
     const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
     const int slo = S < L ? S : L;
-    uint32_t running = 0;
-    for (int w0 = 0; w0 < nw; w0 += TILE_WORDS) {
-        const int w = w0 + tid;
-        uint32_t bits = 0;
-        if (w < nw) {
-            const int t0 = w << 5;
-            const int tile = w0 / TILE_WORDS;
-            uint32_t pb = 0;
-#pragma unroll
-            for (int j = 0; j < PRE_TILES; ++j) pb = tile == j ? pre[j] : pb;
-            bits = (g.need > 0) ? (tile < PRE_TILES ? pb : bm[w]) : 0u;
-            bits |= bits_below(slo - t0);                                  // sink
-            bits |= bits_below(L - t0) & ~bits_below(wlo - t0);            // window
-            bits &= bits_below(L - t0);
-        }
-        s_tile[tid] = bits;
-        __syncthreads();
-        if (partial) {
-            const int tlo = w0 << 5, thi = (w0 + TILE_WORDS) << 5;
-            for (int i = tid; i < nc; i += T3) {
-                const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
-                if (key >= thr) {
-                    const int t = key_token(key);
-                    if (t >= tlo && t < thi) atomicOr(&s_tile[(t - tlo) >> 5], 1u << (t & 31));
-                }
-            }
-            __syncthreads();
-        }
-        const uint32_t mine = s_tile[tid];
-        uint32_t total;
-        const uint32_t incl = block_incl_scan<T3>((uint32_t)__popc(mine), s_w, &total);
-        const uint32_t pop = (uint32_t)__popc(mine);
-        const uint32_t first = incl - pop;   // list position of this word's first entry
-        // each wave emits its 64 words' positions 64 at a time: lane l takes
-        // output slot s, finds the owning word by binary search over the
-        // wave's prefix counts, and picks the bit; stores are coalesced
-        const int lane = tid & 63;
-        const uint32_t wfirst = __shfl(first, 0);
-        const uint32_t wend = __shfl(first + pop, 63);
-        for (uint32_t s0 = wfirst; s0 < wend; s0 += 64) {
-            const uint32_t sl = s0 + (uint32_t)lane;
-            int lo2 = 0;
-#pragma unroll
-            for (int step = 32; step >= 1; step >>= 1) {
-                const uint32_t f = __shfl(first, lo2 + step);
-                if (f <= sl) lo2 += step;
-            }
-            const uint32_t wbits = __shfl(mine, lo2);
-            const uint32_t k = sl - __shfl(first, lo2);
-            const uint32_t p = running + sl;
-            if (sl < wend && p < (uint32_t)cap)
-                dst[p] = ((w0 + (tid & ~63) + lo2) << 5) + select_bit(wbits, k);
-        }
-        running += total;
+    uint32_t bits = (g.need > 0 && w < nwords) ? bitmap[(size_t)seg * nwords + w] : 0u;
+    const uint32_t base = coff[(size_t)seg * nchunks + c];
+    uint32_t n = 0;
+    uint64_t thr = 0;
+    if (partial) {
+        n = ccount[(size_t)seg * nchunks + c];
+        thr = thr_in[seg];
     }
-    if (tid == 0) count[seg] = (int32_t)running;
+    bits |= bits_below(slo - t0);
+    bits |= bits_below(L - t0) & ~bits_below(wlo - t0);
+    bits &= bits_below(L - t0);
+    s_word[lane] = bits;
+    __syncthreads();
+    const uint64_t *cl = cand + (size_t)seg * Lmax + (size_t)c * CHUNK;
+    for (uint32_t i = lane; i < n; i += 64) {
+        const uint64_t key = cl[i];
+        if (key >= thr) {
+            const int t = key_token(key) - c * CHUNK;
+            atomicOr(&s_word[t >> 5], 1u << (t & 31));
+        }
+    }
+    __syncthreads();
+    const uint32_t mine = s_word[lane];
+    const uint32_t pop = (uint32_t)__popc(mine);
+    uint32_t incl = pop;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    const uint32_t first = incl - pop;
+    const uint32_t wend = __shfl(incl, 63);
+    int32_t *dst = idx + (size_t)seg * cap;
+    for (uint32_t s0 = 0; s0 < wend; s0 += 64) {
+        const uint32_t sl = s0 + (uint32_t)lane;
+        int lo2 = 0;
+#pragma unroll
+        for (int step = 32; step >= 1; step >>= 1) {
+            const uint32_t f = __shfl(first, lo2 + step);
+            if (f <= sl) lo2 += step;
+        }
+        const uint32_t wbits = __shfl(mine, lo2);
+        const uint32_t k = sl - __shfl(first, lo2);
+        const uint32_t p = base + sl;
+        if (sl < wend && p < (uint32_t)cap)
+            dst[p] = ((c * (CHUNK / 32) + lo2) << 5) + select_bit(wbits, k);
+    }
 }
 
 }  // namespace
@@ -561,6 +632,7 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
     const size_t hist_b = up(nseg * NBINS * 4);
     const size_t info_b = up(nseg * 8);
     const size_t cc_b = up(nseg * (size_t)nchunks * 4);
+    const size_t thr_b = up(nseg * 8);
     const size_t bm_b = up(nseg * (size_t)nwords * 4);
     const size_t cand_b = up(nseg * (size_t)Lmax * 8);
     if (base && out) {
@@ -571,13 +643,19 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
         p += info_b;
         out->ccount = reinterpret_cast<uint32_t *>(p);
         p += cc_b;
+        out->acount = reinterpret_cast<uint32_t *>(p);
+        p += cc_b;
+        out->coff = reinterpret_cast<uint32_t *>(p);
+        p += cc_b;
+        out->thr = reinterpret_cast<uint64_t *>(p);
+        p += thr_b;
         out->bitmap = reinterpret_cast<uint32_t *>(p);
         p += bm_b;
         out->cand = reinterpret_cast<uint64_t *>(p);
         out->nwords = nwords;
         out->nchunks = nchunks;
     }
-    return hist_b + info_b + cc_b + bm_b + cand_b;
+    return hist_b + info_b + 3 * cc_b + thr_b + bm_b + cand_b;
 }
 
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
@@ -595,13 +673,19 @@ tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *
     e = check_launch("tb_select(boundary)");
     if (e) return e;
     hipLaunchKernelGGL(classify_kernel, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
-                       K, r, ws.info, ws.ccount, ws.nchunks, ws.cand, ws.bitmap, ws.nwords);
+                       K, r, ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand, ws.bitmap,
+                       ws.nwords);
     e = check_launch("tb_select(classify)");
     if (e) return e;
-    hipLaunchKernelGGL(finalize_kernel, dim3(nseg), dim3(T3), 0, st, ctx, plen, Hq, Lmax, S, W, K,
-                       omit_window ? 1 : 0, ws.info, ws.ccount, ws.nchunks, ws.cand, ws.bitmap,
-                       ws.nwords, idx, count, cap);
-    return check_launch("tb_select(finalize)");
+    hipLaunchKernelGGL(thr_kernel, dim3(nseg), dim3(T3), 0, st, ctx, plen, Hq, Lmax, S, W, K,
+                       omit_window ? 1 : 0, ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand,
+                       ws.thr, ws.coff, count);
+    e = check_launch("tb_select(threshold)");
+    if (e) return e;
+    hipLaunchKernelGGL(compact_kernel, grid, dim3(64), 0, st, ctx, plen, Hq, Lmax, S, W, K,
+                       omit_window ? 1 : 0, ws.ccount, ws.nchunks, ws.cand, ws.bitmap, ws.nwords,
+                       ws.thr, ws.coff, idx, cap);
+    return check_launch("tb_select(compact)");
 }
 
 }  // namespace tb

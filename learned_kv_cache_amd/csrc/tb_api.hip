@@ -74,6 +74,32 @@ tb_status tb_predict_queries(const void *x, const void *w1, const void *w2, floa
                               tb::predict_nsplit(E, Eh), static_cast<hipStream_t>(stream));
 }
 
+tb_status tb_predict_project(const void *x, const void *w1, const void *w2, float *qhat, int B,
+                             int E, int Eh, int n_out, void *workspace, size_t ws_bytes,
+                             const void *k_cache, const void *wk, void *kp, const int32_t *pos0,
+                             int n_tokens, int Hkv, int Lmax, int D, int dp, void *stream) {
+    TB_REQUIRE(x && w1 && w2 && qhat && workspace && k_cache && wk && kp && pos0,
+               TB_ERR_INVALID_ARGUMENT, "tb_predict_project: null pointer");
+    TB_REQUIRE(aligned16(x) && aligned16(w1) && aligned16(w2) && aligned16(qhat) &&
+                   aligned16(workspace) && aligned16(k_cache) && aligned16(wk) && aligned16(kp) &&
+                   aligned4(pos0),
+               TB_ERR_INVALID_ARGUMENT, "tb_predict_project: misaligned pointer");
+    TB_REQUIRE(B >= 1 && B <= 64 && E > 0 && Eh > 0 && n_out > 0 && Hkv >= 1 &&
+                   Hkv <= 65535 && Lmax >= 1 && n_tokens >= 0,
+               TB_ERR_INVALID_ARGUMENT, "tb_predict_project: bad sizes");
+    TB_REQUIRE(E % 128 == 0 && Eh % 128 == 0 && n_out % 16 == 0 && Eh <= 1536,
+               TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_predict_project: need E %% 128 == 0, Eh %% 128 == 0, Eh <= 1536, n_out %% 16 == 0");
+    TB_REQUIRE((D == 64 || D == 128) && (dp == 16 || dp == 32), TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_predict_project: D must be 64 or 128 and dp 16 or 32");
+    const size_t need = tb_predict_workspace_bytes(B, E, Eh, n_out);
+    TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
+               "tb_predict_project: workspace %zu < %zu bytes", ws_bytes, need);
+    return tb::launch_predict_project(x, w1, w2, qhat, B, E, Eh, n_out, workspace,
+                                      tb::predict_nsplit(E, Eh), k_cache, wk, kp, pos0, n_tokens,
+                                      Hkv, Lmax, D, dp, static_cast<hipStream_t>(stream));
+}
+
 // ---------------------------------------------------------------- projection
 tb_status tb_project_keys(const void *k_cache, const void *wk, void *kp, const int32_t *pos0,
                           int n_tokens, int B, int Hkv, int Lmax, int D, int dp, void *stream) {

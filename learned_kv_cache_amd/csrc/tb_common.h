@@ -74,6 +74,10 @@ namespace tb {
 tb_status launch_predict(const void *x, const void *w1, const void *w2, float *qhat, int B, int E,
                          int Eh, int n_out, void *ws, int nsplit, hipStream_t st);
 int predict_nsplit(int E, int Eh);
+tb_status launch_predict_project(const void *x, const void *w1, const void *w2, float *qhat,
+                                 int B, int E, int Eh, int n_out, void *ws, int nsplit,
+                                 const void *kc, const void *wk, void *kp, const int32_t *pos0,
+                                 int ntok, int Hkv, int Lmax, int D, int dp, hipStream_t st);
 tb_status launch_project(const void *kc, const void *wk, void *kp, const int32_t *pos0, int ntok,
                          int B, int Hkv, int Lmax, int D, int dp, hipStream_t st);
 tb_status launch_score(const float *qhat, int n_slots, int slot, const void *kp,
@@ -83,6 +87,9 @@ struct SelectWs {
     uint32_t *hist;      // [nseg][4096], zero at rest
     int32_t *info;       // [nseg][2] boundary bin, quota inside it
     uint32_t *ccount;    // [nseg][nchunks] candidates per chunk
+    uint32_t *acount;    // [nseg][nchunks] tokens above the boundary bin per chunk
+    uint32_t *coff;      // [nseg][nchunks] offset of each chunk in the output list
+    uint64_t *thr;       // [nseg] exact threshold key among the candidates
     uint32_t *bitmap;    // [nseg][nwords]
     uint64_t *cand;      // [nseg][Lmax], chunk c owns slots [c * CHUNK, ...)
     int nwords;

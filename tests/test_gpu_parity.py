@@ -268,3 +268,27 @@ def test_attention_repeatable_bitwise_at_c2_shape(tb, orc):
     nsplit = (cap + 255) // 256
     ctr_off = (B * Hq * nsplit * (D + 2) * 4 + 255) // 256 * 256
     assert int(ws[ctr_off:ctr_off + B * Hq * 4].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("B,E,Eh,nout,Hkv,L,D,dp,ntok", [(1, 4096, 1024, 1024, 8, 4096, 128, 32, 1),
+                                                        (3, 512, 128, 128, 2, 300, 64, 16, 16)])
+def test_predict_project_fused_equals_separate(tb, orc, B, E, Eh, nout, Hkv, L, D, dp, ntok):
+    say("predict+project fused", B, E, Eh, Hkv, L, ntok)
+    rng = rng_for(61, B, E, L)
+    x = dev(normal_bf16(rng, (B, E)), torch.bfloat16)
+    w1 = dev(xavier_bf16(rng, Eh, E), torch.bfloat16)
+    w2 = dev(xavier_bf16(rng, nout, Eh), torch.bfloat16)
+    kc = dev(normal_bf16(rng, (B, Hkv, L, D)), torch.bfloat16)
+    wk = dev(xavier_bf16(rng, dp, D, lead=(Hkv,)), torch.bfloat16)
+    pos0 = dev32((L - ntok - np.arange(B)).astype(np.int32))
+    ws = tb.new_workspace(tb.tb_predict_workspace_bytes(B, E, Eh, nout))
+    q1 = torch.empty(B, nout, device="cuda")
+    kp1 = torch.zeros(B, Hkv, L, dp, dtype=torch.float16, device="cuda")
+    tb.tb_predict_queries(x, w1, w2, q1, ws)
+    tb.tb_project_keys(kc, wk, kp1, pos0, ntok)
+    q2 = torch.empty(B, nout, device="cuda")
+    kp2 = torch.zeros(B, Hkv, L, dp, dtype=torch.float16, device="cuda")
+    tb.tb_predict_project(x, w1, w2, q2, ws, kc, wk, kp2, pos0, ntok)
+    torch.cuda.synchronize()
+    assert torch.equal(q1, q2)
+    assert torch.equal(kp1.view(torch.int16), kp2.view(torch.int16))
