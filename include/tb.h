@@ -26,8 +26,9 @@
  *    otherwise).
  *  - Workspaces: size them with the matching *_workspace_bytes() query and
  *    zero-fill them once before first use (e.g. torch.zeros). Every call
- *    that takes a workspace leaves it zero-filled again when its kernels
- *    complete, so it can be reused without clearing.
+ *    that takes a workspace leaves whatever must start at zero (the
+ *    attention's arrival counters) at zero again when its kernels complete,
+ *    so a workspace can be reused without clearing.
  */
 #ifndef TB_H
 #define TB_H

@@ -110,7 +110,7 @@ def _ws(workspace):
 
 
 def new_workspace(nbytes, device="cuda"):
-    """A zero-filled workspace of at least nbytes (the calls keep it zeroed)."""
+    """A zero-filled workspace of at least nbytes (calls leave what must start at zero zeroed)."""
     return torch.zeros(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 

@@ -11,20 +11,23 @@
 // position on ties). The greedy order is exactly descending key order, the
 // keys are distinct, and the important buffer is the min(K, |E|) largest keys.
 //
-// Five launches, all integer work:
-//   hist     per (segment, 2048-token chunk): pooled keys from LDS-staged
-//            scores; 4096-bin LDS histogram of the top 12 key bits (runs of
-//            equal bins in neighbouring lanes are added once), merged into a
-//            per-segment global histogram with atomics;
-//   boundary one workgroup per segment finds the boundary bin once and
-//            returns the histogram to zero;
-//   classify same grid: tokens above the boundary bin go straight into a
-//            selection bitmap (wave ballots); tokens in it are gathered in LDS
-//            and written to the chunk's own slots of the candidate list;
-//   thr      one 1024-thread workgroup per segment: gathers the chunks'
-//            candidates, exact select of the remaining quota among them (10-bit
-//            radix passes narrow the boundary group to at most 64 keys, which
-//            are ranked directly), then each chunk's offset in the output list;
+// Four launches, all integer work:
+//   bounds   eight 1024-thread workgroups per segment sample the pooled key32
+//            of every stride-th eligible token (every token when the region
+//            holds at most 8192); the last to arrive takes sample ranks on
+//            either side of the budget's rank, 5 sigma of the sample rank
+//            apart, as a band [T_lo, T_hi] that holds the K-th key with
+//            overwhelming odds;
+//   classify per (segment, 2048-token chunk): tokens above the band go
+//            straight into a selection bitmap (wave ballots); tokens in it are
+//            gathered in LDS and written to the chunk's own candidate slots;
+//   thr      one 1024-thread workgroup per segment: checks that the K-th key
+//            lies in the band, gathers the candidates, exact select of the
+//            remaining quota among them (10-bit radix passes narrow the group
+//            to at most 64 keys, which are ranked directly), then each chunk's
+//            offset in the output list. If the band missed (a sample that
+//            misrepresents the segment), the workgroup instead selects exactly
+//            over every eligible token and writes the list itself;
 //   compact  one wave per chunk: bitmap words ORed with the chunk's chosen
 //            candidates and the sink / window bits, emitted as ascending
 //            positions with coalesced stores.
@@ -33,10 +36,13 @@
 namespace tb {
 namespace {
 
-constexpr int HBITS = 12;
-constexpr int NBINS = 1 << HBITS;
-constexpr int CHUNK = 2048;          // tokens per hist/classify workgroup
-constexpr int T1 = 256;              // threads of hist/classify
+constexpr int CHUNK = 2048;          // tokens per classify workgroup
+constexpr int T1 = 256;              // threads of classify
+constexpr int NSAMP = 8192;          // sample keys per segment (at most)
+constexpr int BG = 8;                // bounds workgroups per segment
+constexpr int QB = 12;               // bits per level of the band's histograms
+constexpr int QBINS = 1 << QB;
+constexpr float MARGIN_SIGMAS = 5.f; // half-width of the band in sample-rank std
 constexpr int MAXR = 64;
 constexpr int T3 = 1024;             // threads of finalize
 constexpr int LDS_CAND = 8192;       // candidates held in LDS by finalize
@@ -138,123 +144,213 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *s_w, u
     return before + x;
 }
 
-// Boundary of the top `need` among a 4096-bin histogram (bin 4095 highest):
-// bin B1 with above(B1) < need <= above(B1) + hist[B1]; need1 = need -
-// above(B1). Thread t owns the t-th group of PER bins counted from the top.
-// Block-wide; the result lands in *s_bin / *s_need (LDS, left unchanged when
-// the histogram holds fewer than `need` entries).
-template <int NT>
-struct HistSlice {
-    static constexpr int PER = NBINS / NT;
-    uint32_t v[PER];
-    // thread t owns the t-th group of PER bins counted from the top
-    __device__ __forceinline__ void load(const uint32_t *hist) {
-        const int top = NBINS - ((int)threadIdx.x + 1) * PER;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) v[i] = hist[top + i];
+// Pooled key of eligible token t read straight from the scores (global).
+__device__ __forceinline__ uint64_t pooled_key_g(const float *s, int t, int e0, int e1, int r) {
+    const int a = t - r < e0 ? e0 : t - r;
+    const int z = t + r >= e1 ? e1 - 1 : t + r;
+    uint32_t best = order_key(s[a]);
+    int c = a;
+    for (int u = a + 1; u <= z; ++u) {
+        const uint32_t k = order_key(s[u]);
+        if (k > best) {
+            best = k;
+            c = u;
+        }
     }
-};
+    const int d = t < c ? c - t : t - c;
+    const uint32_t low = ((uint32_t)(0xffffff - c) << 8) | ((uint32_t)(0x7f - d) << 1) |
+                         (uint32_t)(t <= c ? 1 : 0);
+    return ((uint64_t)best << 32) | low;
+}
 
-template <int NT>
-__device__ void find_boundary(const HistSlice<NT> &hs, int need, int *s_bin, int *s_need,
-                              uint32_t *s_w) {
-    constexpr int PER = HistSlice<NT>::PER;
-    const int top = NBINS - ((int)threadIdx.x + 1) * PER;
-    uint32_t sum = 0;
+// Band edges from the n sample keys held PER to a thread (key i * T3 + tid in
+// v[i], zero past n): t_hi >= the key of rank ka and t_lo <= the key of rank
+// kb (ranks 0-based, descending), each the outer edge of the 24-bit bin that
+// holds that key (two 12-bit histogram levels: top bits over all keys, then
+// bits 19..8 within each rank's top bin). The band only has to contain the
+// budget's key, so bin edges serve as well as the exact order statistics.
+// Block-wide, T3 threads; s_hist holds 2 * QBINS counters, s_w T3 / 64,
+// s_sel 4.
+template <int PER>
+__device__ __forceinline__ void band_edges(const uint32_t (&v)[PER], int n, int ka, int kb,
+                                           uint32_t *s_hist, uint32_t *s_w, int *s_sel,
+                                           uint32_t *t_hi, uint32_t *t_lo) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // level 1: bins of the top QB bits, bin index = descending digit
+    for (int i = tid; i < QBINS; i += T3) s_hist[i] = 0u;
+    __syncthreads();
 #pragma unroll
-    for (int i = 0; i < PER; ++i) sum += hs.v[i];
-    uint32_t total;
-    const uint32_t incl = block_incl_scan<NT>(sum, s_w, &total);
-    const uint32_t above = incl - sum;
-    if (above < (uint32_t)need && (uint32_t)need <= incl) {
-        uint32_t acc = above;
+    for (int i = 0; i < PER; ++i)
+        if (i * T3 + tid < n) atomicAdd(&s_hist[QBINS - 1 - (v[i] >> (32 - QB))], 1u);
+    __syncthreads();
+    {
+        constexpr int PB = QBINS / T3;
+        uint32_t c[PB], sum = 0;
 #pragma unroll
-        for (int i = PER - 1; i >= 0; --i) {
-            if (acc + hs.v[i] >= (uint32_t)need) {
-                *s_bin = top + i;
-                *s_need = need - (int)acc;
-                break;
+        for (int u = 0; u < PB; ++u) {
+            c[u] = s_hist[tid * PB + u];
+            sum += c[u];
+        }
+        uint32_t tot;
+        uint32_t run = block_incl_scan<T3>(sum, s_w, &tot) - sum;
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int d = QBINS - 1 - (tid * PB + u);
+            if (c[u] > 0 && run <= (uint32_t)ka && (uint32_t)ka < run + c[u]) {
+                s_sel[0] = d;
+                s_sel[1] = ka - (int)run;
             }
-            acc += hs.v[i];
+            if (c[u] > 0 && run <= (uint32_t)kb && (uint32_t)kb < run + c[u]) {
+                s_sel[2] = d;
+                s_sel[3] = kb - (int)run;
+            }
+            run += c[u];
         }
     }
     __syncthreads();
+    const uint32_t da = (uint32_t)s_sel[0], db = (uint32_t)s_sel[2];
+    const int ka2 = s_sel[1], kb2 = s_sel[3];
+    // level 2: bits 19..8 of the keys in each rank's top bin (histograms A, B)
+    for (int i = tid; i < 2 * QBINS; i += T3) s_hist[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const uint32_t key = v[i], top = key >> (32 - QB);
+        const int d = QBINS - 1 - (int)((key >> (32 - 2 * QB)) & (QBINS - 1));
+        const bool in = i * T3 + tid < n;
+        if (in && top == da) atomicAdd(&s_hist[d], 1u);
+        if (in && top == db) atomicAdd(&s_hist[QBINS + d], 1u);
+    }
+    __syncthreads();
+    {
+        // threads [0, T3/2) scan histogram A, [T3/2, T3) histogram B
+        constexpr int PB = 2 * QBINS / T3;
+        uint32_t c[PB], sum = 0;
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            c[u] = s_hist[tid * PB + u];
+            sum += c[u];
+        }
+        uint32_t x = sum;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_up(x, off);
+            if (lane >= off) x += y;
+        }
+        if (lane == 63) s_w[wave] = x;
+        __syncthreads();
+        constexpr int HW = T3 / 128;   // waves per half
+        uint32_t run = 0;
+        for (int w = wave < HW ? 0 : HW; w < wave; ++w) run += s_w[w];
+        run += x - sum;
+        const bool A = tid < T3 / 2;
+        const int kk = A ? ka2 : kb2;
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            if (c[u] > 0 && run <= (uint32_t)kk && (uint32_t)kk < run + c[u]) {
+                s_sel[A ? 0 : 2] = QBINS - 1 - ((tid * PB + u) & (QBINS - 1));
+            }
+            run += c[u];
+        }
+    }
+    __syncthreads();
+    *t_hi = (da << (32 - QB)) | ((uint32_t)s_sel[0] << (32 - 2 * QB)) | ((1u << (32 - 2 * QB)) - 1u);
+    *t_lo = (db << (32 - QB)) | ((uint32_t)s_sel[2] << (32 - 2 * QB));
 }
 
-__global__ __launch_bounds__(T1) void hist_kernel(const float *__restrict__ scores,
-                                                  const int32_t *__restrict__ ctx,
-                                                  const int32_t *__restrict__ plen, int Hq,
-                                                  int Lmax, int S, int W, int K, int r,
-                                                  uint32_t *__restrict__ ghist) {
-    __shared__ uint32_t sk[CHUNK + 2 * MAXR];
-    __shared__ uint32_t lh[NBINS];
+// Workgroup x of a segment samples j in [x * T3, (x + 1) * T3). R >= 0: the
+// radius is R (a thread's neighbour loads are all issued before any is used);
+// R < 0: any radius, read token by token. Samples go to samp[seg] with
+// agent-scope stores; the last workgroup to arrive reads them back with
+// agent-scope loads, resets the arrival counter and writes the band.
+template <int R>
+__global__ __launch_bounds__(T3) void bounds_kernel(const float *__restrict__ scores,
+                                                    const int32_t *__restrict__ ctx,
+                                                    const int32_t *__restrict__ plen, int Hq,
+                                                    int Lmax, int S, int W, int K, int r,
+                                                    uint32_t *__restrict__ samp,
+                                                    uint32_t *__restrict__ bctr,
+                                                    uint32_t *__restrict__ info) {
+    static_assert(BG * T3 == NSAMP, "one sample per thread");
+    __shared__ uint32_t s_hist[2 * QBINS];
+    __shared__ uint32_t s_w[T3 / 64];
+    __shared__ int s_sel[4];
+    __shared__ bool s_last;
     const int seg = blockIdx.y, b = seg / Hq;
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
-    if (g.bad || g.need == 0 || g.need == g.e1 - g.e0) return;
-    const int c0 = blockIdx.x * CHUNK;
-    const int a = c0 > g.e0 ? c0 : g.e0;
-    const int z = c0 + CHUNK < g.e1 ? c0 + CHUNK : g.e1;
-    if (a >= z) return;
-    const int lo = a - r, hi = z + r;
-    const float *s = scores + (size_t)seg * Lmax;
-    stage_keys<T1>(sk, s, lo, hi, g.e0, g.e1);
-    for (int i = threadIdx.x; i < NBINS; i += T1) lh[i] = 0u;
-    __syncthreads();
-    const int lane = threadIdx.x & 63;
-    for (int base = a + (int)(threadIdx.x & ~63); base < z; base += T1) {
-        const int t = base + lane;
-        const bool valid = t < z;
-        const uint32_t bin = valid ? (uint32_t)(pooled_key(sk, lo, t, g.e0, g.e1, r) >> (64 - HBITS))
-                                   : 0xffffffffu;
-        // valid lanes are a prefix of the wave; add each run of equal bins once
-        const uint32_t prev = __shfl_up(bin, 1);
-        const bool start = valid && (lane == 0 || prev != bin);
-        const uint64_t edges = __ballot(start || !valid);
-        if (start) {
-            const uint64_t after = lane == 63 ? 0ull : edges & (~0ull << (lane + 1));
-            const int end = after ? __ffsll((long long)after) - 1 : 64;
-            atomicAdd(&lh[bin], (uint32_t)(end - lane));
-        }
-    }
-    __syncthreads();
-    uint32_t *gh = ghist + (size_t)seg * NBINS;
-    for (int i = threadIdx.x; i < NBINS; i += T1)
-        if (lh[i]) atomicAdd(&gh[i], lh[i]);
-}
-
-// One workgroup per segment: the boundary bin of the complete histogram
-// (written to info), then the histogram is returned to zero for the next call.
-__global__ __launch_bounds__(T1) void boundary_kernel(const int32_t *__restrict__ ctx,
-                                                      const int32_t *__restrict__ plen, int Hq,
-                                                      int Lmax, int S, int W, int K,
-                                                      uint32_t *__restrict__ ghist,
-                                                      int32_t *__restrict__ info) {
-    __shared__ uint32_t s_w[T1 / 64];
-    __shared__ int s_bin, s_need;
-    const int seg = blockIdx.x, b = seg / Hq;
-    const Region g = region(ctx, plen, b, Lmax, S, W, K);
-    if (g.bad || g.need == 0 || g.need == g.e1 - g.e0) return;
-    uint32_t *gh = ghist + (size_t)seg * NBINS;
-    HistSlice<T1> hs;
-    hs.load(gh);
-    if (threadIdx.x == 0) {
-        s_bin = NBINS;
-        s_need = 0;
-    }
-    find_boundary<T1>(hs, g.need, &s_bin, &s_need, s_w);
-    if (threadIdx.x == 0) {
-        info[2 * seg] = s_bin;
-        info[2 * seg + 1] = s_need;
-    }
-    const int top = NBINS - ((int)threadIdx.x + 1) * HistSlice<T1>::PER;
+    const int nE = g.e1 - g.e0;
+    if (g.bad || g.need == 0 || g.need == nE) return;   // the same for every workgroup of seg
+    const int stride = (nE + NSAMP - 1) / NSAMP;
+    const int off = stride / 2;
+    const int ns = (nE - off + stride - 1) / stride;
+    const float *sc = scores + (size_t)seg * Lmax;
+    uint32_t *sp = samp + (size_t)seg * NSAMP;
+    const int j = blockIdx.x * T3 + threadIdx.x;
+    if (j < ns) {
+        const int t = g.e0 + off + j * stride;
+        uint32_t key;
+        if constexpr (R >= 0) {
+            // key32 of a pooled key = max order key over [t - R, t + R] within
+            // E; a neighbour outside E is clamped onto E's end, which is in range
+            float x[2 * R + 1];
 #pragma unroll
-    for (int i = 0; i < HistSlice<T1>::PER; ++i) gh[top + i] = 0u;
+            for (int u = 0; u <= 2 * R; ++u) {
+                int p = t - R + u;
+                p = p < g.e0 ? g.e0 : (p >= g.e1 ? g.e1 - 1 : p);
+                x[u] = sc[p];
+            }
+            key = order_key(x[0]);
+#pragma unroll
+            for (int u = 1; u <= 2 * R; ++u) {
+                const uint32_t k = order_key(x[u]);
+                key = k > key ? k : key;
+            }
+        } else {
+            key = (uint32_t)(pooled_key_g(sc, t, g.e0, g.e1, r) >> 32);
+        }
+        __hip_atomic_store(sp + j, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // every wave's sample stores complete before the arrival is counted
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0)
+        s_last = __hip_atomic_fetch_add(bctr + seg, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(BG - 1);
+    __syncthreads();
+    if (!s_last) return;
+    if (threadIdx.x == 0) __hip_atomic_store(bctr + seg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    constexpr int PER = NSAMP / T3;
+    uint32_t v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int k = threadIdx.x + i * T3;
+        v[i] = k < ns ? __hip_atomic_load(sp + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    }
+    // sample ranks (0-based from the top) on either side of the budget's rank
+    int rhi, rlo;
+    if (stride == 1) {
+        rhi = rlo = g.need - 1;
+    } else {
+        const float f = (float)g.need / (float)nE;
+        const float p = f * (float)ns;
+        const int m = (int)ceilf(MARGIN_SIGMAS * sqrtf((float)ns * f * (1.f - f))) + 2;
+        rhi = (int)floorf(p) - 1 - m;
+        rlo = (int)ceilf(p) - 1 + m;
+    }
+    uint32_t thi, tlo;
+    band_edges(v, ns, rhi < 0 ? 0 : rhi, rlo >= ns ? ns - 1 : rlo, s_hist, s_w, s_sel, &thi, &tlo);
+    if (rhi < 0) thi = 0xffffffffu;   // nothing is surely above the budget's key
+    if (rlo >= ns) tlo = 0u;          // every key may be a candidate
+    if (threadIdx.x == 0) {
+        info[2 * seg] = tlo;
+        info[2 * seg + 1] = thi;
+    }
 }
 
 __global__ __launch_bounds__(T1) void classify_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx,
     const int32_t *__restrict__ plen, int Hq, int Lmax, int S, int W, int K, int r,
-    const int32_t *__restrict__ info, uint32_t *__restrict__ ccount,
+    const uint32_t *__restrict__ info, uint32_t *__restrict__ ccount,
     uint32_t *__restrict__ acount, int nchunks, uint64_t *__restrict__ cand,
     uint32_t *__restrict__ bitmap, int nwords) {
     __shared__ uint32_t sk[CHUNK + 2 * MAXR];
@@ -272,13 +368,14 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     const int z = c0 + CHUNK < g.e1 ? c0 + CHUNK : g.e1;
     const bool touch = partial && a < z;
     const int lo = a - r, hi = z + r;
-    int B1 = NBINS;
+    uint32_t tlo = 0, thi = 0xffffffffu;
     if (threadIdx.x == 0) {
         s_nc = 0;
         s_na = 0;
     }
     if (touch) {
-        B1 = info[2 * seg];
+        tlo = info[2 * seg];
+        thi = info[2 * seg + 1];
         stage_keys<T1>(sk, scores + (size_t)seg * Lmax, lo, hi, g.e0, g.e1);
     }
     __syncthreads();
@@ -293,9 +390,9 @@ __global__ __launch_bounds__(T1) void classify_kernel(
                 sel = true;
             } else if (touch) {
                 key = pooled_key(sk, lo, t, g.e0, g.e1, r);
-                const int bin = (int)(key >> (64 - HBITS));
-                sel = bin > B1;
-                isc = bin == B1;
+                const uint32_t k32 = (uint32_t)(key >> 32);
+                sel = k32 > thi;
+                isc = !sel && k32 >= tlo;
             }
         }
         const uint64_t m = __ballot(sel);
@@ -375,25 +472,93 @@ __device__ __forceinline__ int fixed_in(int t0, int t1, int slo, int wlo, int L)
     return n > 0 ? n : 0;
 }
 
-// One workgroup per segment: gather the chunks' candidates, find the exact
-// threshold key among them, then every chunk's output offset (above-boundary
-// tokens + chosen candidates + sink / window positions in the chunk, scanned).
+struct KthLds {
+    uint32_t tile[RBINS];
+    uint64_t grp[GMAX];
+    uint32_t w[T3 / 64];
+    int sel[3];
+    uint32_t ng;
+    uint64_t thr;
+};
+
+// The k-th largest (1 <= k <= count) of distinct 64-bit keys that all carry
+// `prefix` on `mask` (every bit at or above `shift`). visit(f) hands each key
+// to f exactly once, from any thread; every thread calls it and it may hold
+// barriers. grp: how many keys carry the prefix (anything above GMAX when
+// unknown). 10-bit radix passes narrow the group to at most GMAX keys, which
+// are ranked directly.
+template <class Visit>
+__device__ __forceinline__ uint64_t kth_largest(const Visit &visit, int k, uint64_t prefix,
+                                                uint64_t mask, int shift, int grp, KthLds &sh) {
+    static_assert(RBINS == T3, "one radix bin per thread");
+    const int tid = threadIdx.x;
+    while (grp > GMAX && shift > 0) {
+        const int width = shift < RBITS ? shift : RBITS;
+        shift -= width;
+        const uint32_t dmask = (1u << width) - 1u;
+        // thread t counts digit (RBINS - 1 - t): thread order = descending digit
+        sh.tile[tid] = 0u;
+        __syncthreads();
+        visit([&](uint64_t key) {
+            if ((key & mask) == prefix)
+                atomicAdd(&sh.tile[RBINS - 1 - (int)((key >> shift) & dmask)], 1u);
+        });
+        __syncthreads();
+        const uint32_t c = sh.tile[tid];
+        uint32_t tot;
+        const uint32_t incl = block_incl_scan<T3>(c, sh.w, &tot);
+        const uint32_t above = incl - c;
+        if (c > 0 && above < (uint32_t)k && (uint32_t)k <= incl) {
+            sh.sel[0] = RBINS - 1 - tid;
+            sh.sel[1] = k - (int)above;
+            sh.sel[2] = (int)c;
+        }
+        __syncthreads();
+        prefix |= (uint64_t)sh.sel[0] << shift;
+        mask |= (uint64_t)dmask << shift;
+        k = sh.sel[1];
+        grp = sh.sel[2];
+        __syncthreads();
+    }
+    if (tid == 0) sh.ng = 0u;
+    __syncthreads();
+    visit([&](uint64_t key) {
+        if ((key & mask) == prefix) {
+            const uint32_t slot = atomicAdd(&sh.ng, 1u);
+            if (slot < (uint32_t)GMAX) sh.grp[slot] = key;
+        }
+    });
+    __syncthreads();
+    const int ng = sh.ng < (uint32_t)GMAX ? (int)sh.ng : GMAX;
+    if (tid < ng) {
+        const uint64_t mine = sh.grp[tid];
+        int rank = 0;
+        for (int j = 0; j < ng; ++j) rank += sh.grp[j] > mine ? 1 : 0;
+        if (rank == k - 1) sh.thr = mine;
+    }
+    __syncthreads();
+    return sh.thr;
+}
+
+// One workgroup per segment. With A tokens above the band and C candidates
+// in it, the band holds the budget's key iff 0 <= need - A <= C; then the
+// (need - A)-th largest candidate is the threshold and every chunk's output
+// offset (above-band tokens + chosen candidates + sink / window positions in
+// the chunk) is scanned. Otherwise the workgroup finds the threshold over
+// every eligible token and rewrites the eligible part of the bitmap itself
+// (compact then takes no candidates).
 __global__ __launch_bounds__(T3) void thr_kernel(
-    const int32_t *__restrict__ ctx, const int32_t *__restrict__ plen, int Hq, int Lmax, int S,
-    int W, int K, int omit_window, const int32_t *__restrict__ info,
-    const uint32_t *__restrict__ ccount, const uint32_t *__restrict__ acount, int nchunks,
-    const uint64_t *__restrict__ cand, uint64_t *__restrict__ thr_out,
+    const float *__restrict__ scores, const int32_t *__restrict__ ctx,
+    const int32_t *__restrict__ plen, int Hq, int Lmax, int S, int W, int K, int r,
+    int omit_window, const uint32_t *__restrict__ info, const uint32_t *__restrict__ ccount,
+    const uint32_t *__restrict__ acount, int nchunks, const uint64_t *__restrict__ cand,
+    uint32_t *__restrict__ bitmap, int nwords, uint64_t *__restrict__ thr_out,
     uint32_t *__restrict__ coff, int32_t *__restrict__ count) {
     __shared__ uint64_t s_cand[LDS_CAND];
     __shared__ uint16_t s_cc[LDS_CAND];          // chunk of each LDS candidate
     __shared__ uint32_t s_off[MAX_CHUNKS];
     __shared__ uint32_t s_chosen[MAX_CHUNKS];
-    __shared__ uint32_t s_tile[RBINS];
-    __shared__ uint64_t s_grp[GMAX];
-    __shared__ uint32_t s_w[T3 / 64];
-    __shared__ int s_bin, s_need, s_cnt;
-    __shared__ uint32_t s_ng;
-    __shared__ uint64_t s_thr;
+    __shared__ KthLds s_k;
 
     const int seg = blockIdx.x, b = seg / Hq;
     const int tid = threadIdx.x;
@@ -409,7 +574,7 @@ __global__ __launch_bounds__(T3) void thr_kernel(
     const int slo = S < L ? S : L;
     constexpr int PC = MAX_CHUNKS / T3;
     uint32_t cc[PC], ac[PC];
-    uint32_t csum = 0;
+    uint32_t csum = 0, asum = 0;
 #pragma unroll
     for (int j = 0; j < PC; ++j) {
         const int c = tid * PC + j;
@@ -417,113 +582,110 @@ __global__ __launch_bounds__(T3) void thr_kernel(
         cc[j] = in && partial ? ccount[(size_t)seg * nchunks + c] : 0u;
         ac[j] = in ? acount[(size_t)seg * nchunks + c] : 0u;
         csum += cc[j];
+        asum += ac[j];
         if (c < nchunks) s_chosen[c] = 0u;
     }
-    int nc = 0;
     uint64_t thr = ~0ull;   // candidates with key >= thr are chosen (none by default)
     const uint64_t *cl = cand + (size_t)seg * Lmax;
-    bool lds = true;
     if (partial) {
-        int k = info[2 * seg + 1];
-        const int B1 = info[2 * seg];
-        uint32_t total;
-        uint32_t run = block_incl_scan<T3>(csum, s_w, &total) - csum;
+        uint32_t nc, above;
+        uint32_t run = block_incl_scan<T3>(csum, s_k.w, &nc) - csum;
 #pragma unroll
         for (int j = 0; j < PC; ++j) {
             const int c = tid * PC + j;
             if (c < nchunks) s_off[c] = run;
             run += cc[j];
         }
-        nc = (int)total;
-        lds = nc <= LDS_CAND;
-        __syncthreads();
-        if (lds) {
-            constexpr int PER = LDS_CAND / T3;
-            uint64_t v[PER];
-            int vc[PER];
+        block_incl_scan<T3>(asum, s_k.w, &above);
+        const int need1 = g.need - (int)above;
+        if (need1 >= 0 && need1 <= (int)nc) {
+            if (need1 == (int)nc) {
+                thr = 0ull;   // every candidate is chosen
 #pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const int i = tid + j * T3;
-                vc[j] = 0;
-                v[j] = 0ull;
-                if (i < nc) {
-                    vc[j] = chunk_of(s_off, nchunks, (uint32_t)i);
-                    v[j] = cl[(size_t)vc[j] * CHUNK + ((uint32_t)i - s_off[vc[j]])];
+                for (int j = 0; j < PC; ++j) {
+                    const int c = tid * PC + j;
+                    if (c < nchunks) s_chosen[c] = cc[j];
                 }
-            }
+            } else if (need1 > 0) {
+                const bool lds = nc <= (uint32_t)LDS_CAND;
+                if (lds) {
+                    constexpr int PER = LDS_CAND / T3;
+                    uint64_t v[PER];
+                    int vc[PER];
 #pragma unroll
-            for (int j = 0; j < PER; ++j) {
-                const int i = tid + j * T3;
-                if (i < nc) {
-                    s_cand[i] = v[j];
-                    s_cc[i] = (uint16_t)vc[j];
+                    for (int j = 0; j < PER; ++j) {
+                        const int i = tid + j * T3;
+                        vc[j] = 0;
+                        v[j] = 0ull;
+                        if (i < (int)nc) {
+                            vc[j] = chunk_of(s_off, nchunks, (uint32_t)i);
+                            v[j] = cl[(size_t)vc[j] * CHUNK + ((uint32_t)i - s_off[vc[j]])];
+                        }
+                    }
+#pragma unroll
+                    for (int j = 0; j < PER; ++j) {
+                        const int i = tid + j * T3;
+                        if (i < (int)nc) {
+                            s_cand[i] = v[j];
+                            s_cc[i] = (uint16_t)vc[j];
+                        }
+                    }
                 }
-            }
-            __syncthreads();
-        }
-        if (k >= nc) {
-            thr = 0ull;   // every candidate is chosen
-        } else {
-            // the k-th largest key (all keys are distinct) among the candidates
-            uint64_t prefix = (uint64_t)B1 << (64 - HBITS);
-            uint64_t mask = (uint64_t)(NBINS - 1) << (64 - HBITS);
-            int grp = nc;
-            int shift = 64 - HBITS;
-            while (grp > GMAX && shift > 0) {
-                const int width = shift < RBITS ? shift : RBITS;
-                shift -= width;
-                const uint32_t dmask = (1u << width) - 1u;
-                // thread t counts digit (RBINS - 1 - t): thread order = descending digit
-                s_tile[tid] = 0u;
                 __syncthreads();
-                for (int i = tid; i < nc; i += T3) {
+                auto visit_cand = [&](auto f) {
+                    for (int i = tid; i < (int)nc; i += T3)
+                        f(lds ? s_cand[i] : cand_at(cl, s_off, nchunks, (uint32_t)i));
+                };
+                // candidates share the key32 bits on which the band's ends agree
+                const uint32_t tlo = info[2 * seg], thi = info[2 * seg + 1];
+                const uint32_t x = tlo ^ thi;
+                const int shift = 32 + (x ? 32 - __clz((int)x) : 0);
+                const uint64_t mask = shift >= 64 ? 0ull : (~0ull << shift);
+                thr = kth_largest(visit_cand, need1, ((uint64_t)thi << 32) & mask, mask, shift,
+                                  (int)nc, s_k);
+                for (int i = tid; i < (int)nc; i += T3) {
                     const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
-                    if ((key & mask) == prefix)
-                        atomicAdd(&s_tile[RBINS - 1 - (int)((key >> shift) & dmask)], 1u);
-                }
-                __syncthreads();
-                const uint32_t c = s_tile[tid];
-                uint32_t tot;
-                const uint32_t incl = block_incl_scan<T3>(c, s_w, &tot);
-                const uint32_t above = incl - c;
-                if (c > 0 && above < (uint32_t)k && (uint32_t)k <= incl) {
-                    s_bin = RBINS - 1 - tid;
-                    s_need = k - (int)above;
-                    s_cnt = (int)c;
-                }
-                __syncthreads();
-                prefix |= (uint64_t)s_bin << shift;
-                mask |= (uint64_t)dmask << shift;
-                k = s_need;
-                grp = s_cnt;
-                __syncthreads();
-            }
-            // rank the (at most GMAX) keys that carry the prefix
-            if (tid == 0) s_ng = 0;
-            __syncthreads();
-            for (int i = tid; i < nc; i += T3) {
-                const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
-                if ((key & mask) == prefix) {
-                    const uint32_t slot = atomicAdd(&s_ng, 1u);
-                    if (slot < (uint32_t)GMAX) s_grp[slot] = key;
+                    if (key >= thr)
+                        atomicAdd(&s_chosen[lds ? (int)s_cc[i] : chunk_of(s_off, nchunks, i)], 1u);
                 }
             }
-            __syncthreads();
-            const int ng = s_ng < (uint32_t)GMAX ? (int)s_ng : GMAX;
-            if (tid < ng) {
-                const uint64_t mine = s_grp[tid];
-                int rank = 0;
-                for (int j = 0; j < ng; ++j) rank += s_grp[j] > mine ? 1 : 0;
-                if (rank == k - 1) s_thr = mine;
+        } else {
+            // the band missed the budget's key: exact selection over every
+            // eligible token, pooled keys rebuilt from the scores tile by tile
+            const float *sc = scores + (size_t)seg * Lmax;
+            uint32_t *sk = reinterpret_cast<uint32_t *>(s_cand);
+            auto visit_all = [&](auto f) {
+                for (int a = g.e0; a < g.e1; a += CHUNK) {
+                    const int z = a + CHUNK < g.e1 ? a + CHUNK : g.e1;
+                    __syncthreads();
+                    stage_keys<T3>(sk, sc, a - r, z + r, g.e0, g.e1);
+                    __syncthreads();
+                    for (int t = a + tid; t < z; t += T3) f(pooled_key(sk, a - r, t, g.e0, g.e1, r));
+                }
+            };
+            const uint64_t kth = kth_largest(visit_all, g.need, 0ull, 0ull, 64, nE, s_k);
+            uint32_t *bm = bitmap + (size_t)seg * nwords;
+            const int lane = tid & 63, wave = tid >> 6;
+            for (int c0 = (g.e0 / CHUNK) * CHUNK; c0 < g.e1; c0 += CHUNK) {
+                const int a = c0 > g.e0 ? c0 : g.e0;
+                const int z = c0 + CHUNK < g.e1 ? c0 + CHUNK : g.e1;
+                __syncthreads();
+                stage_keys<T3>(sk, sc, a - r, z + r, g.e0, g.e1);
+                __syncthreads();
+                for (int base = c0 + wave * 64; base < c0 + CHUNK; base += T3) {
+                    const int t = base + lane;
+                    const bool sel = t >= a && t < z && pooled_key(sk, a - r, t, g.e0, g.e1, r) >= kth;
+                    const uint64_t m = __ballot(sel);
+                    if (lane == 0 && base + 64 > a && base < z) {
+                        const int w = base >> 5;
+                        bm[w] = (uint32_t)m;
+                        if (w + 1 < nwords) bm[w + 1] = (uint32_t)(m >> 32);
+                        if (m) atomicAdd(&s_chosen[c0 / CHUNK], (uint32_t)__popcll(m));
+                    }
+                }
             }
-            __syncthreads();
-            thr = s_thr;
-        }
-        // chosen candidates per chunk
-        for (int i = tid; i < nc; i += T3) {
-            const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
-            if (key >= thr)
-                atomicAdd(&s_chosen[lds ? (int)s_cc[i] : chunk_of(s_off, nchunks, i)], 1u);
+#pragma unroll
+            for (int j = 0; j < PC; ++j) ac[j] = 0u;   // counted in s_chosen instead
         }
     }
     __syncthreads();
@@ -539,7 +701,7 @@ __global__ __launch_bounds__(T3) void thr_kernel(
         lsum += tot_c[j];
     }
     uint32_t total;
-    uint32_t run = block_incl_scan<T3>(lsum, s_w, &total) - lsum;
+    uint32_t run = block_incl_scan<T3>(lsum, s_k.w, &total) - lsum;
 #pragma unroll
     for (int j = 0; j < PC; ++j) {
         const int c = tid * PC + j;
@@ -578,8 +740,8 @@ __global__ __launch_bounds__(64) void compact_kernel(
     uint32_t n = 0;
     uint64_t thr = 0;
     if (partial) {
-        n = ccount[(size_t)seg * nchunks + c];
         thr = thr_in[seg];
+        n = thr == ~0ull ? 0u : ccount[(size_t)seg * nchunks + c];
     }
     bits |= bits_below(slo - t0);
     bits |= bits_below(L - t0) & ~bits_below(wlo - t0);
@@ -629,17 +791,18 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
     const int nwords = (Lmax + 31) / 32 + 1;
     const int nchunks = (Lmax + CHUNK - 1) / CHUNK;
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t hist_b = up(nseg * NBINS * 4);
+    const size_t bctr_b = up(nseg * 4);
     const size_t info_b = up(nseg * 8);
     const size_t cc_b = up(nseg * (size_t)nchunks * 4);
     const size_t thr_b = up(nseg * 8);
     const size_t bm_b = up(nseg * (size_t)nwords * 4);
     const size_t cand_b = up(nseg * (size_t)Lmax * 8);
+    const size_t samp_b = up(nseg * (size_t)NSAMP * 4);
     if (base && out) {
         char *p = static_cast<char *>(base);
-        out->hist = reinterpret_cast<uint32_t *>(p);
-        p += hist_b;
-        out->info = reinterpret_cast<int32_t *>(p);
+        out->bctr = reinterpret_cast<uint32_t *>(p);
+        p += bctr_b;
+        out->info = reinterpret_cast<uint32_t *>(p);
         p += info_b;
         out->ccount = reinterpret_cast<uint32_t *>(p);
         p += cc_b;
@@ -652,10 +815,12 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
         out->bitmap = reinterpret_cast<uint32_t *>(p);
         p += bm_b;
         out->cand = reinterpret_cast<uint64_t *>(p);
+        p += cand_b;
+        out->samp = reinterpret_cast<uint32_t *>(p);
         out->nwords = nwords;
         out->nchunks = nchunks;
     }
-    return hist_b + info_b + 3 * cc_b + thr_b + bm_b + cand_b;
+    return bctr_b + info_b + 3 * cc_b + thr_b + bm_b + cand_b + samp_b;
 }
 
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
@@ -664,22 +829,20 @@ tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *
                         hipStream_t st) {
     const int nseg = B * Hq;
     dim3 grid(ws.nchunks, nseg);
-    hipLaunchKernelGGL(hist_kernel, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W, K,
-                       r, ws.hist);
-    tb_status e = check_launch("tb_select(hist)");
-    if (e) return e;
-    hipLaunchKernelGGL(boundary_kernel, dim3(nseg), dim3(T1), 0, st, ctx, plen, Hq, Lmax, S, W, K,
-                       ws.hist, ws.info);
-    e = check_launch("tb_select(boundary)");
+    auto bounds = r == 0 ? bounds_kernel<0> : r == 1 ? bounds_kernel<1>
+                                        : r == 2 ? bounds_kernel<2> : bounds_kernel<-1>;
+    hipLaunchKernelGGL(bounds, dim3(BG, nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
+                       K, r, ws.samp, ws.bctr, ws.info);
+    tb_status e = check_launch("tb_select(bounds)");
     if (e) return e;
     hipLaunchKernelGGL(classify_kernel, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
                        K, r, ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand, ws.bitmap,
                        ws.nwords);
     e = check_launch("tb_select(classify)");
     if (e) return e;
-    hipLaunchKernelGGL(thr_kernel, dim3(nseg), dim3(T3), 0, st, ctx, plen, Hq, Lmax, S, W, K,
-                       omit_window ? 1 : 0, ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand,
-                       ws.thr, ws.coff, count);
+    hipLaunchKernelGGL(thr_kernel, dim3(nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
+                       K, r, omit_window ? 1 : 0, ws.info, ws.ccount, ws.acount, ws.nchunks,
+                       ws.cand, ws.bitmap, ws.nwords, ws.thr, ws.coff, count);
     e = check_launch("tb_select(threshold)");
     if (e) return e;
     hipLaunchKernelGGL(compact_kernel, grid, dim3(64), 0, st, ctx, plen, Hq, Lmax, S, W, K,

@@ -84,14 +84,15 @@ tb_status launch_score(const float *qhat, int n_slots, int slot, const void *kp,
                        const int32_t *plen, float *scores, int B, int Hq, int Hkv, int Lmax,
                        int dp, hipStream_t st);
 struct SelectWs {
-    uint32_t *hist;      // [nseg][4096], zero at rest
-    int32_t *info;       // [nseg][2] boundary bin, quota inside it
+    uint32_t *bctr;      // [nseg] arrival counters of the band workgroups, zero at rest
+    uint32_t *info;      // [nseg][2] band [T_lo, T_hi] of key32 around the budget's key
     uint32_t *ccount;    // [nseg][nchunks] candidates per chunk
-    uint32_t *acount;    // [nseg][nchunks] tokens above the boundary bin per chunk
+    uint32_t *acount;    // [nseg][nchunks] tokens above the band per chunk
     uint32_t *coff;      // [nseg][nchunks] offset of each chunk in the output list
-    uint64_t *thr;       // [nseg] exact threshold key among the candidates
+    uint64_t *thr;       // [nseg] threshold key among the candidates (~0: none chosen)
     uint32_t *bitmap;    // [nseg][nwords]
     uint64_t *cand;      // [nseg][Lmax], chunk c owns slots [c * CHUNK, ...)
+    uint32_t *samp;      // [nseg][8192] sampled pooled key32
     int nwords;
     int nchunks;
 };

@@ -175,12 +175,69 @@ def test_select_bad_lengths_flagged(tb, orc):
 
 def test_select_workspace_reuse(tb, orc):
     rng = rng_for(57)
-    ws = None
+    B, Hq, Lmax = 2, 8, 9000
+    ws = tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax))
     for i in range(3):
-        s = rng.standard_normal((2, 8, 9000)).astype(np.float32)
+        s = rng.standard_normal((B, Hq, Lmax)).astype(np.float32)
         ws = assert_same_selection(orc, tb, s, [9000, 7777], [9000, 7700], 16, 64, 900, 1,
                                    "reuse %d" % i, ws)
-    assert int(ws[: 2 * 8 * 4096 * 4].count_nonzero()) == 0   # histograms back to zero
+        assert int(ws[: B * Hq * 4].count_nonzero()) == 0   # arrival counters back at zero
+
+
+def _sample_positions(e0, e1):
+    """Eligible positions whose pooled keys the band estimate samples: every
+    stride-th token from e0 + stride // 2, stride = ceil(|E| / 8192)."""
+    n = e1 - e0
+    stride = -(-n // 8192)
+    return np.arange(e0 + stride // 2, e1, stride), stride
+
+
+def _thr_words(ws, B, Hq, Lmax):
+    """Per-segment threshold keys from the selection workspace (~0 = the
+    compaction takes no candidates, as after the exact fallback)."""
+    up = lambda x: (x + 255) // 256 * 256
+    nseg, nchunks = B * Hq, -(-Lmax // 2048)
+    off = up(nseg * 4) + up(nseg * 8) + 3 * up(nseg * nchunks * 4)
+    return host(ws[off: off + nseg * 8].view(torch.int64)).astype(np.uint64)
+
+
+def _around(pos, r, lo, hi):
+    """Positions within r of any of pos, clipped to [lo, hi)."""
+    p = (pos[:, None] + np.arange(-r, r + 1)[None, :]).ravel()
+    return np.unique(p[(p >= lo) & (p < hi)])
+
+
+@pytest.mark.parametrize("r", [0, 1, 2])
+def test_select_band_miss_takes_exact_path(tb, orc, r):
+    """Scores built so that the sampled tokens misrepresent the segment: in
+    head 0 every sampled token outranks every other token (the band sits far
+    above the budget's key), in head 1 every token within r of a sampled one
+    is below all the others, so every sampled pooled key is low (the band sits
+    far below it). Head 2 is plain noise. The result must still equal the
+    oracle's, and heads 0 and 1 must have taken the exact fallback."""
+    rng = rng_for(58, r)
+    B, Hq, L, S, W, K = 1, 3, 70000, 16, 64, 4000
+    s = rng.standard_normal((B, Hq, L)).astype(np.float32)
+    pos, stride = _sample_positions(S, L - W)
+    assert stride > 2 * r + 1
+    s[0, 0, pos] += 100.0
+    s[0, 1, _around(pos, r, S, L - W)] -= 100.0
+    ws = assert_same_selection(orc, tb, s, [L], [L], S, W, K, r, "band miss r=%d" % r)
+    thr = _thr_words(ws, B, Hq, L)
+    none = np.uint64(0xFFFFFFFFFFFFFFFF)
+    assert thr[0] == none and thr[1] == none, thr
+    assert thr[2] != none
+
+
+def test_select_band_miss_with_ties(tb, orc):
+    rng = rng_for(59)
+    B, Hq, L, S, W, K = 1, 2, 70000, 8, 32, 2500
+    for r in (0, 1, 2):
+        s = integer_scores(rng, (B, Hq, L), -3, 4)
+        pos, _ = _sample_positions(S, L - W)
+        s[0, 0, pos] = 9.0
+        s[0, 1, _around(pos, r, S, L - W)] = -9.0
+        assert_same_selection(orc, tb, s, [L], [L], S, W, K, r, "band miss ties r=%d" % r)
 
 
 # ------------------------------------------------------------------ attention
