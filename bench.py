@@ -9,8 +9,11 @@ sink 64, window 256, budget 7872, radius 1, 64 planted 8-token spans.
 
 Inputs are resident in HBM before the timed region; R replicas of every
 per-step input are rotated so that each step reads cold memory (the working
-set of one step fits in the 256 MiB MALL). The dominant kernel (sparse
-attention gather) is timed live with HIP events on its launch stream.
+set of one step fits in the 256 MiB MALL). The timed steps replay a HIP graph
+that holds R consecutive steps (one per replica), as a serving loop would;
+the same steps issued call by call are timed too ("eager"). The dominant
+kernel (sparse attention gather) is timed live with HIP events on its launch
+stream during the eager pass.
 
 Prints one JSON line. Run with --gpus 1 only.
 """
@@ -260,6 +263,8 @@ def main():
     from synthetic.workload import make_layer
 
     torch.cuda.set_device(0)
+    # all work on one non-default stream (graph capture needs one)
+    torch.cuda.set_stream(torch.cuda.Stream())
     if args.copy_calibration:
         n = 1 << 30
         a = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -356,15 +361,37 @@ def main():
     K = args.steps
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(K)]
-    log("timing %d steps" % K)
+    log("timing %d eager steps" % K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         run_step(i, evs[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    eager_elapsed = time.perf_counter() - t0
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg_s = float(np.mean(attn_ms)) / 1e3
+
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(i)
+        return g
+
+    full, rem = divmod(K, R)
+    g_all = capture(run_step, R)
+    g_rem = capture(run_step, rem) if rem else None
+    for _ in range(max(1, args.warmup // R)):
+        g_all.replay()
+    torch.cuda.synchronize()
+    log("timing %d graph-replayed steps" % K)
+    t0 = time.perf_counter()
+    for _ in range(full):
+        g_all.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
 
     # algorithmic bytes of one attention launch: each distinct (kv head, token)
     # row of the g heads' attended sets, K and V, bf16 -- counted from idx
@@ -390,17 +417,25 @@ def main():
 
     stages = None
     if args.stages:
+        # each stage alone, as a graph of that stage over the R replicas
         names = ["predict+project", "score", "select", "attention"]
-        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(200)]
-        for i in range(200):
-            c = calls[i % R]
-            for j, (fn, a) in enumerate(c):
-                sev[i][j].record(stream)
-                fn(*a)
-            sev[i][4].record(stream)
-        torch.cuda.synchronize()
-        stages = {n: round(float(np.median([e[j].elapsed_time(e[j + 1]) for e in sev])) * 1e3, 2)
-                  for j, n in enumerate(names)}
+        stages = {}
+        n_rep = 50
+        for j, n in enumerate(names):
+            def one(i, j=j):
+                fn, a = calls[i % R][j]
+                if fn(*a):
+                    raise RuntimeError(L_.tb_last_error_detail().decode())
+            g = capture(one, R)
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n_rep):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            stages[n] = round(e0.elapsed_time(e1) * 1e3 / (n_rep * R), 2)
 
     traffic = traffic_record()
     res = {
@@ -426,12 +461,19 @@ def main():
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "sparse decode attention gather (attn_kernel<128>)",
                      "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6},
+        "eager_steps_per_s": K / eager_elapsed,
         "step_gbps": step_bytes / step_s / 1e9,
         "step_compulsory_bytes": step_bytes,
         "attended_rows": {"union": union_rows, "per_head": per_head_rows},
     }
     if stages:
         res["stages_us"] = stages
+        # score + select + attention: compulsory bytes are the K' read and the union gather
+        span_us = stages["score"] + stages["select"] + stages["attention"]
+        span_bytes = kp_bytes + union_rows * row_bytes
+        res["score_select_attn"] = {"us": round(span_us, 2), "bytes": span_bytes,
+                                    "gbps": span_bytes / span_us / 1e3,
+                                    "frac": span_bytes / span_us / 1e3 / PEAK_HBM_GBS}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)
         res["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)

@@ -357,8 +357,20 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     __shared__ uint64_t s_cand[CHUNK];
     __shared__ uint32_t s_nc, s_na;
     const int seg = blockIdx.y, b = seg / Hq;
-    const Region g = region(ctx, plen, b, Lmax, S, W, K);
     const int c0 = blockIdx.x * CHUNK;
+    const int lo = c0 - r;   // LDS slot i holds position lo + i
+    // the chunk's scores (with halo) and the band are loaded before the
+    // lengths are known; positions outside E are masked when staged
+    constexpr int PER = (CHUNK + 2 * MAXR + T1 - 1) / T1;
+    const float *sc = scores + (size_t)seg * Lmax;
+    float v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int t = lo + (int)threadIdx.x + k * T1;
+        v[k] = (t >= 0 && t < Lmax && t < c0 + CHUNK + r) ? sc[t] : 0.f;
+    }
+    const uint32_t tlo = info[2 * seg], thi = info[2 * seg + 1];
+    const Region g = region(ctx, plen, b, Lmax, S, W, K);
     uint32_t *bm = bitmap + (size_t)seg * nwords;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nE = g.e1 - g.e0;
@@ -367,16 +379,17 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     const int a = c0 > g.e0 ? c0 : g.e0;
     const int z = c0 + CHUNK < g.e1 ? c0 + CHUNK : g.e1;
     const bool touch = partial && a < z;
-    const int lo = a - r, hi = z + r;
-    uint32_t tlo = 0, thi = 0xffffffffu;
     if (threadIdx.x == 0) {
         s_nc = 0;
         s_na = 0;
     }
     if (touch) {
-        tlo = info[2 * seg];
-        thi = info[2 * seg + 1];
-        stage_keys<T1>(sk, scores + (size_t)seg * Lmax, lo, hi, g.e0, g.e1);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int i = (int)threadIdx.x + k * T1;
+            const int t = lo + i;
+            if (t < c0 + CHUNK + r) sk[i] = (t >= g.e0 && t < g.e1) ? order_key(v[k]) : 0u;
+        }
     }
     __syncthreads();
     // every word of this chunk is written: 64 tokens per wave per step
@@ -562,6 +575,16 @@ __global__ __launch_bounds__(T3) void thr_kernel(
 
     const int seg = blockIdx.x, b = seg / Hq;
     const int tid = threadIdx.x;
+    constexpr int PC = MAX_CHUNKS / T3;
+    uint32_t cc[PC], ac[PC];
+    // per-chunk counts and the band are loaded before the lengths are known
+#pragma unroll
+    for (int j = 0; j < PC; ++j) {
+        const int c = tid * PC + j;
+        cc[j] = c < nchunks ? ccount[(size_t)seg * nchunks + c] : 0u;
+        ac[j] = c < nchunks ? acount[(size_t)seg * nchunks + c] : 0u;
+    }
+    const uint32_t tlo = info[2 * seg], thi = info[2 * seg + 1];
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
     if (g.bad) {
         if (tid == 0) count[seg] = -1;
@@ -572,15 +595,12 @@ __global__ __launch_bounds__(T3) void thr_kernel(
     const int L = g.L;
     const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
     const int slo = S < L ? S : L;
-    constexpr int PC = MAX_CHUNKS / T3;
-    uint32_t cc[PC], ac[PC];
     uint32_t csum = 0, asum = 0;
 #pragma unroll
     for (int j = 0; j < PC; ++j) {
         const int c = tid * PC + j;
-        const bool in = c < nchunks && g.need > 0;
-        cc[j] = in && partial ? ccount[(size_t)seg * nchunks + c] : 0u;
-        ac[j] = in ? acount[(size_t)seg * nchunks + c] : 0u;
+        if (!partial) cc[j] = 0u;
+        if (g.need == 0) ac[j] = 0u;
         csum += cc[j];
         asum += ac[j];
         if (c < nchunks) s_chosen[c] = 0u;
@@ -637,7 +657,6 @@ __global__ __launch_bounds__(T3) void thr_kernel(
                         f(lds ? s_cand[i] : cand_at(cl, s_off, nchunks, (uint32_t)i));
                 };
                 // candidates share the key32 bits on which the band's ends agree
-                const uint32_t tlo = info[2 * seg], thi = info[2 * seg + 1];
                 const uint32_t x = tlo ^ thi;
                 const int shift = 32 + (x ? 32 - __clz((int)x) : 0);
                 const uint64_t mask = shift >= 64 ? 0ull : (~0ull << shift);
@@ -726,22 +745,27 @@ __global__ __launch_bounds__(64) void compact_kernel(
     __shared__ uint32_t s_word[64];
     const int c = blockIdx.x, seg = blockIdx.y, b = seg / Hq;
     const int lane = threadIdx.x;
+    const int w = c * (CHUNK / 32) + lane;
+    const int t0 = w << 5;
+    // the chunk's words, offset, candidate count and the threshold are loaded
+    // before the lengths are known
+    uint32_t bits = w < nwords ? bitmap[(size_t)seg * nwords + w] : 0u;
+    const uint32_t base = coff[(size_t)seg * nchunks + c];
+    const uint32_t nraw = ccount[(size_t)seg * nchunks + c];
+    const uint64_t thr_raw = thr_in[seg];
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
     const int L = g.L;
     if (g.bad || c * CHUNK >= L) return;
     const int nE = g.e1 - g.e0;
     const bool partial = g.need > 0 && g.need < nE;
-    const int w = c * (CHUNK / 32) + lane;
-    const int t0 = w << 5;
     const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
     const int slo = S < L ? S : L;
-    uint32_t bits = (g.need > 0 && w < nwords) ? bitmap[(size_t)seg * nwords + w] : 0u;
-    const uint32_t base = coff[(size_t)seg * nchunks + c];
+    if (g.need == 0) bits = 0u;
     uint32_t n = 0;
     uint64_t thr = 0;
     if (partial) {
-        thr = thr_in[seg];
-        n = thr == ~0ull ? 0u : ccount[(size_t)seg * nchunks + c];
+        thr = thr_raw;
+        n = thr == ~0ull ? 0u : nraw;
     }
     bits |= bits_below(slo - t0);
     bits |= bits_below(L - t0) & ~bits_below(wlo - t0);

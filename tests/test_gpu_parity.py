@@ -192,13 +192,30 @@ def _sample_positions(e0, e1):
     return np.arange(e0 + stride // 2, e1, stride), stride
 
 
-def _thr_words(ws, B, Hq, Lmax):
-    """Per-segment threshold keys from the selection workspace (~0 = the
-    compaction takes no candidates, as after the exact fallback)."""
+def _band_missed(ws, scores, L, S, W, K, r):
+    """Per segment: whether the key band left in the selection workspace
+    misses the budget's key, i.e. with A eligible tokens whose pooled key32
+    lies above the band and C inside it, need - A falls outside [0, C]."""
+    B, Hq, Lmax = scores.shape
     up = lambda x: (x + 255) // 256 * 256
-    nseg, nchunks = B * Hq, -(-Lmax // 2048)
-    off = up(nseg * 4) + up(nseg * 8) + 3 * up(nseg * nchunks * 4)
-    return host(ws[off: off + nseg * 8].view(torch.int64)).astype(np.uint64)
+    info = host(ws[up(B * Hq * 4): up(B * Hq * 4) + B * Hq * 8].view(torch.int32))
+    info = (info.astype(np.int64) & 0xFFFFFFFF).reshape(-1, 2)
+    out = []
+    for b in range(B):
+        e0, e1 = S, max(S, L[b] - W)
+        need = min(K, e1 - e0)
+        for h in range(Hq):
+            u = scores[b, h, e0:e1].view(np.uint32).astype(np.int64)
+            key = np.where(u >> 31, u ^ 0xFFFFFFFF, u ^ 0x80000000)
+            pooled = key.copy()
+            for d in range(1, r + 1):
+                pooled[d:] = np.maximum(pooled[d:], key[:-d])
+                pooled[:-d] = np.maximum(pooled[:-d], key[d:])
+            tlo, thi = info[b * Hq + h, 0], info[b * Hq + h, 1]
+            A = int((pooled > thi).sum())
+            C = int(((pooled >= tlo) & (pooled <= thi)).sum())
+            out.append(not (0 <= need - A <= C))
+    return np.array(out)
 
 
 def _around(pos, r, lo, hi):
@@ -223,10 +240,7 @@ def test_select_band_miss_takes_exact_path(tb, orc, r):
     s[0, 0, pos] += 100.0
     s[0, 1, _around(pos, r, S, L - W)] -= 100.0
     ws = assert_same_selection(orc, tb, s, [L], [L], S, W, K, r, "band miss r=%d" % r)
-    thr = _thr_words(ws, B, Hq, L)
-    none = np.uint64(0xFFFFFFFFFFFFFFFF)
-    assert thr[0] == none and thr[1] == none, thr
-    assert thr[2] != none
+    assert _band_missed(ws, s, [L], S, W, K, r).tolist() == [True, True, False]
 
 
 def test_select_band_miss_with_ties(tb, orc):
