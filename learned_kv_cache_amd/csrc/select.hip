@@ -44,8 +44,8 @@ constexpr int QB = 12;               // bits per level of the band's histograms
 constexpr int QBINS = 1 << QB;
 constexpr float MARGIN_SIGMAS = 5.f; // half-width of the band in sample-rank std
 constexpr int MAXR = 64;
-constexpr int T3 = 1024;             // threads of finalize
-constexpr int LDS_CAND = 8192;       // candidates held in LDS by finalize
+constexpr int T3 = 1024;             // threads of the bounds and threshold kernels
+constexpr int LDS_CAND = 8192;       // candidates held in LDS by the threshold kernel
 constexpr int RBITS = 10;            // radix digit of the exact select
 constexpr int RBINS = 1 << RBITS;
 constexpr int GMAX = 64;             // boundary group size ranked directly
