@@ -61,9 +61,10 @@ def lib():
     L.orc_score.restype = None
     L.orc_score.argtypes = [_f32p, _c_int, _c_int, _u16p, _i32p, _f32p,
                             _c_int, _c_int, _c_int, _c_int, _c_int]
-    L.orc_select.restype = ctypes.c_int
-    L.orc_select.argtypes = [_f32p, _i32p, _i32p, _c_int, _c_int, _c_int,
-                             _c_int, _c_int, _c_int, _c_int, _i32p, _i32p, _c_int]
+    for fn in (L.orc_select, L.orc_select_dilate):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [_f32p, _i32p, _i32p, _c_int, _c_int, _c_int,
+                       _c_int, _c_int, _c_int, _c_int, _i32p, _i32p, _c_int]
     L.orc_sparse_attention.restype = None
     L.orc_sparse_attention.argtypes = [_u16p, _u16p, _u16p, _i32p, _i32p, _c_int,
                                        _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -137,18 +138,20 @@ def score(qhat, kp, proj_len, Hq, n_slots=1, slot=0, fill=np.nan):
     return s
 
 
-def select(scores, ctx_len, proj_len, S, W, K, r, cap=None):
+def select(scores, ctx_len, proj_len, S, W, K, r, cap=None, dilate=False):
     """Fixed-budget important buffer (greedy neighbour fill) unioned with sink
-    and window. Returns (idx int32 [B,Hq,cap] ascending, -1 past count;
+    and window; with dilate=True the top-K centres widened by +-r beyond the
+    budget instead. Returns (idx int32 [B,Hq,cap] ascending, -1 past count;
     count int32 [B,Hq])."""
     s = np.ascontiguousarray(scores, dtype=np.float32)
     B, Hq, Lmax = s.shape
     if cap is None:
-        cap = min(Lmax, S + W + K)
+        cap = min(Lmax, S + W + ((2 * r + 1) * K if dilate else K))
     idx = np.full((B, Hq, cap), -1, np.int32)
     cnt = np.zeros((B, Hq), np.int32)
-    st = lib().orc_select(s, _i32(ctx_len), _i32(proj_len), B, Hq, Lmax,
-                          int(S), int(W), int(K), int(r), idx, cnt, int(cap))
+    fn = lib().orc_select_dilate if dilate else lib().orc_select
+    st = fn(s, _i32(ctx_len), _i32(proj_len), B, Hq, Lmax,
+            int(S), int(W), int(K), int(r), idx, cnt, int(cap))
     if st != 0:
         raise ValueError("oracle select: status %d" % st)
     return idx, cnt

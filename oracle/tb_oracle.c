@@ -307,6 +307,79 @@ int orc_select(const float *scores, const int *ctx_len, const int *proj_len,
     return status;
 }
 
+/*
+ * Neighbour fetching read the other way ("Optimizations", neighbour
+ * fetching: the chosen tokens are widened to take in their neighbours; the
+ * summary leaves open whether the neighbours count against the budget). Per
+ * (b, query head):
+ *   eligible region E and need = min(K, |E|) as for orc_select;
+ *   the centres are the first `need` eligible positions in candidate order
+ *   (descending score under IEEE totalOrder, lower position first on ties);
+ *   every position of E within distance r of a centre is attended (the
+ *   neighbours come on top of the budget, so up to (2r+1) * need of them);
+ *   the attended set is sink U window U that widened set, written ascending.
+ * Returns as orc_select.
+ */
+int orc_select_dilate(const float *scores, const int *ctx_len, const int *proj_len,
+                      int B, int Hq, int Lmax, int S, int W, int K, int r,
+                      int *idx, int *count, int cap)
+{
+    int status = 0;
+    for (int b = 0; b < B; ++b) {
+        int L = ctx_len[b];
+        int P = proj_len[b];
+        if (L < 0 || L > Lmax || P < 0 || P > Lmax) {
+            status = -2;
+            count[(size_t)b * Hq] = -1;
+            continue;
+        }
+        int e0 = S;
+        int e1 = L - W < P ? L - W : P;
+        if (e1 < e0)
+            e1 = e0;
+        int nE = e1 - e0;
+        int need = K < nE ? K : nE;
+        unsigned char *keep = (unsigned char *)calloc((size_t)(L > 0 ? L : 1), 1);
+        int *order = (int *)malloc(sizeof(int) * (size_t)(nE > 0 ? nE : 1));
+        for (int h = 0; h < Hq; ++h) {
+            const float *s = scores + ((size_t)b * Hq + h) * Lmax;
+            memset(keep, 0, (size_t)(L > 0 ? L : 1));
+
+            for (int i = 0; i < nE; ++i)
+                order[i] = e0 + i;
+            g_cmp_scores = s;
+            qsort(order, (size_t)nE, sizeof(int), cmp_candidates);
+
+            for (int i = 0; i < need; ++i) {
+                int c = order[i];
+                for (int t = c - r; t <= c + r; ++t)
+                    if (t >= e0 && t < e1)
+                        keep[t] = 1;
+            }
+
+            for (int t = 0; t < L && t < S; ++t)
+                keep[t] = 1;
+            for (int t = L - W < 0 ? 0 : L - W; t < L; ++t)
+                keep[t] = 1;
+
+            int n = 0;
+            int *dst = idx + ((size_t)b * Hq + h) * cap;
+            for (int t = 0; t < L; ++t)
+                if (keep[t]) {
+                    if (n < cap)
+                        dst[n] = t;
+                    else
+                        status = -1;
+                    ++n;
+                }
+            count[(size_t)b * Hq + h] = n;
+        }
+        free(order);
+        free(keep);
+    }
+    return status;
+}
+
 /* ------------------------------------------------------------------ */
 /* Decode attention over the attended positions only ("Significance":  */
 /* the full cache is kept, only the most relevant tokens are read).     */
