@@ -49,7 +49,7 @@ typedef int tb_status;
 
 /* Neighbour-fetching modes of tb_select (low byte of `mode`). */
 #define TB_NF_FILL 0     /* neighbours count against the fixed budget       */
-#define TB_NF_DILATE 1   /* reserved: neighbours added beyond the budget     */
+#define TB_NF_DILATE 1   /* neighbours of the top-budget centres added beyond it */
 /* Flag of tb_select's `mode`: leave the local window out of idx (the list is
  * sink U important); tb_sparse_decode_attn then adds the window itself from
  * ctx_len, so one selection serves every step of a prediction interval. */
@@ -137,18 +137,24 @@ tb_status tb_score(const float *qhat, int n_slots, int slot, const void *kp,
  *     scores: lower position first); each visited centre c brings c, c-1,
  *     c+1, ..., c-radius, c+radius (those in E and not yet taken) until the
  *     buffer is full (mode TB_NF_FILL);
+ *   with mode TB_NF_DILATE (the other reading of neighbour fetching: the
+ *     neighbours come on top of the budget) the min(budget, |E|) first
+ *     tokens of E in that order are centres and every position of E within
+ *     distance radius of a centre is important;
  *   idx[b, h, 0:count) = sink U window U important, ascending, where
  *     sink = [0, min(sink, L)), window = [max(0, L - window), L), L = ctx_len[b];
  *     with TB_SEL_OMIT_WINDOW in mode the window is left out.
- *   scores  [B, Hq, Lmax] fp32 (read only at eligible positions; finite)
+ *   scores  [B, Hq, Lmax] fp32 (any position in [0, Lmax) may be read; only
+ *           eligible positions' values are used and must be finite)
  *   ctx_len [B], proj_len [B]  int32, device
  *   idx     [B, Hq, cap]  int32 (slots >= count are left unspecified)
  *   count   [B, Hq]       int32 (-1 when ctx_len or proj_len is outside
  *                                [0, Lmax]; idx is then not written)
- * Limits: cap >= min(Lmax, sink + window + budget) (sink + budget with
- * TB_SEL_OMIT_WINDOW); 0 <= radius <= 64;
- * Lmax <= 2^24; sink, window, budget >= 0; mode is TB_NF_FILL, optionally
- * ORed with TB_SEL_OMIT_WINDOW.
+ * Limits: cap >= min(Lmax, sink + window + I) with I = budget (TB_NF_FILL)
+ * or (2 radius + 1) budget (TB_NF_DILATE), the window left out of the sum
+ * with TB_SEL_OMIT_WINDOW; 0 <= radius <= 64; Lmax <= 2^24; sink, window,
+ * budget >= 0; mode is TB_NF_FILL or TB_NF_DILATE, optionally ORed with
+ * TB_SEL_OMIT_WINDOW.
  */
 size_t tb_select_workspace_bytes(int B, int Hq, int Lmax);
 tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *proj_len,

@@ -193,7 +193,7 @@ def tb_select_workspace_bytes(B, Hq, Lmax):
 def tb_select(scores, ctx_len, proj_len, sink, window, budget, radius, idx, count, workspace,
               mode=TB_NF_FILL, stream=None):
     """Sink U window U fixed-budget important tokens (neighbour fill), ascending.
-    mode: TB_NF_FILL, optionally | TB_SEL_OMIT_WINDOW."""
+    mode: TB_NF_FILL or TB_NF_DILATE, optionally | TB_SEL_OMIT_WINDOW."""
     B, Hq, Lmax = scores.shape
     cap = idx.shape[-1]
     if tuple(idx.shape) != (B, Hq, cap) or tuple(count.shape) != (B, Hq):

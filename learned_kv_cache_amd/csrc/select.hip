@@ -733,6 +733,38 @@ __global__ __launch_bounds__(T3) void thr_kernel(
     }
 }
 
+// Wave-wide: lane l holds word l of chunk c (tokens c * CHUNK + 32 l + bit);
+// the set bits are written as ascending positions from list slot `base` on,
+// 64 at a time (a converged binary search over the words' prefix counts gives
+// each lane its word and bit), stopping at cap.
+__device__ __forceinline__ void emit_words(uint32_t mine, int c, uint32_t base, int32_t *dst,
+                                           int cap) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t pop = (uint32_t)__popc(mine);
+    uint32_t incl = pop;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    const uint32_t first = incl - pop;
+    const uint32_t wend = __shfl(incl, 63);
+    for (uint32_t s0 = 0; s0 < wend; s0 += 64) {
+        const uint32_t sl = s0 + (uint32_t)lane;
+        int lo2 = 0;
+#pragma unroll
+        for (int step = 32; step >= 1; step >>= 1) {
+            const uint32_t f = __shfl(first, lo2 + step);
+            if (f <= sl) lo2 += step;
+        }
+        const uint32_t wbits = __shfl(mine, lo2);
+        const uint32_t k = sl - __shfl(first, lo2);
+        const uint32_t p = base + sl;
+        if (sl < wend && p < (uint32_t)cap)
+            dst[p] = ((c * (CHUNK / 32) + lo2) << 5) + select_bit(wbits, k);
+    }
+}
+
 // One wave per (chunk, segment): the chunk's 64 bitmap words, ORed with its
 // chosen candidates and the sink / window bits, are emitted as ascending
 // positions at the chunk's offset with coalesced stores.
@@ -781,33 +813,111 @@ __global__ __launch_bounds__(64) void compact_kernel(
         }
     }
     __syncthreads();
-    const uint32_t mine = s_word[lane];
-    const uint32_t pop = (uint32_t)__popc(mine);
-    uint32_t incl = pop;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-    }
-    const uint32_t first = incl - pop;
-    const uint32_t wend = __shfl(incl, 63);
-    int32_t *dst = idx + (size_t)seg * cap;
-    for (uint32_t s0 = 0; s0 < wend; s0 += 64) {
-        const uint32_t sl = s0 + (uint32_t)lane;
-        int lo2 = 0;
-#pragma unroll
-        for (int step = 32; step >= 1; step >>= 1) {
-            const uint32_t f = __shfl(first, lo2 + step);
-            if (f <= sl) lo2 += step;
-        }
-        const uint32_t wbits = __shfl(mine, lo2);
-        const uint32_t k = sl - __shfl(first, lo2);
-        const uint32_t p = base + sl;
-        if (sl < wend && p < (uint32_t)cap)
-            dst[p] = ((c * (CHUNK / 32) + lo2) << 5) + select_bit(wbits, k);
-    }
+    emit_words(s_word[lane], c, base, idx + (size_t)seg * cap, cap);
 }
 
+
+// Dilation mode, one wave per (chunk, segment): the centres are the top-K
+// tokens found with radius 0 (bitmap words and chosen candidates). Lane l
+// widens word l of the chunk: it ORs the centre bit stream shifted by every
+// distance in [-r, r] (the chunk's words plus HALO words on either side,
+// candidates of the neighbouring chunks included), keeps the eligible bits,
+// and stores the word and the chunk's count.
+constexpr int HALO = (MAXR + 31) / 32;
+__global__ __launch_bounds__(64) void dilate_kernel(
+    const int32_t *__restrict__ ctx, const int32_t *__restrict__ plen, int Hq, int Lmax, int S,
+    int W, int K, int r, const uint32_t *__restrict__ ccount, int nchunks,
+    const uint64_t *__restrict__ cand, const uint32_t *__restrict__ bitmap, int nwords,
+    const uint64_t *__restrict__ thr_in, uint32_t *__restrict__ dbm,
+    uint32_t *__restrict__ dcount) {
+    __shared__ uint32_t s_cw[64 + 2 * HALO + 1];
+    const int c = blockIdx.x, seg = blockIdx.y, b = seg / Hq;
+    const int lane = threadIdx.x;
+    const int w0 = c * (CHUNK / 32) - HALO;   // word of s_cw[0]
+    const Region g = region(ctx, plen, b, Lmax, S, W, K);
+    if (g.bad) return;
+    const int nE = g.e1 - g.e0;
+    const bool partial = g.need > 0 && g.need < nE;
+    const uint64_t thr = partial ? thr_in[seg] : ~0ull;
+    for (int j = lane; j < 64 + 2 * HALO + 1; j += 64) {
+        const int w = w0 + j;
+        s_cw[j] = (g.need > 0 && j < 64 + 2 * HALO && w >= 0 && w < nwords)
+                      ? bitmap[(size_t)seg * nwords + w] : 0u;
+    }
+    __syncthreads();
+    if (thr != ~0ull) {
+        for (int cc = c - 1; cc <= c + 1; ++cc) {
+            if (cc < 0 || cc >= nchunks) continue;
+            const uint32_t n = ccount[(size_t)seg * nchunks + cc];
+            const uint64_t *cl = cand + (size_t)seg * Lmax + (size_t)cc * CHUNK;
+            for (uint32_t i = lane; i < n; i += 64) {
+                const uint64_t key = cl[i];
+                if (key >= thr) {
+                    const int t = key_token(key);
+                    const int j = (t >> 5) - w0;
+                    if (j >= 0 && j < 64 + 2 * HALO) atomicOr(&s_cw[j], 1u << (t & 31));
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int w = c * (CHUNK / 32) + lane;
+    const int t0 = w << 5;
+    uint32_t d = 0;
+    if (g.need > 0) {
+        for (int dd = -r; dd <= r; ++dd) {
+            const int p = 32 * (lane + HALO) + dd;   // >= 0 since 32 * HALO >= r
+            const int q = p >> 5, o = p & 31;
+            d |= o ? (s_cw[q] >> o) | (s_cw[q + 1] << (32 - o)) : s_cw[q];
+        }
+        d &= bits_below(g.e1 - t0) & ~bits_below(g.e0 - t0);
+    }
+    if (w < nwords) dbm[(size_t)seg * nwords + w] = d;
+    uint32_t n = (uint32_t)__popc(d);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off);
+    if (lane == 0) dcount[(size_t)seg * nchunks + c] = n;
+}
+
+// Dilation mode, one wave per (chunk, segment): the chunk's list offset is
+// the widened tokens of the earlier chunks plus the sink / window positions
+// before it; its widened words ORed with the sink / window bits are emitted.
+// The wave of chunk 0 writes the segment's count.
+__global__ __launch_bounds__(64) void emit_dilated_kernel(
+    const int32_t *__restrict__ ctx, const int32_t *__restrict__ plen, int Hq, int Lmax, int S,
+    int W, int K, int omit_window, const uint32_t *__restrict__ dbm, int nwords,
+    const uint32_t *__restrict__ dcount, int nchunks, int32_t *__restrict__ idx,
+    int32_t *__restrict__ count, int cap) {
+    const int c = blockIdx.x, seg = blockIdx.y, b = seg / Hq;
+    const int lane = threadIdx.x;
+    const Region g = region(ctx, plen, b, Lmax, S, W, K);
+    if (g.bad) return;
+    const int L = g.L;
+    const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
+    const int slo = S < L ? S : L;
+    const uint32_t *dc = dcount + (size_t)seg * nchunks;
+    uint32_t before = 0, all = 0;
+    for (int j = lane; j < nchunks; j += 64) {
+        const uint32_t v = dc[j];
+        before += j < c ? v : 0u;
+        all += v;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        before += __shfl_xor(before, off);
+        all += __shfl_xor(all, off);
+    }
+    if (c == 0 && lane == 0) count[seg] = (int32_t)(all + (uint32_t)fixed_in(0, L, slo, wlo, L));
+    if (c * CHUNK >= L) return;
+    const int w = c * (CHUNK / 32) + lane;
+    const int t0 = w << 5;
+    uint32_t bits = w < nwords ? dbm[(size_t)seg * nwords + w] : 0u;
+    bits |= bits_below(slo - t0);
+    bits |= bits_below(L - t0) & ~bits_below(wlo - t0);
+    bits &= bits_below(L - t0);
+    emit_words(bits, c, before + (uint32_t)fixed_in(0, c * CHUNK, slo, wlo, L),
+               idx + (size_t)seg * cap, cap);
+}
 }  // namespace
 
 size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
@@ -822,6 +932,8 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
     const size_t bm_b = up(nseg * (size_t)nwords * 4);
     const size_t cand_b = up(nseg * (size_t)Lmax * 8);
     const size_t samp_b = up(nseg * (size_t)NSAMP * 4);
+    const size_t dbm_b = bm_b;
+    const size_t dc_b = cc_b;
     if (base && out) {
         char *p = static_cast<char *>(base);
         out->bctr = reinterpret_cast<uint32_t *>(p);
@@ -841,38 +953,55 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
         out->cand = reinterpret_cast<uint64_t *>(p);
         p += cand_b;
         out->samp = reinterpret_cast<uint32_t *>(p);
+        p += samp_b;
+        out->dbm = reinterpret_cast<uint32_t *>(p);
+        p += dbm_b;
+        out->dcount = reinterpret_cast<uint32_t *>(p);
         out->nwords = nwords;
         out->nchunks = nchunks;
     }
-    return bctr_b + info_b + 3 * cc_b + thr_b + bm_b + cand_b + samp_b;
+    return bctr_b + info_b + 3 * cc_b + thr_b + bm_b + cand_b + samp_b + dbm_b + dc_b;
 }
 
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
-                        int Hq, int Lmax, int S, int W, int K, int r, bool omit_window,
-                        int32_t *idx, int32_t *count, int cap, const SelectWs &ws,
-                        hipStream_t st) {
+                        int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
+                        bool omit_window, int32_t *idx, int32_t *count, int cap,
+                        const SelectWs &ws, hipStream_t st) {
     const int nseg = B * Hq;
     dim3 grid(ws.nchunks, nseg);
-    auto bounds = r == 0 ? bounds_kernel<0> : r == 1 ? bounds_kernel<1>
-                                        : r == 2 ? bounds_kernel<2> : bounds_kernel<-1>;
+    // dilation: the centres are the plain top-K (radius 0), widened afterwards
+    const int rk = dilate ? 0 : r;
+    auto bounds = rk == 0 ? bounds_kernel<0> : rk == 1 ? bounds_kernel<1>
+                                         : rk == 2 ? bounds_kernel<2> : bounds_kernel<-1>;
     hipLaunchKernelGGL(bounds, dim3(BG, nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
-                       K, r, ws.samp, ws.bctr, ws.info);
+                       K, rk, ws.samp, ws.bctr, ws.info);
     tb_status e = check_launch("tb_select(bounds)");
     if (e) return e;
     hipLaunchKernelGGL(classify_kernel, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
-                       K, r, ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand, ws.bitmap,
+                       K, rk, ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand, ws.bitmap,
                        ws.nwords);
     e = check_launch("tb_select(classify)");
     if (e) return e;
     hipLaunchKernelGGL(thr_kernel, dim3(nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
-                       K, r, omit_window ? 1 : 0, ws.info, ws.ccount, ws.acount, ws.nchunks,
+                       K, rk, omit_window ? 1 : 0, ws.info, ws.ccount, ws.acount, ws.nchunks,
                        ws.cand, ws.bitmap, ws.nwords, ws.thr, ws.coff, count);
     e = check_launch("tb_select(threshold)");
     if (e) return e;
-    hipLaunchKernelGGL(compact_kernel, grid, dim3(64), 0, st, ctx, plen, Hq, Lmax, S, W, K,
-                       omit_window ? 1 : 0, ws.ccount, ws.nchunks, ws.cand, ws.bitmap, ws.nwords,
-                       ws.thr, ws.coff, idx, cap);
-    return check_launch("tb_select(compact)");
+    if (!dilate) {
+        hipLaunchKernelGGL(compact_kernel, grid, dim3(64), 0, st, ctx, plen, Hq, Lmax, S, W, K,
+                           omit_window ? 1 : 0, ws.ccount, ws.nchunks, ws.cand, ws.bitmap,
+                           ws.nwords, ws.thr, ws.coff, idx, cap);
+        return check_launch("tb_select(compact)");
+    }
+    hipLaunchKernelGGL(dilate_kernel, grid, dim3(64), 0, st, ctx, plen, Hq, Lmax, S, W, K, r,
+                       ws.ccount, ws.nchunks, ws.cand, ws.bitmap, ws.nwords, ws.thr, ws.dbm,
+                       ws.dcount);
+    e = check_launch("tb_select(dilate)");
+    if (e) return e;
+    hipLaunchKernelGGL(emit_dilated_kernel, grid, dim3(64), 0, st, ctx, plen, Hq, Lmax, S, W, K,
+                       omit_window ? 1 : 0, ws.dbm, ws.nwords, ws.dcount, ws.nchunks, idx, count,
+                       cap);
+    return check_launch("tb_select(emit dilated)");
 }
 
 }  // namespace tb

@@ -157,13 +157,15 @@ tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *
     TB_REQUIRE(radius <= 64, TB_ERR_UNSUPPORTED_SHAPE, "tb_select: radius > 64");
     TB_REQUIRE((mode & ~(0xff | TB_SEL_OMIT_WINDOW)) == 0, TB_ERR_INVALID_ARGUMENT,
                "tb_select: unknown mode bits 0x%x", mode);
-    TB_REQUIRE((mode & 0xff) == TB_NF_FILL, TB_ERR_UNSUPPORTED_SHAPE,
-               "tb_select: only TB_NF_FILL is implemented");
+    TB_REQUIRE((mode & 0xff) == TB_NF_FILL || (mode & 0xff) == TB_NF_DILATE,
+               TB_ERR_INVALID_ARGUMENT, "tb_select: unknown neighbour mode %d", mode & 0xff);
     const bool omit = (mode & TB_SEL_OMIT_WINDOW) != 0;
-    const long long need_cap = (long long)sink + (omit ? 0 : window) + budget;
+    const bool dilate = (mode & 0xff) == TB_NF_DILATE;
+    const long long imp = dilate ? (2LL * radius + 1) * budget : (long long)budget;
+    const long long need_cap = (long long)sink + (omit ? 0 : window) + imp;
     const long long min_cap = need_cap < Lmax ? need_cap : Lmax;
     TB_REQUIRE(cap >= 1 && cap >= min_cap, TB_ERR_INVALID_ARGUMENT,
-               "tb_select: cap %d < min(Lmax, sink + budget (+ window unless omitted)) = %lld",
+               "tb_select: cap %d < min(Lmax, sink + important (+ window unless omitted)) = %lld",
                cap, min_cap);
     const size_t need = tb_select_workspace_bytes(B, Hq, Lmax);
     TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
@@ -171,7 +173,7 @@ tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *
     tb::SelectWs ws;
     tb::select_ws_layout(B, Hq, Lmax, workspace, &ws);
     return tb::launch_select(scores, ctx_len, proj_len, B, Hq, Lmax, sink, window, budget, radius,
-                             omit, idx, count, cap, ws,
+                             dilate, omit, idx, count, cap, ws,
                              static_cast<hipStream_t>(stream));
 }
 

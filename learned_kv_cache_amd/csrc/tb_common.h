@@ -93,14 +93,16 @@ struct SelectWs {
     uint32_t *bitmap;    // [nseg][nwords]
     uint64_t *cand;      // [nseg][Lmax], chunk c owns slots [c * CHUNK, ...)
     uint32_t *samp;      // [nseg][8192] sampled pooled key32
+    uint32_t *dbm;       // [nseg][nwords] widened bitmap (dilation mode)
+    uint32_t *dcount;    // [nseg][nchunks] widened tokens per chunk (dilation mode)
     int nwords;
     int nchunks;
 };
 size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out);
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
-                        int Hq, int Lmax, int S, int W, int K, int r, bool omit_window,
-                        int32_t *idx, int32_t *count, int cap, const SelectWs &ws,
-                        hipStream_t st);
+                        int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
+                        bool omit_window, int32_t *idx, int32_t *count, int cap,
+                        const SelectWs &ws, hipStream_t st);
 int attn_nsplit(int rows);
 size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr);
 tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32_t *idx,

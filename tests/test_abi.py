@@ -78,7 +78,8 @@ def test_validation_rejects_before_launch(tb):
     assert L.tb_select(*args(4, 16, 32, 65, 0, 52, ws)) == 2
     assert L.tb_select(*args(4, 16, 32, 1, 0, 51, ws)) == 1
     assert L.tb_select(*args(4, 16, 32, 1, 0, 52, 100)) == 3
-    assert L.tb_select(*args(4, 16, 32, 1, 1, 52, ws)) == 2
+    assert L.tb_select(*args(4, 16, 32, 1, 1, 115, ws)) == 1   # DILATE needs S + W + (2r+1)K
+    assert L.tb_select(*args(4, 16, 32, 1, 2, 300, ws)) == 1   # unknown neighbour mode
     # attention: D unsupported, workspace too small, Hq % Hkv
     A = lambda Hq, D, wsb, win=0: (vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 64, None, win, 1, Hq,
                                    2, 300, D, ctypes.c_float(0.1), vp(FAKE), vp(FAKE), wsb, None)

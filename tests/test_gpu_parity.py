@@ -101,24 +101,27 @@ def test_score(tb, orc, B, Hq, Hkv, L, dp, P, ns, slot):
 
 # ------------------------------------------------------------------ selection
 
-def run_select(tb, scores, L, P, S, W, K, r, cap=None, ws=None):
+def run_select(tb, scores, L, P, S, W, K, r, cap=None, ws=None, dilate=False, omit=False):
     B, Hq, Lmax = scores.shape
-    cap = cap or min(Lmax, S + W + K)
+    imp = (2 * r + 1) * K if dilate else K
+    cap = cap or min(Lmax, S + (0 if omit else W) + imp)
     idx = torch.full((B, Hq, cap), -7, dtype=torch.int32, device="cuda")
     cnt = torch.full((B, Hq), -7, dtype=torch.int32, device="cuda")
     if ws is None:
         ws = tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax))
+    mode = (tb.TB_NF_DILATE if dilate else tb.TB_NF_FILL) | (tb.TB_SEL_OMIT_WINDOW if omit else 0)
     tb.tb_select(dev32(scores), dev32(np.asarray(L, np.int32)), dev32(np.asarray(P, np.int32)),
-                 S, W, K, r, idx, cnt, ws)
+                 S, W, K, r, idx, cnt, ws, mode=mode)
     torch.cuda.synchronize()
     return host(idx), host(cnt), ws
 
 
-def assert_same_selection(orc, tb, scores, L, P, S, W, K, r, what, ws=None):
-    say("select", what, scores.shape, S, W, K, r)
-    cap = min(scores.shape[-1], S + W + K)
-    ri, rc = orc.select(scores, np.asarray(L, np.int32), np.asarray(P, np.int32), S, W, K, r, cap)
-    gi, gc, ws = run_select(tb, scores, L, P, S, W, K, r, cap, ws)
+def assert_same_selection(orc, tb, scores, L, P, S, W, K, r, what, ws=None, dilate=False):
+    say("select", what, scores.shape, S, W, K, r, "dilate" if dilate else "fill")
+    cap = min(scores.shape[-1], S + W + ((2 * r + 1) * K if dilate else K))
+    ri, rc = orc.select(scores, np.asarray(L, np.int32), np.asarray(P, np.int32), S, W, K, r, cap,
+                        dilate=dilate)
+    gi, gc, ws = run_select(tb, scores, L, P, S, W, K, r, cap, ws, dilate=dilate)
     assert np.array_equal(gc, rc), what
     for b in range(rc.shape[0]):
         for h in range(rc.shape[1]):
@@ -252,6 +255,69 @@ def test_select_band_miss_with_ties(tb, orc):
         s[0, 0, pos] = 9.0
         s[0, 1, _around(pos, r, S, L - W)] = -9.0
         assert_same_selection(orc, tb, s, [L], [L], S, W, K, r, "band miss ties r=%d" % r)
+
+
+# ------------------------------------------------- selection, dilation mode
+
+@pytest.mark.parametrize("r", [0, 1, 2])
+def test_select_dilate_c1_shapes(tb, orc, r):
+    rng = rng_for(60, r)
+    s = rng.standard_normal((1, 8, 300)).astype(np.float32)
+    assert_same_selection(orc, tb, s, [300], [300], 4, 16, 32, r, "dilate c1 r=%d" % r, dilate=True)
+
+
+def test_select_dilate_c2_shape(tb, orc):
+    rng = rng_for(61)
+    s = rng.standard_normal((1, 32, 65536)).astype(np.float32)
+    assert_same_selection(orc, tb, s, [65536], [65536], 64, 256, 7872, 1, "dilate c2",
+                          dilate=True)
+
+
+def test_select_dilate_ties_edges_and_max_radius(tb, orc):
+    rng = rng_for(62)
+    s = integer_scores(rng, (2, 4, 20000), -3, 4)
+    s[:, :, ::7] = -0.0
+    for r in (1, 2):
+        assert_same_selection(orc, tb, s, [20000, 15001], [20000, 14900], 16, 64, 900, r,
+                              "dilate ints r%d" % r, dilate=True)
+    e = rng.standard_normal((3, 4, 1000)).astype(np.float32)
+    L = [1000, 400, 60]
+    assert_same_selection(orc, tb, e, L, L, 8, 32, 10000, 1, "dilate budget >= |E|", dilate=True)
+    assert_same_selection(orc, tb, e, L, L, 8, 32, 0, 1, "dilate budget 0", dilate=True)
+    assert_same_selection(orc, tb, e, L, [500, 100, 60], 8, 32, 40, 2, "dilate projection lag",
+                          dilate=True)
+    assert_same_selection(orc, tb, e, [1, 1, 2], [1, 1, 2], 0, 0, 1, 3, "dilate tiny", dilate=True)
+    # radius 64 spans chunk boundaries: centres next to every 2048-token edge
+    m = rng.uniform(-1, 0, (1, 2, 9000)).astype(np.float32)
+    m[:, :, [2047, 2048, 4095, 6144, 8191, 100, 8900]] = 5.0
+    assert_same_selection(orc, tb, m, [9000], [9000], 16, 32, 7, 64, "dilate r=64 chunk edges",
+                          dilate=True)
+    assert_same_selection(orc, tb, m, [9000], [9000], 16, 32, 150, 64, "dilate r=64 overlap",
+                          dilate=True)
+
+
+def test_select_dilate_band_miss(tb, orc):
+    rng = rng_for(63)
+    B, Hq, L, S, W, K = 1, 2, 70000, 16, 64, 3000
+    s = rng.standard_normal((B, Hq, L)).astype(np.float32)
+    pos, _ = _sample_positions(S, L - W)
+    s[0, 0, pos] += 100.0
+    s[0, 1, pos] -= 100.0
+    assert_same_selection(orc, tb, s, [L], [L], S, W, K, 2, "dilate band miss", dilate=True)
+
+
+def test_select_dilate_omit_window(tb, orc):
+    rng = rng_for(64)
+    B, Hq, L, S, W, K, r = 2, 4, 6000, 8, 64, 500, 2
+    s = rng.standard_normal((B, Hq, L)).astype(np.float32)
+    Ls = np.array([6000, 4321], np.int32)
+    gi, gc, _ = run_select(tb, s, Ls, Ls, S, W, K, r, dilate=True, omit=True)
+    ri, rc = orc.select(s, Ls, Ls, S, W, K, r, dilate=True)
+    for b in range(B):
+        for h in range(Hq):
+            ref = ri[b, h, :rc[b, h]]
+            ref = ref[ref < Ls[b] - W]
+            assert np.array_equal(gi[b, h, :gc[b, h]], ref), (b, h)
 
 
 # ------------------------------------------------------------------ attention
