@@ -58,6 +58,9 @@ def lib():
     L.orc_project_keys.restype = None
     L.orc_project_keys.argtypes = [_u16p, _u16p, _u16p, _i32p, _c_int,
                                    _c_int, _c_int, _c_int, _c_int, _c_int]
+    L.orc_append_kv.restype = None
+    L.orc_append_kv.argtypes = [_u16p, _u16p, _u16p, _u16p, _u16p, _u16p, _i32p, _i32p,
+                                _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]
     L.orc_score.restype = None
     L.orc_score.argtypes = [_f32p, _c_int, _c_int, _u16p, _i32p, _f32p,
                             _c_int, _c_int, _c_int, _c_int, _c_int]
@@ -125,6 +128,21 @@ def project_keys(kc, wk, kp, pos0, ntok):
     assert wk.shape == (Hkv, dp, D) and kp.shape == (B, Hkv, Lmax, dp)
     lib().orc_project_keys(kc, wk, kp, _i32(pos0), int(ntok), B, Hkv, Lmax, D, dp)
     return kp
+
+
+def append_kv(k_new, v_new, kc, vc, kp, wk, ctx_len, proj_len, n_p):
+    """Append one token's K/V rows per sequence at ctx_len and project the
+    pending keys once n_p of them have accumulated. Updates kc, vc, kp,
+    ctx_len and proj_len in place (numpy arrays: uint16 bit patterns for
+    bf16 / fp16, int32 lengths)."""
+    B, Hkv, Lmax, D = kc.shape
+    dp = wk.shape[1]
+    for a in (kc, vc, kp, ctx_len, proj_len):
+        assert a.flags["C_CONTIGUOUS"] and a.flags["WRITEABLE"]
+    assert kc.dtype == vc.dtype == kp.dtype == np.uint16
+    assert ctx_len.dtype == proj_len.dtype == np.int32
+    lib().orc_append_kv(_u16(k_new), _u16(v_new), kc, vc, kp, _u16(wk), ctx_len, proj_len,
+                        B, Hkv, Lmax, D, dp, int(n_p))
 
 
 def score(qhat, kp, proj_len, Hq, n_slots=1, slot=0, fill=np.nan):

@@ -172,6 +172,41 @@ void orc_project_keys(const uint16_t *kc, const uint16_t *wk, uint16_t *kp,
             }
 }
 
+/*
+ * One decode step's cache append with batched key projection ("Inference
+ * strategy": the newest token's key and value join the retained cache;
+ * "Optimizations": the key projection runs once per batch of n_p new tokens
+ * rather than every step). Per sequence b, with L = ctx_len[b] and
+ * P = proj_len[b]:
+ *   if 0 <= P <= L < Lmax: the new rows are written at position L of every
+ *   KV head, ctx_len[b] = L + 1, and when L + 1 - P >= n_p the keys
+ *   [P, L + 1) are projected (orc_project_keys) and proj_len[b] = L + 1;
+ *   otherwise (a full cache or lengths out of range) nothing changes for b.
+ *   k_new, v_new [B, Hkv, D] bf16; n_p >= 1.
+ */
+void orc_append_kv(const uint16_t *k_new, const uint16_t *v_new, uint16_t *kc, uint16_t *vc,
+                   uint16_t *kp, const uint16_t *wk, int *ctx_len, int *proj_len,
+                   int B, int Hkv, int Lmax, int D, int dp, int n_p)
+{
+    for (int b = 0; b < B; ++b) {
+        int L = ctx_len[b], P = proj_len[b];
+        if (!(P >= 0 && P <= L && L < Lmax))
+            continue;
+        for (int j = 0; j < Hkv; ++j) {
+            size_t src = ((size_t)b * Hkv + j) * D;
+            size_t dst = (((size_t)b * Hkv + j) * Lmax + L) * D;
+            memcpy(kc + dst, k_new + src, sizeof(uint16_t) * (size_t)D);
+            memcpy(vc + dst, v_new + src, sizeof(uint16_t) * (size_t)D);
+        }
+        ctx_len[b] = L + 1;
+        if (L + 1 - P >= n_p) {
+            size_t off = (size_t)b * Hkv * Lmax;
+            orc_project_keys(kc + off * D, wk, kp + off * dp, &P, L + 1 - P, 1, Hkv, Lmax, D, dp);
+            proj_len[b] = L + 1;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* Scoring: importance = predicted query . projected key               */
 /* ("Core architecture", scoring). Query head h reads KV head h/g.      */
