@@ -98,11 +98,13 @@ def cpu_baseline(inp, cfg, seconds):
 
 def run_interval(cfg, args):
     """Prediction-interval pipeline over all layers of a multi-layer workload:
-    once per interval, project the pending N_p tokens of every layer, run every
-    producer's predictor, score and select every consumer layer (the window
-    left out of the list); then I decode steps, each appending one token per
-    sequence and running sparse attention on every layer with the sliding
-    window. steps/s = I / interval time. The caches are generated on the GPU
+    once per interval, run every producer's predictor, score and select every
+    consumer layer (the window left out of the list); then I decode steps,
+    each appending one token's K/V per sequence to every layer (tb_append_kv,
+    which projects the pending keys once N_p of them have accumulated) and
+    running sparse attention on every layer with the sliding window. Every
+    interval starts from the same lengths (the appended rows are rewritten).
+    steps/s = I / interval time. The caches are generated on the GPU
     (torch.randn, bf16): they are far larger than the 256 MiB MALL."""
     import torch
     import learned_kv_cache_amd as tb
@@ -154,12 +156,11 @@ def run_interval(cfg, args):
                     pos = torch.randint(cfg.S, int(L0[b]) - cfg.W, (n,), generator=gen, device="cuda")
                     kv = h // cfg.g
                     K[l][b, kv, pos] = (K[l][b, kv, pos].float() + cfg.heavy_shift * v[b, h]).to(torch.bfloat16)
-    # projected keys of everything but the pending batch
+    # projected keys of the whole context; the decode steps append after it
     Kp = [torch.zeros(B, Hkv, Lmax, dp, dtype=torch.float16, device="cuda") for _ in range(nl)]
-    pend = torch.from_numpy(L0 - Np).cuda()
     zero = torch.zeros(B, dtype=torch.int32, device="cuda")
     for l in range(nl):
-        tb.tb_project_keys(K[l], Wk[l], Kp[l], zero, int(L0.max()) - Np)
+        tb.tb_project_keys(K[l], Wk[l], Kp[l], zero, int(L0.max()))
     torch.cuda.synchronize()
     scores = torch.empty(B, Hq, Lmax, device="cuda")
     cap = cfg.S + cfg.K
@@ -168,24 +169,33 @@ def run_interval(cfg, args):
     out = torch.empty(B, Hq, D, device="cuda")
     ws_s = tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax))
     ws_a = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, cfg.W, D))
-    step_ctx = [torch.from_numpy(L0 + 1 + j).cuda() for j in range(I)]
+    # per-layer device lengths [layer, (ctx, proj), B], reset at every interval
+    lens0 = torch.from_numpy(np.stack([np.stack([L0, L0])] * nl)).cuda()
+    lens = lens0.clone()
+    k_new = [randn(B, Hkv, D) for _ in range(I)]
+    v_new = [randn(B, Hkv, D) for _ in range(I)]
     mode = tb.TB_NF_FILL | tb.TB_SEL_OMIT_WINDOW
     stream = torch.cuda.current_stream()
 
-    def interval(attn_ev=None):
-        for l in range(nl):
-            tb.tb_project_keys(K[l], Wk[l], Kp[l], pend, Np)
+    def interval(attn_ev=None, app_ev=None):
+        lens.copy_(lens0)
         for p in range(npro):
             tb.tb_predict_queries(X[p], W1[p], W2[p], qhat[p], ws_p)
         for l in range(nl):
             tb.tb_score(qhat[l // cfg.producer_stride], Kp[l], ctx0, scores)
             tb.tb_select(scores, ctx0, ctx0, cfg.S, cfg.W, cfg.K, cfg.r, idx[l], cnt[l], ws_s, mode=mode)
         for j in range(I):
+            if app_ev is not None:
+                app_ev[j][0].record(stream)
             for l in range(nl):
-                if attn_ev is not None and l == 0:
-                    attn_ev[j][0].record(stream)
+                tb.tb_append_kv(k_new[j], v_new[j], K[l], V[l], Kp[l], Wk[l], lens[l, 0], lens[l, 1],
+                                Np)
+            if attn_ev is not None:
+                app_ev[j][1].record(stream)
+                attn_ev[j][0].record(stream)
+            for l in range(nl):
                 tb.tb_sparse_decode_attn(Q[l], K[l], V[l], idx[l], cnt[l], out, ws_a,
-                                         ctx_len=step_ctx[j], window=cfg.W)
+                                         ctx_len=lens[l, 0], window=cfg.W)
             if attn_ev is not None:
                 attn_ev[j][1].record(stream)
 
@@ -193,16 +203,23 @@ def run_interval(cfg, args):
     interval()
     torch.cuda.synchronize()
     n_int = max(1, args.intervals)
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(I)] for _ in range(n_int)]
+    mk = lambda: [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(I)] for _ in range(n_int)]
+    evs, aevs = mk(), mk()
     log("timing %d intervals of %d steps" % (n_int, I))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(n_int):
-        interval(evs[k])
+        interval(evs[k], aevs[k])
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     attn_us = float(np.mean([a.elapsed_time(b) for row in evs for a, b in row])) * 1e3 / nl
+    app = np.array([[a.elapsed_time(b) * 1e3 / nl for a, b in row] for row in aevs])
+    proj_step = Np - 1 if Np <= I else None   # the step whose appends project the batch
+    append = {"us_per_layer_call": round(float(np.median(app)), 2),
+              "us_per_layer_call_projecting": (round(float(np.median(app[:, proj_step])), 2)
+                                               if proj_step is not None else None),
+              "n_p": Np}
     # compulsory gather bytes of one layer's attention launch at the first step
     gi, gc = idx[0].cpu().numpy(), cnt[0].cpu().numpy()
     rows = 0
@@ -231,6 +248,7 @@ def run_interval(cfg, args):
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None,
                      "kernel": "sparse decode attention gather (one layer, one step)",
                      "bytes_per_launch": attn_bytes, "avg_launch_us": attn_us},
+        "append": append,
     }
     print(json.dumps(res), flush=True)
 
@@ -298,6 +316,22 @@ def main():
         tb.tb_project_keys(r["kc"], r["wk"], r["kp"], zeros, L - 1)   # the cache before this step
         reps.append(r)
     torch.cuda.synchronize()
+
+    # whole-context key projection (the prefill step before the decode path),
+    # timed over the rotated replicas
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(3 * R)]
+    for i, (e0, e1) in enumerate(pev):
+        r_ = reps[i % R]
+        e0.record()
+        tb.tb_project_keys(r_["kc"], r_["wk"], r_["kp"], zeros, L - 1)
+        e1.record()
+    torch.cuda.synchronize()
+    proj_us = float(np.mean([a.elapsed_time(b) for a, b in pev[R:]])) * 1e3
+    proj_bytes = B * cfg.Hkv * (L - 1) * (cfg.D * 2 + cfg.dp * 2) + cfg.Hkv * cfg.dp * cfg.D * 2
+    prefill = {"tokens": (L - 1) * B, "kv_heads": cfg.Hkv, "us": round(proj_us, 2),
+               "bytes": proj_bytes, "gbps": proj_bytes / proj_us / 1e3,
+               "frac": proj_bytes / proj_us / 1e3 / PEAK_HBM_GBS}
 
     ctx = torch.full((B,), L, dtype=torch.int32, device="cuda")
     pos_new = torch.full((B,), L - 1, dtype=torch.int32, device="cuda")
@@ -516,6 +550,7 @@ def main():
         "step_compulsory_bytes": step_bytes,
         "attended_rows": {"union": union_rows, "per_head": per_head_rows},
         "dilate_mode": dilate,
+        "prefill_projection": prefill,
     }
     if stages:
         res["stages_us"] = stages

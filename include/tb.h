@@ -110,6 +110,28 @@ tb_status tb_project_keys(const void *k_cache, const void *wk, void *kp,
                           int B, int Hkv, int Lmax, int D, int dp, void *stream);
 
 /*
+ * Decode-step cache append with batched projection ("Inference strategy":
+ * the newest token's key and value join the retained cache; "Optimizations":
+ * the key projection runs once per batch of n_p new tokens). Per sequence b,
+ * with L = ctx_len[b] and P = proj_len[b] read on the device:
+ *   if 0 <= P <= L < Lmax: k_new[b, j] and v_new[b, j] are written at
+ *   position L of every KV head j; ctx_len[b] becomes L + 1; and when
+ *   L + 1 - P >= n_p the keys [P, L + 1) are projected as by tb_project_keys
+ *   and proj_len[b] becomes L + 1. Otherwise (a full cache, or lengths out of
+ *   range) nothing is written for b.
+ *   k_new, v_new [B, Hkv, D]          bf16
+ *   k_cache, v_cache [B, Hkv, Lmax, D] bf16, kp [B, Hkv, Lmax, dp] fp16
+ *   wk      [Hkv, dp, D]              bf16
+ *   ctx_len, proj_len [B]             int32, device, updated in place
+ * One workgroup per sequence; meant for n_p up to a few hundred (use
+ * tb_project_keys for a whole context). Limits: D in {64, 128}, dp in
+ * {16, 32}, n_p >= 1.
+ */
+tb_status tb_append_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                       void *kp, const void *wk, int32_t *ctx_len, int32_t *proj_len,
+                       int B, int Hkv, int Lmax, int D, int dp, int n_p, void *stream);
+
+/*
  * Scoring ("Core architecture", scoring): token importance is the dot product
  * of the predicted query with the projected key; query head h reads KV head
  * h / (Hq / Hkv):

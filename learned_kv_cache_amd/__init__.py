@@ -58,6 +58,8 @@ def lib():
                                      _vp, _i, _i, _i, _i, _i, _vp]
     L.tb_project_keys.restype = _i
     L.tb_project_keys.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+    L.tb_append_kv.restype = _i
+    L.tb_append_kv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
     L.tb_score.restype = _i
     L.tb_score.argtypes = [_vp, _i, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
     L.tb_select_workspace_bytes.restype = _sz
@@ -167,6 +169,26 @@ def tb_project_keys(k_cache, wk, kp, pos0, n_tokens, stream=None):
                                  _ptr(pos0, torch.int32, "pos0"), int(n_tokens), B, Hkv, Lmax, D, dp,
                                  _stream(stream)))
     return kp
+
+
+def tb_append_kv(k_new, v_new, k_cache, v_cache, kp, wk, ctx_len, proj_len, n_p, stream=None):
+    """Write one token's K/V per sequence at ctx_len[b]; project the pending
+    keys once n_p have accumulated; advance ctx_len / proj_len in place."""
+    B, Hkv, Lmax, D = k_cache.shape
+    dp = wk.shape[1]
+    if (tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D)
+            or tuple(v_cache.shape) != (B, Hkv, Lmax, D) or tuple(wk.shape) != (Hkv, dp, D)
+            or tuple(kp.shape) != (B, Hkv, Lmax, dp) or ctx_len.numel() != B
+            or proj_len.numel() != B):
+        raise ValueError("tb_append_kv: shape mismatch")
+    _check(lib().tb_append_kv(_ptr(k_new, torch.bfloat16, "k_new", 3),
+                              _ptr(v_new, torch.bfloat16, "v_new", 3),
+                              _ptr(k_cache, torch.bfloat16, "k_cache", 4),
+                              _ptr(v_cache, torch.bfloat16, "v_cache", 4),
+                              _ptr(kp, torch.float16, "kp", 4), _ptr(wk, torch.bfloat16, "wk", 3),
+                              _ptr(ctx_len, torch.int32, "ctx_len"),
+                              _ptr(proj_len, torch.int32, "proj_len"), B, Hkv, Lmax, D, dp,
+                              int(n_p), _stream(stream)))
 
 
 # ---------------------------------------------------------------- scoring

@@ -14,6 +14,80 @@
 namespace tb {
 namespace {
 
+// Bulk projection (whole-context prefill): each wave keeps its W_k
+// fragments in registers and walks kBulkIter batches of 16 tokens with the
+// rows of the next NBUF - 1 batches in flight, so the weights are read once
+// per 64 tokens instead of once per 16.
+constexpr int kBulkIter = 4;
+constexpr int kBulkTokPerWave = kBulkIter * 16;
+constexpr int kBulkTokPerBlock = (kProjThreads / 64) * kBulkTokPerWave;
+constexpr int kBulkMinTokens = 2048;
+
+template <int D, int DP>
+__global__ __launch_bounds__(kProjThreads) void project_bulk_kernel(
+    const uint16_t *__restrict__ kc, const uint16_t *__restrict__ wk, uint16_t *__restrict__ kp,
+    const int32_t *__restrict__ pos0, int ntok, int Hkv, int Lmax) {
+    constexpr int NV = D / 32;
+    constexpr int MT = DP / 16;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, kq = lane >> 4;
+    const int kvh = blockIdx.y, b = blockIdx.z;
+    const int base = blockIdx.x * kBulkTokPerBlock + wave * kBulkTokPerWave;
+    if (base >= ntok) return;
+    const int p0 = pos0[b];
+    const size_t head = (size_t)(b * Hkv + kvh);
+    uint4 w[MT][NV];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const uint4 *wrow = reinterpret_cast<const uint4 *>(
+            wk + ((size_t)kvh * DP + mt * 16 + n) * D + kq * (D / 4));
+#pragma unroll
+        for (int v = 0; v < NV; ++v) w[mt][v] = wrow[v];
+    }
+    constexpr int NBUF = 3;   // batches in flight per wave
+    uint4 kv[NBUF][NV];
+    auto load = [&](int it, uint4 (&dst)[NV]) {
+        const int run = base + it * 16 + n;
+        const int t = p0 + run;
+        if (run < ntok && t >= 0 && t < Lmax) {
+            const uint4 *row =
+                reinterpret_cast<const uint4 *>(kc + (head * Lmax + t) * D + kq * (D / 4));
+#pragma unroll
+            for (int v = 0; v < NV; ++v) dst[v] = row[v];
+        } else {
+#pragma unroll
+            for (int v = 0; v < NV; ++v) dst[v] = make_uint4(0, 0, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int it = 0; it < NBUF - 1; ++it) load(it, kv[it]);
+#pragma unroll
+    for (int it = 0; it < kBulkIter; ++it) {
+        if (base + it * 16 >= ntok) break;
+        if (it + NBUF - 1 < kBulkIter) load(it + NBUF - 1, kv[(it + NBUF - 1) % NBUF]);
+        const uint4 *cur = kv[it % NBUF];
+        const int run = base + it * 16 + n;
+        const int t = p0 + run;
+        const bool valid = run < ntok && t >= 0 && t < Lmax;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w[mt][v]),
+                                                              __builtin_bit_cast(bf16x8_t, cur[v]),
+                                                              acc, 0, 0, 0);
+            // acc[i] = channel mt*16 + 4*kq + i of token t
+            if (valid) {
+                const uint32_t lo = f32_to_f16_bits(acc[0]) | (f32_to_f16_bits(acc[1]) << 16);
+                const uint32_t hi = f32_to_f16_bits(acc[2]) | (f32_to_f16_bits(acc[3]) << 16);
+                *reinterpret_cast<uint2 *>(kp + (head * Lmax + t) * DP + mt * 16 + 4 * kq) =
+                    make_uint2(lo, hi);
+            }
+        }
+    }
+}
+
 template <int D, int DP>
 __global__ __launch_bounds__(kProjThreads) void project_kernel(
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ wk, uint16_t *__restrict__ kp,
@@ -21,24 +95,124 @@ __global__ __launch_bounds__(kProjThreads) void project_kernel(
     project_block<D, DP>(kc, wk, kp, pos0, ntok, Hkv, Lmax, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
+// Decode-step append with batched projection, one workgroup per sequence:
+// the new K/V rows go to position L = ctx_len[b] of every KV head; once the
+// pending keys [P, L + 1) number n_p, the waves project them (16 tokens of
+// one head per item, the new token's row read from k_new rather than from
+// the cache it was just written to); then the lengths are advanced.
+template <int D, int DP>
+__global__ __launch_bounds__(kProjThreads) void append_kernel(
+    const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
+    uint16_t *__restrict__ kc, uint16_t *__restrict__ vc, uint16_t *__restrict__ kp,
+    const uint16_t *__restrict__ wk, int32_t *__restrict__ ctx, int32_t *__restrict__ plen,
+    int Hkv, int Lmax, int n_p) {
+    constexpr int NV = D / 32;   // 16-byte pieces per lane per row
+    constexpr int MT = DP / 16;
+    constexpr int R16 = D / 8;   // 16-byte pieces per row
+    const int b = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int L = ctx[b], P = plen[b];
+    if (!(P >= 0 && P <= L && L < Lmax)) return;
+    for (int i = threadIdx.x; i < 2 * Hkv * R16; i += kProjThreads) {
+        const int which = i / (Hkv * R16), r = i % (Hkv * R16);
+        const int j = r / R16, v = r % R16;
+        const uint4 *src = reinterpret_cast<const uint4 *>((which ? v_new : k_new) +
+                                                           ((size_t)b * Hkv + j) * D) + v;
+        uint4 *dst = reinterpret_cast<uint4 *>((which ? vc : kc) +
+                                               (((size_t)b * Hkv + j) * Lmax + L) * D) + v;
+        *dst = *src;
+    }
+    const int L1 = L + 1;
+    const bool proj = L1 - P >= n_p;
+    if (proj) {
+        const int n = lane & 15, kq = lane >> 4;
+        const int nb = (L1 - P + 15) / 16;
+        for (int item = wave; item < Hkv * nb; item += kProjThreads / 64) {
+            const int j = item / nb, blk = item % nb;
+            const int t = P + blk * 16 + n;
+            const bool valid = t < L1;
+            const size_t head = (size_t)b * Hkv + j;
+            uint4 kv[NV];
+            if (valid) {
+                const uint16_t *rowp = t == L ? k_new + head * D : kc + (head * Lmax + t) * D;
+                const uint4 *row = reinterpret_cast<const uint4 *>(rowp + kq * (D / 4));
+#pragma unroll
+                for (int v = 0; v < NV; ++v) kv[v] = row[v];
+            } else {
+#pragma unroll
+                for (int v = 0; v < NV; ++v) kv[v] = make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint4 *wrow = reinterpret_cast<const uint4 *>(
+                    wk + ((size_t)j * DP + mt * 16 + n) * D + kq * (D / 4));
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, wrow[v]), __builtin_bit_cast(bf16x8_t, kv[v]),
+                        acc, 0, 0, 0);
+                if (valid) {
+                    const uint32_t lo = f32_to_f16_bits(acc[0]) | (f32_to_f16_bits(acc[1]) << 16);
+                    const uint32_t hi = f32_to_f16_bits(acc[2]) | (f32_to_f16_bits(acc[3]) << 16);
+                    *reinterpret_cast<uint2 *>(kp + (head * Lmax + t) * DP + mt * 16 + 4 * kq) =
+                        make_uint2(lo, hi);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        ctx[b] = L1;
+        if (proj) plen[b] = L1;
+    }
+}
+
 }  // namespace
 
 tb_status launch_project(const void *kc, const void *wk, void *kp, const int32_t *pos0, int ntok,
                          int B, int Hkv, int Lmax, int D, int dp, hipStream_t st) {
     if (ntok == 0) return TB_OK;
-    dim3 grid((ntok + kProjTokPerBlock - 1) / kProjTokPerBlock, Hkv, B);
+    const bool bulk = ntok >= kBulkMinTokens;
+    const int per = bulk ? kBulkTokPerBlock : kProjTokPerBlock;
+    dim3 grid((ntok + per - 1) / per, Hkv, B);
     const uint16_t *k = static_cast<const uint16_t *>(kc);
     const uint16_t *w = static_cast<const uint16_t *>(wk);
     uint16_t *o = static_cast<uint16_t *>(kp);
 #define TB_P(DD, PP)                                                                        \
     if (D == DD && dp == PP) {                                                              \
-        hipLaunchKernelGGL((project_kernel<DD, PP>), grid, dim3(kProjThreads), 0, st, k, w, o, pos0, \
-                           ntok, Hkv, Lmax);                                                \
+        if (bulk)                                                                           \
+            hipLaunchKernelGGL((project_bulk_kernel<DD, PP>), grid, dim3(kProjThreads), 0, st, k, \
+                               w, o, pos0, ntok, Hkv, Lmax);                                \
+        else                                                                                \
+            hipLaunchKernelGGL((project_kernel<DD, PP>), grid, dim3(kProjThreads), 0, st, k, w, \
+                               o, pos0, ntok, Hkv, Lmax);                                   \
         return check_launch("tb_project_keys");                                             \
     }
     TB_P(128, 32) TB_P(128, 16) TB_P(64, 32) TB_P(64, 16)
 #undef TB_P
     set_error("tb_project_keys: unsupported D=%d dp=%d", D, dp);
+    return TB_ERR_UNSUPPORTED_SHAPE;
+}
+
+tb_status launch_append(const void *k_new, const void *v_new, void *kc, void *vc, void *kp,
+                        const void *wk, int32_t *ctx, int32_t *plen, int B, int Hkv, int Lmax,
+                        int D, int dp, int n_p, hipStream_t st) {
+    const uint16_t *kn = static_cast<const uint16_t *>(k_new);
+    const uint16_t *vn = static_cast<const uint16_t *>(v_new);
+    uint16_t *k = static_cast<uint16_t *>(kc);
+    uint16_t *v = static_cast<uint16_t *>(vc);
+    uint16_t *o = static_cast<uint16_t *>(kp);
+    const uint16_t *w = static_cast<const uint16_t *>(wk);
+#define TB_A(DD, PP)                                                                        \
+    if (D == DD && dp == PP) {                                                              \
+        hipLaunchKernelGGL((append_kernel<DD, PP>), dim3(B), dim3(kProjThreads), 0, st, kn, vn, k, \
+                           v, o, w, ctx, plen, Hkv, Lmax, n_p);                             \
+        return check_launch("tb_append_kv");                                                \
+    }
+    TB_A(128, 32) TB_A(128, 16) TB_A(64, 32) TB_A(64, 16)
+#undef TB_A
+    set_error("tb_append_kv: unsupported D=%d dp=%d", D, dp);
     return TB_ERR_UNSUPPORTED_SHAPE;
 }
 

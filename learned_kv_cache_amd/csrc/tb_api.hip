@@ -116,6 +116,23 @@ tb_status tb_project_keys(const void *k_cache, const void *wk, void *kp, const i
                               static_cast<hipStream_t>(stream));
 }
 
+tb_status tb_append_kv(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                       void *kp, const void *wk, int32_t *ctx_len, int32_t *proj_len, int B,
+                       int Hkv, int Lmax, int D, int dp, int n_p, void *stream) {
+    TB_REQUIRE(k_new && v_new && k_cache && v_cache && kp && wk && ctx_len && proj_len,
+               TB_ERR_INVALID_ARGUMENT, "tb_append_kv: null pointer");
+    TB_REQUIRE(aligned16(k_new) && aligned16(v_new) && aligned16(k_cache) && aligned16(v_cache) &&
+                   aligned16(kp) && aligned16(wk) && aligned4(ctx_len) && aligned4(proj_len),
+               TB_ERR_INVALID_ARGUMENT, "tb_append_kv: misaligned pointer");
+    TB_REQUIRE(B >= 1 && B <= 65535 && Hkv >= 1 && Hkv <= 65535 && Lmax >= 1 && n_p >= 1,
+               TB_ERR_INVALID_ARGUMENT, "tb_append_kv: bad sizes B=%d Hkv=%d Lmax=%d n_p=%d", B,
+               Hkv, Lmax, n_p);
+    TB_REQUIRE((D == 64 || D == 128) && (dp == 16 || dp == 32), TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_append_kv: D must be 64 or 128 and dp 16 or 32 (got %d, %d)", D, dp);
+    return tb::launch_append(k_new, v_new, k_cache, v_cache, kp, wk, ctx_len, proj_len, B, Hkv,
+                             Lmax, D, dp, n_p, static_cast<hipStream_t>(stream));
+}
+
 // ---------------------------------------------------------------- scoring
 tb_status tb_score(const float *qhat, int n_slots, int slot, const void *kp,
                    const int32_t *proj_len, float *scores, int B, int Hq, int Hkv, int Lmax,

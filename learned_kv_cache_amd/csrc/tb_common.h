@@ -78,6 +78,9 @@ tb_status launch_predict_project(const void *x, const void *w1, const void *w2, 
                                  int B, int E, int Eh, int n_out, void *ws, int nsplit,
                                  const void *kc, const void *wk, void *kp, const int32_t *pos0,
                                  int ntok, int Hkv, int Lmax, int D, int dp, hipStream_t st);
+tb_status launch_append(const void *k_new, const void *v_new, void *kc, void *vc, void *kp,
+                        const void *wk, int32_t *ctx, int32_t *plen, int B, int Hkv, int Lmax,
+                        int D, int dp, int n_p, hipStream_t st);
 tb_status launch_project(const void *kc, const void *wk, void *kp, const int32_t *pos0, int ntok,
                          int B, int Hkv, int Lmax, int D, int dp, hipStream_t st);
 tb_status launch_score(const float *qhat, int n_slots, int slot, const void *kp,

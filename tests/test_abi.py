@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(tb):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     lib = ctypes.CDLL(tb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -67,6 +67,12 @@ def test_validation_rejects_before_launch(tb):
     assert b"aligned" in L.tb_last_error_detail()
     # unsupported shapes
     assert L.tb_project_keys(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 1, 2, 300, 96, 16, None) == 2
+    # append: n_p < 1, unsupported dp, null pointer
+    ap = lambda n_p, dp, first=vp(FAKE): (first, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                          vp(FAKE), vp(FAKE), 1, 2, 300, 64, dp, n_p, None)
+    assert L.tb_append_kv(*ap(0, 16)) == 1
+    assert L.tb_append_kv(*ap(4, 8)) == 2
+    assert L.tb_append_kv(*ap(4, 16, None)) == 1
     assert L.tb_score(vp(FAKE), 1, 0, vp(FAKE), vp(FAKE), vp(FAKE), 1, 18, 2, 300, 16, None) == 2
     assert L.tb_score(vp(FAKE), 1, 0, vp(FAKE), vp(FAKE), vp(FAKE), 1, 9, 2, 300, 16, None) == 1
     assert L.tb_predict_queries(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 500, 128, 128, vp(FAKE), 1 << 20, None) == 2

@@ -32,6 +32,8 @@ def tb():
     (1, 8, 4099, 128, 32, [0], 4099),
     (3, 4, 1000, 128, 16, [999, 17, 640], 16),
     (1, 8, 64, 128, 32, [63], 1),
+    (2, 2, 6000, 64, 16, [100, 3000], 4000),   # bulk path; second row runs past Lmax
+    (1, 4, 2048, 128, 16, [0], 2048),          # bulk path, exactly one batch multiple
 ])
 def test_project_keys(tb, orc, B, Hkv, L, D, dp, pos0, ntok):
     say("project", B, Hkv, L, D, dp, pos0, ntok)
@@ -51,6 +53,22 @@ def test_project_keys(tb, orc, B, Hkv, L, D, dp, pos0, ntok):
         lo, hi = pos0[b], min(L, pos0[b] + ntok)
         assert_rel(bits_to_f32_f16(got[b, :, lo:hi]), bits_to_f32_f16(ref[b, :, lo:hi]), 2e-3,
                    "project b=%d" % b)
+
+
+def test_project_bulk_equals_small_batches(tb):
+    # the whole-context path (>= 2048 tokens per call) and the per-step path
+    # (a few tokens per call) give the same bits
+    rng = rng_for(51)
+    B, Hkv, L, D, dp = 2, 8, 9000, 128, 32
+    kc = dev(normal_bf16(rng, (B, Hkv, L, D)), torch.bfloat16)
+    wk = dev(xavier_bf16(rng, dp, D, lead=(Hkv,)), torch.bfloat16)
+    a = torch.zeros((B, Hkv, L, dp), dtype=torch.float16, device="cuda")
+    b = torch.zeros_like(a)
+    tb.tb_project_keys(kc, wk, a, dev32(np.array([0, 0], np.int32)), L)
+    for p0 in range(0, L, 1500):
+        tb.tb_project_keys(kc, wk, b, dev32(np.array([p0, p0], np.int32)), min(1500, L - p0))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a), bits(b))
 
 
 # ------------------------------------------------------------------ predictor
