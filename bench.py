@@ -253,6 +253,163 @@ def run_interval(cfg, args):
     print(json.dumps(res), flush=True)
 
 
+def run_offload(cfg, args):
+    """CPU-offload decoding on the 256K-context shape: every layer's full K/V
+    cache in pinned host memory (read over the host link), K' and the
+    per-query-head sink + important + circular-window buffers in HBM. One
+    interval per layer: score and select (window left out), gather the
+    selected rows from host memory into the buffers; then I steps, each
+    appending the new token (host cache, window slot, K') and attending over
+    the buffers. Compared with dense decoding over the same offloaded cache:
+    every step fetches all L rows of every KV head over the host link, then
+    attends over them."""
+    import torch
+    import learned_kv_cache_amd as tb
+
+    B, Hq, Hkv, D, dp = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.dp
+    I, nl = cfg.interval, max(1, args.offload_layers)
+    n_int = max(1, args.intervals)
+    L = cfg.L
+    Lmax = L + I * (n_int + 1)
+    cap = cfg.S + cfg.K
+    W = cfg.W
+    buf_rows = cap + W
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260101 + cfg.cid)
+
+    def randn(*shape, std=1.0):
+        return (torch.randn(*shape, generator=gen, device="cuda") * std).to(torch.bfloat16)
+
+    log("building %d layers: K/V [%d, %d, %d, %d] bf16 in pinned host memory" % (nl, B, Hkv, Lmax, D))
+    kh, vh, kp, wk, kb, vb, qs = [], [], [], [], [], [], []
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for l in range(nl):
+        kd, vd = randn(B, Hkv, Lmax, D), randn(B, Hkv, Lmax, D)
+        w = randn(Hkv, dp, D, std=D ** -0.5)
+        p_ = torch.zeros(B, Hkv, Lmax, dp, dtype=torch.float16, device="cuda")
+        tb.tb_project_keys(kd, w, p_, zero, L)
+        hk = torch.empty(kd.shape, dtype=torch.bfloat16, pin_memory=True)
+        hv = torch.empty(vd.shape, dtype=torch.bfloat16, pin_memory=True)
+        hk.copy_(kd)
+        hv.copy_(vd)
+        del kd, vd
+        kh.append(hk), vh.append(hv), kp.append(p_), wk.append(w)
+        kb.append(torch.zeros(B, Hq, buf_rows, D, dtype=torch.bfloat16, device="cuda"))
+        vb.append(torch.zeros(B, Hq, buf_rows, D, dtype=torch.bfloat16, device="cuda"))
+        qs.append(randn(B, Hq, D))
+    torch.cuda.synchronize()
+    lens = torch.full((nl, 2, B), L, dtype=torch.int32, device="cuda")
+    win = torch.arange(L - W, L, dtype=torch.int32, device="cuda").expand(B, Hq, W).contiguous()
+    wcnt = torch.full((B, Hq), W, dtype=torch.int32, device="cuda")
+    for l in range(nl):
+        tb.tb_offload_gather(kh[l], vh[l], win, wcnt, kb[l], vb[l], slot0=cap, wrap=W)
+    qhat = torch.randn(B, Hq * dp, generator=gen, device="cuda")
+    scores = torch.empty(B, Hq, Lmax, device="cuda")
+    idx = torch.zeros(B, Hq, cap, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(B, Hq, dtype=torch.int32, device="cuda")
+    ws_s = tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax))
+    ws_a = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, W, D))
+    iota = torch.arange(cap, dtype=torch.int32, device="cuda").expand(B, Hq, cap).contiguous()
+    full = torch.full((B,), buf_rows, dtype=torch.int32, device="cuda")
+    out = torch.empty(B, Hq, D, device="cuda")
+    k_new = [randn(B, Hkv, D) for _ in range(I)]
+    v_new = [randn(B, Hkv, D) for _ in range(I)]
+    mode = tb.TB_NF_FILL | tb.TB_SEL_OMIT_WINDOW
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def interval(rec):
+        for l in range(nl):
+            ctx, pl = lens[l, 0], lens[l, 1]
+            e = [ev() for _ in range(3)]
+            e[0].record()
+            tb.tb_score(qhat, kp[l], pl, scores)
+            tb.tb_select(scores, ctx, pl, cfg.S, W, cfg.K, cfg.r, idx, cnt, ws_s, mode=mode)
+            e[1].record()
+            tb.tb_offload_gather(kh[l], vh[l], idx, cnt, kb[l], vb[l])
+            e[2].record()
+            rec["select"].append(e[:2])
+            rec["gather"].append(e[1:])
+        for j in range(I):
+            e = [ev() for _ in range(3)]
+            e[0].record()
+            for l in range(nl):
+                tb.tb_offload_append(k_new[j], v_new[j], wk[l], kh[l], vh[l], kp[l], lens[l, 0],
+                                     lens[l, 1], kb[l], vb[l], W)
+            e[1].record()
+            for l in range(nl):
+                tb.tb_sparse_decode_attn(qs[l], kb[l], vb[l], iota, cnt, out, ws_a, ctx_len=full,
+                                         window=W)
+            e[2].record()
+            rec["append"].append(e[:2])
+            rec["attn"].append(e[1:])
+
+    log("warmup interval")
+    interval({"select": [], "gather": [], "append": [], "attn": []})
+    torch.cuda.synchronize()
+    rec = {"select": [], "gather": [], "append": [], "attn": []}
+    log("timing %d intervals of %d steps over %d layers" % (n_int - 1, I, nl))
+    t0 = time.perf_counter()
+    for _ in range(n_int - 1):
+        interval(rec)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms = lambda k: float(np.mean([a.elapsed_time(b) for a, b in rec[k]]))
+    gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+    gather_bytes = int(gc.sum()) * 2 * D * 2
+    union = 0
+    for kvh in range(Hkv):
+        su = set()
+        for h in range(kvh * cfg.g, (kvh + 1) * cfg.g):
+            su.update(gi[0, h, :gc[0, h]].tolist())
+        union += len(su)
+    steps = (n_int - 1) * I
+    # dense decoding over the offloaded cache, one layer: fetch all rows of
+    # every KV head over the host link, attend over them
+    log("dense comparison: fetching %d rows x %d KV heads over the host link" % (L, Hkv))
+    dk = torch.empty(B, Hkv, L, D, dtype=torch.bfloat16, device="cuda")
+    dv = torch.empty_like(dk)
+    didx = torch.arange(L, dtype=torch.int32, device="cuda").expand(B, Hkv, L).contiguous()
+    dcnt = torch.full((B, Hkv), L, dtype=torch.int32, device="cuda")
+    aidx = torch.arange(L, dtype=torch.int32, device="cuda").expand(B, Hq, L).contiguous()
+    acnt = torch.full((B, Hq), L, dtype=torch.int32, device="cuda")
+    ws_d = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, L, 0, D))
+    dres = []
+    for rep in range(3):
+        e = [ev() for _ in range(3)]
+        e[0].record()
+        tb.tb_offload_gather(kh[0], vh[0], didx, dcnt, dk, dv)
+        e[1].record()
+        tb.tb_sparse_decode_attn(qs[0], dk, dv, aidx, acnt, out, ws_d)
+        e[2].record()
+        dres.append(e)
+    torch.cuda.synchronize()
+    dense_fetch = float(np.mean([e[0].elapsed_time(e[1]) for e in dres[1:]]))
+    dense_attn = float(np.mean([e[1].elapsed_time(e[2]) for e in dres[1:]]))
+    dense_bytes = B * Hkv * L * 2 * D * 2
+    per_step_layer = el / steps / nl
+    res = {
+        "metric": "offloaded decode steps/s at 256K ctx, 8K budget; host-link GB/s",
+        "value": steps / el, "unit": "steps/s (all %d layers)" % nl, "n_gpus": 1, "steps": steps,
+        "warmup": I, "ms_per_step": el / steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (device-generated, copied to pinned host memory)",
+        "config": {"workload": "%s, CPU offload: B=%d L=%d layers=%d Hq=%d Hkv=%d D=%d sink=%d window=%d "
+                               "budget=%d radius=%d interval=%d" % (cfg.name, B, L, nl, Hq, Hkv, D,
+                                                                   cfg.S, W, cfg.K, cfg.r, I),
+                   "global_batch": B, "seq_len": L},
+        "per_layer_ms": {"select": round(ms("select"), 4), "gather": round(ms("gather"), 4),
+                         "append_step": round(ms("append") / nl, 4),
+                         "attention_step": round(ms("attn") / nl, 4),
+                         "per_step_amortised": round(per_step_layer * 1e3, 4)},
+        "gather": {"rows_per_head_total": int(gc.sum()), "union_rows": union,
+                   "bytes": gather_bytes, "gbps": gather_bytes / ms("gather") / 1e6},
+        "dense_offload_per_layer_ms": {"fetch": round(dense_fetch, 3), "attention": round(dense_attn, 3),
+                                       "bytes": dense_bytes,
+                                       "fetch_gbps": dense_bytes / dense_fetch / 1e6},
+        "speedup_vs_dense_offload": (dense_fetch + dense_attn) / (per_step_layer * 1e3),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +423,9 @@ def main():
                     help="2: the single-layer decode step (default); 3, 4, 5: the multi-layer "
                          "prediction-interval workloads")
     ap.add_argument("--intervals", type=int, default=3)
+    ap.add_argument("--offload", action="store_true",
+                    help="CPU-offload decoding on the 256K-context shape (with --config 4)")
+    ap.add_argument("--offload-layers", type=int, default=4)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy (for PMC byte-counter calibration) and exit")
     args = ap.parse_args()
@@ -295,6 +455,9 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
         return
 
+    if args.offload:
+        run_offload(CONFIGS[4 if args.config == 2 else args.config], args)
+        return
     if args.config != 2:
         run_interval(CONFIGS[args.config], args)
         return

@@ -132,6 +132,46 @@ tb_status tb_append_kv(const void *k_new, const void *v_new, void *k_cache, void
                        int B, int Hkv, int Lmax, int D, int dp, int n_p, void *stream);
 
 /*
+ * CPU-offload decoding ("Inference strategy": the full cache is retained and
+ * attention reads a sink buffer, a circular local window and an important
+ * buffer; "Significance": only the selected tokens are accessed). The full
+ * K/V cache [B, Hkv, Lmax, D] bf16 lives in pinned host memory (e.g.
+ * hipHostMalloc, torch pin_memory) and is read over the host link. Each
+ * query head h owns device buffers k_buf, v_buf [B, Hq, buf_rows, D] bf16;
+ * attention over them is tb_sparse_decode_attn with Hkv = Hq, Lmax =
+ * buf_rows, an identity list over the gathered slots and the implicit
+ * window (ctx_len = buf_rows, window = the window size).
+ *
+ * tb_offload_gather: for every (b, h) and i < count[b, h] (clamped to
+ * [0, cap]), the row t = idx[b, h, i] (clamped to [0, Lmax)) of KV head
+ * h / (Hq / Hkv) is copied from the host cache to slot s of head h's
+ * buffers, s = slot0 + i, or s = slot0 + t mod wrap when wrap > 0 (the
+ * circular window); rows whose slot would reach buf_rows are skipped.
+ * Limits: D in {64, 128}; Hq % Hkv == 0; 0 <= slot0 < buf_rows;
+ * slot0 + wrap <= buf_rows. Returns TB_ERR_INVALID_ARGUMENT if the caches
+ * are not pinned host memory.
+ */
+tb_status tb_offload_gather(const void *k_host, const void *v_host, int B, int Hkv, int Lmax,
+                            int D, const int32_t *idx, const int32_t *count, int cap, int Hq,
+                            void *k_buf, void *v_buf, int buf_rows, int slot0, int wrap,
+                            void *stream);
+
+/*
+ * tb_offload_append: one decode step of the offloaded cache. Per sequence b
+ * with L = ctx_len[b] == proj_len[b] < Lmax (otherwise nothing is written
+ * for b): k_new[b, j], v_new[b, j] [B, Hkv, D] are written at position L of
+ * the host cache and, when window > 0, into slot buf_rows - window +
+ * L mod window of the buffers of every query head of group j; the new key is
+ * projected (kp[b, j, L] = fp16(k_new[b, j] wk[j]^T), kp and wk on the
+ * device as for tb_project_keys); ctx_len[b] and proj_len[b] become L + 1.
+ * Limits: D in {64, 128}, dp in {16, 32}, 0 <= window <= buf_rows.
+ */
+tb_status tb_offload_append(const void *k_new, const void *v_new, const void *wk, void *k_host,
+                            void *v_host, void *kp, int32_t *ctx_len, int32_t *proj_len, int B,
+                            int Hkv, int Lmax, int D, int dp, void *k_buf, void *v_buf, int Hq,
+                            int buf_rows, int window, void *stream);
+
+/*
  * Scoring ("Core architecture", scoring): token importance is the dot product
  * of the predicted query with the projected key; query head h reads KV head
  * h / (Hq / Hkv):

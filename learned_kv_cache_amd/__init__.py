@@ -60,6 +60,12 @@ def lib():
     L.tb_project_keys.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
     L.tb_append_kv.restype = _i
     L.tb_append_kv.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp]
+    L.tb_offload_gather.restype = _i
+    L.tb_offload_gather.argtypes = [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _i, _i, _vp, _vp, _i, _i, _i,
+                                    _vp]
+    L.tb_offload_append.restype = _i
+    L.tb_offload_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
+                                    _vp, _i, _i, _i, _vp]
     L.tb_score.restype = _i
     L.tb_score.argtypes = [_vp, _i, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
     L.tb_select_workspace_bytes.restype = _sz
@@ -189,6 +195,54 @@ def tb_append_kv(k_new, v_new, k_cache, v_cache, kp, wk, ctx_len, proj_len, n_p,
                               _ptr(ctx_len, torch.int32, "ctx_len"),
                               _ptr(proj_len, torch.int32, "proj_len"), B, Hkv, Lmax, D, dp,
                               int(n_p), _stream(stream)))
+
+
+def _host_ptr(t, name):
+    if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
+        raise ValueError("%s must be a pinned host tensor" % name)
+    if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 4:
+        raise ValueError("%s must be a contiguous 4-d bfloat16 tensor" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def tb_offload_gather(k_host, v_host, idx, count, k_buf, v_buf, slot0=0, wrap=0, stream=None):
+    """Copy the listed rows of the pinned host cache into the per-query-head
+    device buffers: slot slot0 + i (or slot0 + t % wrap when wrap > 0)."""
+    B, Hkv, Lmax, D = k_host.shape
+    Bq, Hq, buf_rows, Db = k_buf.shape
+    cap = idx.shape[-1]
+    if (tuple(v_host.shape) != (B, Hkv, Lmax, D) or (Bq, Db) != (B, D)
+            or tuple(v_buf.shape) != tuple(k_buf.shape) or tuple(idx.shape) != (B, Hq, cap)
+            or tuple(count.shape) != (B, Hq)):
+        raise ValueError("tb_offload_gather: shape mismatch")
+    _check(lib().tb_offload_gather(_host_ptr(k_host, "k_host"), _host_ptr(v_host, "v_host"), B, Hkv,
+                                   Lmax, D, _ptr(idx, torch.int32, "idx", 3),
+                                   _ptr(count, torch.int32, "count", 2), cap, Hq,
+                                   _ptr(k_buf, torch.bfloat16, "k_buf", 4),
+                                   _ptr(v_buf, torch.bfloat16, "v_buf", 4), buf_rows, int(slot0),
+                                   int(wrap), _stream(stream)))
+
+
+def tb_offload_append(k_new, v_new, wk, k_host, v_host, kp, ctx_len, proj_len, k_buf, v_buf,
+                      window, stream=None):
+    """One decode step of the offloaded cache: new rows to the host cache and
+    the window slots, the new key projected into kp, lengths advanced."""
+    B, Hkv, Lmax, D = k_host.shape
+    dp = wk.shape[1]
+    Hq, buf_rows = k_buf.shape[1], k_buf.shape[2]
+    if (tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D)
+            or tuple(wk.shape) != (Hkv, dp, D) or tuple(kp.shape) != (B, Hkv, Lmax, dp)
+            or tuple(k_buf.shape) != (B, Hq, buf_rows, D) or tuple(v_buf.shape) != tuple(k_buf.shape)):
+        raise ValueError("tb_offload_append: shape mismatch")
+    _check(lib().tb_offload_append(_ptr(k_new, torch.bfloat16, "k_new", 3),
+                                   _ptr(v_new, torch.bfloat16, "v_new", 3),
+                                   _ptr(wk, torch.bfloat16, "wk", 3), _host_ptr(k_host, "k_host"),
+                                   _host_ptr(v_host, "v_host"), _ptr(kp, torch.float16, "kp", 4),
+                                   _ptr(ctx_len, torch.int32, "ctx_len"),
+                                   _ptr(proj_len, torch.int32, "proj_len"), B, Hkv, Lmax, D, dp,
+                                   _ptr(k_buf, torch.bfloat16, "k_buf", 4),
+                                   _ptr(v_buf, torch.bfloat16, "v_buf", 4), Hq, buf_rows,
+                                   int(window), _stream(stream)))
 
 
 # ---------------------------------------------------------------- scoring

@@ -25,6 +25,18 @@ tb_status check_launch(const char *what) {
     return TB_OK;
 }
 
+// Device address of pinned host memory (false if ptr is not pinned host
+// memory the device can reach); the failed query's error is cleared.
+bool host_to_device(const void *ptr, const void **dev) {
+    void *d = nullptr;
+    if (hipHostGetDevicePointer(&d, const_cast<void *>(ptr), 0) != hipSuccess || !d) {
+        (void)hipGetLastError();
+        return false;
+    }
+    *dev = d;
+    return true;
+}
+
 }  // namespace tb
 
 using tb::aligned16;
@@ -131,6 +143,54 @@ tb_status tb_append_kv(const void *k_new, const void *v_new, void *k_cache, void
                "tb_append_kv: D must be 64 or 128 and dp 16 or 32 (got %d, %d)", D, dp);
     return tb::launch_append(k_new, v_new, k_cache, v_cache, kp, wk, ctx_len, proj_len, B, Hkv,
                              Lmax, D, dp, n_p, static_cast<hipStream_t>(stream));
+}
+
+tb_status tb_offload_gather(const void *k_host, const void *v_host, int B, int Hkv, int Lmax,
+                            int D, const int32_t *idx, const int32_t *count, int cap, int Hq,
+                            void *k_buf, void *v_buf, int buf_rows, int slot0, int wrap,
+                            void *stream) {
+    TB_REQUIRE(k_host && v_host && idx && count && k_buf && v_buf, TB_ERR_INVALID_ARGUMENT,
+               "tb_offload_gather: null pointer");
+    TB_REQUIRE(aligned16(k_host) && aligned16(v_host) && aligned4(idx) && aligned4(count) &&
+                   aligned16(k_buf) && aligned16(v_buf),
+               TB_ERR_INVALID_ARGUMENT, "tb_offload_gather: misaligned pointer");
+    TB_REQUIRE(B >= 1 && B <= 65535 && Hkv >= 1 && Hq >= 1 && Hq <= 65535 && Lmax >= 1 &&
+                   cap >= 1 && buf_rows >= 1 && slot0 >= 0 && slot0 < buf_rows && wrap >= 0 &&
+                   slot0 + wrap <= buf_rows,
+               TB_ERR_INVALID_ARGUMENT, "tb_offload_gather: bad sizes");
+    TB_REQUIRE(Hq % Hkv == 0, TB_ERR_INVALID_ARGUMENT, "tb_offload_gather: Hq %% Hkv != 0");
+    TB_REQUIRE(D == 64 || D == 128, TB_ERR_UNSUPPORTED_SHAPE, "tb_offload_gather: D must be 64 or 128");
+    const void *kd, *vd;
+    TB_REQUIRE(tb::host_to_device(k_host, &kd) && tb::host_to_device(v_host, &vd),
+               TB_ERR_INVALID_ARGUMENT, "tb_offload_gather: caches must be pinned host memory");
+    return tb::launch_offload_gather(kd, vd, B, Hkv, Lmax, D, idx, count, cap, Hq, k_buf, v_buf,
+                                     buf_rows, slot0, wrap, static_cast<hipStream_t>(stream));
+}
+
+tb_status tb_offload_append(const void *k_new, const void *v_new, const void *wk, void *k_host,
+                            void *v_host, void *kp, int32_t *ctx_len, int32_t *proj_len, int B,
+                            int Hkv, int Lmax, int D, int dp, void *k_buf, void *v_buf, int Hq,
+                            int buf_rows, int window, void *stream) {
+    TB_REQUIRE(k_new && v_new && wk && k_host && v_host && kp && ctx_len && proj_len && k_buf &&
+                   v_buf,
+               TB_ERR_INVALID_ARGUMENT, "tb_offload_append: null pointer");
+    TB_REQUIRE(aligned16(k_new) && aligned16(v_new) && aligned16(wk) && aligned16(k_host) &&
+                   aligned16(v_host) && aligned16(kp) && aligned4(ctx_len) && aligned4(proj_len) &&
+                   aligned16(k_buf) && aligned16(v_buf),
+               TB_ERR_INVALID_ARGUMENT, "tb_offload_append: misaligned pointer");
+    TB_REQUIRE(B >= 1 && B <= 65535 && Hkv >= 1 && Hq >= 1 && Lmax >= 1 && buf_rows >= 1 &&
+                   window >= 0 && window <= buf_rows,
+               TB_ERR_INVALID_ARGUMENT, "tb_offload_append: bad sizes");
+    TB_REQUIRE(Hq % Hkv == 0, TB_ERR_INVALID_ARGUMENT, "tb_offload_append: Hq %% Hkv != 0");
+    TB_REQUIRE((D == 64 || D == 128) && (dp == 16 || dp == 32), TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_offload_append: D must be 64 or 128 and dp 16 or 32");
+    const void *kd, *vd;
+    TB_REQUIRE(tb::host_to_device(k_host, &kd) && tb::host_to_device(v_host, &vd),
+               TB_ERR_INVALID_ARGUMENT, "tb_offload_append: caches must be pinned host memory");
+    return tb::launch_offload_append(k_new, v_new, wk, const_cast<void *>(kd),
+                                     const_cast<void *>(vd), kp, ctx_len, proj_len, B, Hkv, Lmax,
+                                     D, dp, k_buf, v_buf, Hq, buf_rows, window,
+                                     static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------- scoring

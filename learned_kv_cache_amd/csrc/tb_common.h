@@ -81,6 +81,15 @@ tb_status launch_predict_project(const void *x, const void *w1, const void *w2, 
 tb_status launch_append(const void *k_new, const void *v_new, void *kc, void *vc, void *kp,
                         const void *wk, int32_t *ctx, int32_t *plen, int B, int Hkv, int Lmax,
                         int D, int dp, int n_p, hipStream_t st);
+bool host_to_device(const void *ptr, const void **dev);
+tb_status launch_offload_gather(const void *kh, const void *vh, int B, int Hkv, int Lmax, int D,
+                                const int32_t *idx, const int32_t *count, int cap, int Hq,
+                                void *kb, void *vb, int buf_rows, int slot0, int wrap,
+                                hipStream_t st);
+tb_status launch_offload_append(const void *k_new, const void *v_new, const void *wk, void *kh,
+                                void *vh, void *kp, int32_t *ctx, int32_t *plen, int B, int Hkv,
+                                int Lmax, int D, int dp, void *kb, void *vb, int Hq,
+                                int buf_rows, int window, hipStream_t st);
 tb_status launch_project(const void *kc, const void *wk, void *kp, const int32_t *pos0, int ntok,
                          int B, int Hkv, int Lmax, int D, int dp, hipStream_t st);
 tb_status launch_score(const float *qhat, int n_slots, int slot, const void *kp,

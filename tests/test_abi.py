@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(tb):
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     lib = ctypes.CDLL(tb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -73,6 +73,20 @@ def test_validation_rejects_before_launch(tb):
     assert L.tb_append_kv(*ap(0, 16)) == 1
     assert L.tb_append_kv(*ap(4, 8)) == 2
     assert L.tb_append_kv(*ap(4, 16, None)) == 1
+    # offload: bad slot range, unsupported D, unpinned (unregistered) host memory
+    og = lambda D, slot0, wrap, host=vp(FAKE): (host, vp(FAKE), 1, 2, 300, D, vp(FAKE), vp(FAKE), 64,
+                                                8, vp(FAKE), vp(FAKE), 100, slot0, wrap, None)
+    assert L.tb_offload_gather(*og(128, 100, 0)) == 1
+    assert L.tb_offload_gather(*og(128, 50, 60)) == 1
+    assert L.tb_offload_gather(*og(96, 0, 0)) == 2
+    import torch
+    if not torch.cuda.is_available():
+        # every other argument passes validation here, so only run where no
+        # kernel could be launched should the pinned-memory check let it by
+        buf = ctypes.create_string_buffer(4096 + 16)
+        plain = vp((ctypes.addressof(buf) + 15) & ~15)
+        assert L.tb_offload_gather(*og(128, 0, 0, plain)) == 1
+        assert b"pinned" in L.tb_last_error_detail()
     assert L.tb_score(vp(FAKE), 1, 0, vp(FAKE), vp(FAKE), vp(FAKE), 1, 18, 2, 300, 16, None) == 2
     assert L.tb_score(vp(FAKE), 1, 0, vp(FAKE), vp(FAKE), vp(FAKE), 1, 9, 2, 300, 16, None) == 1
     assert L.tb_predict_queries(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 500, 128, 128, vp(FAKE), 1 << 20, None) == 2
