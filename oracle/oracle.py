@@ -61,6 +61,9 @@ def lib():
     L.orc_append_kv.restype = None
     L.orc_append_kv.argtypes = [_u16p, _u16p, _u16p, _u16p, _u16p, _u16p, _i32p, _i32p,
                                 _c_int, _c_int, _c_int, _c_int, _c_int, _c_int]
+    L.orc_distill_loss.restype = None
+    L.orc_distill_loss.argtypes = [_u16p, _u16p, _f32p, _u16p, _i32p, _c_int, _c_int, _c_int,
+                                   _c_int, _c_int, _c_int, _c_int, ctypes.c_double, _f32p]
     L.orc_score.restype = None
     L.orc_score.argtypes = [_f32p, _c_int, _c_int, _u16p, _i32p, _f32p,
                             _c_int, _c_int, _c_int, _c_int, _c_int]
@@ -143,6 +146,24 @@ def append_kv(k_new, v_new, kc, vc, kp, wk, ctx_len, proj_len, n_p):
     assert ctx_len.dtype == proj_len.dtype == np.int32
     lib().orc_append_kv(_u16(k_new), _u16(v_new), kc, vc, kp, _u16(wk), ctx_len, proj_len,
                         B, Hkv, Lmax, D, dp, int(n_p))
+
+
+def distill_loss(q, kc, qhat, kp, pos, scale=None):
+    """Cross entropy between the teacher's causal attention distribution and
+    the predictor's logits at R query positions: loss [B, R, Hq] fp32.
+    q [B,R,Hq,D] bf16 bits, kc [B,Hkv,Lmax,D] bf16 bits, qhat [B,R,Hq,dp]
+    fp32, kp [B,Hkv,Lmax,dp] fp16 bits, pos [B,R] int32."""
+    q, kc, kp = _u16(q), _u16(kc), _u16(kp)
+    qhat = np.ascontiguousarray(qhat, dtype=np.float32)
+    B, R, Hq, D = q.shape
+    _, Hkv, Lmax, _ = kc.shape
+    dp = kp.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    loss = np.zeros((B, R, Hq), np.float32)
+    lib().orc_distill_loss(q, kc, qhat, kp, _i32(pos), B, R, Hq, Hkv, Lmax, D, dp, float(scale),
+                           loss)
+    return loss
 
 
 def score(qhat, kp, proj_len, Hq, n_slots=1, slot=0, fill=np.nan):

@@ -415,6 +415,68 @@ int orc_select_dilate(const float *scores, const int *ctx_len, const int *proj_l
     return status;
 }
 
+/*
+ * Distillation loss ("Training": the predictor learns from the frozen base
+ * model's masked causal attention distribution by minimizing the cross
+ * entropy between the teacher's attention logits and the predictor's
+ * logits; the loss is evaluated at a subset of R query positions, which
+ * makes it O(R L) instead of O(L^2)). Per (b, r, query head h) with
+ * position i = pos[b, r] (clamped to [0, Lmax - 1]) and KV head h / g, over
+ * the causal tokens t <= i:
+ *   teacher logits z_t = scale * q[b, r, h] . k[b, h/g, t]      (bf16 inputs)
+ *   student logits s_t = qhat[b, r, h] . kp[b, h/g, t]          (fp32 . fp16)
+ *   p = softmax(z);  loss[b, r, h] = -sum_t p_t log softmax(s)_t
+ *                                  = logsumexp_t(s_t) - sum_t p_t s_t
+ *   q [B, R, Hq, D] bf16, qhat [B, R, Hq, dp] fp32, loss [B, R, Hq] fp32.
+ */
+void orc_distill_loss(const uint16_t *q, const uint16_t *kc, const float *qhat,
+                      const uint16_t *kp, const int *pos, int B, int R, int Hq, int Hkv,
+                      int Lmax, int D, int dp, double scale, float *loss)
+{
+    int g = Hq / Hkv;
+    double *z = (double *)malloc(sizeof(double) * (size_t)Lmax);
+    double *sl = (double *)malloc(sizeof(double) * (size_t)Lmax);
+    for (int b = 0; b < B; ++b)
+        for (int r = 0; r < R; ++r) {
+            int i = pos[(size_t)b * R + r];
+            if (i < 0)
+                i = 0;
+            if (i > Lmax - 1)
+                i = Lmax - 1;
+            for (int h = 0; h < Hq; ++h) {
+                const uint16_t *qr = q + (((size_t)b * R + r) * Hq + h) * D;
+                const float *qh = qhat + (((size_t)b * R + r) * Hq + h) * dp;
+                size_t head = (size_t)b * Hkv + h / g;
+                double zmax = -INFINITY, smax = -INFINITY;
+                for (int t = 0; t <= i; ++t) {
+                    const uint16_t *kr = kc + (head * Lmax + t) * D;
+                    const uint16_t *kpr = kp + (head * Lmax + t) * dp;
+                    double a = 0.0, c = 0.0;
+                    for (int d = 0; d < D; ++d)
+                        a += bf16_value(qr[d]) * bf16_value(kr[d]);
+                    for (int d = 0; d < dp; ++d)
+                        c += (double)qh[d] * f16_value(kpr[d]);
+                    z[t] = scale * a;
+                    sl[t] = c;
+                    if (z[t] > zmax)
+                        zmax = z[t];
+                    if (sl[t] > smax)
+                        smax = sl[t];
+                }
+                double zs = 0.0, ps = 0.0, ss = 0.0;
+                for (int t = 0; t <= i; ++t) {
+                    double w = exp(z[t] - zmax);
+                    zs += w;
+                    ps += w * sl[t];
+                    ss += exp(sl[t] - smax);
+                }
+                loss[((size_t)b * R + r) * Hq + h] = (float)(smax + log(ss) - ps / zs);
+            }
+        }
+    free(sl);
+    free(z);
+}
+
 /* ------------------------------------------------------------------ */
 /* Decode attention over the attended positions only ("Significance":  */
 /* the full cache is kept, only the most relevant tokens are read).     */
