@@ -410,6 +410,62 @@ def run_offload(cfg, args):
     print(json.dumps(res), flush=True)
 
 
+def run_distill(cfg, args):
+    """The distillation loss on the 64K single-layer shape: R query positions
+    per sequence taken from the late context (the last quarter, always
+    including the final token), every query head, the causal tokens up to
+    each position. Reports the time per call against HBM (K and K' read
+    once per row group) and against bf16 MFMA (teacher logits)."""
+    import torch
+    import learned_kv_cache_amd as tb
+
+    B, Hq, Hkv, D, dp, L = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.dp, cfg.L
+    R = args.distill_positions
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260101 + cfg.cid)
+    rn = lambda *sh: torch.randn(*sh, generator=gen, device="cuda").to(torch.bfloat16)
+    reps = []
+    for i in range(args.replicas):
+        reps.append(dict(q=rn(B, R, Hq, D), kc=rn(B, Hkv, L, D),
+                         qhat=torch.randn(B, R, Hq, dp, generator=gen, device="cuda"),
+                         kp=torch.randn(B, Hkv, L, dp, generator=gen, device="cuda").half()))
+    pos_np = np.sort(np.random.default_rng(20260101).integers(3 * L // 4, L, size=(B, R)), axis=1)
+    pos_np[:, -1] = L - 1
+    pos = torch.from_numpy(pos_np.astype(np.int32)).cuda()
+    loss = torch.empty(B, R, Hq, device="cuda")
+    ws = tb.new_workspace(tb.tb_distill_workspace_bytes(B, R, Hq, Hkv, L))
+    for r_ in reps:
+        tb.tb_distill_loss(r_["q"], r_["kc"], r_["qhat"], r_["kp"], pos, loss, ws)
+    torch.cuda.synchronize()
+    n = 10 * len(reps)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n):
+        r_ = reps[i % len(reps)]
+        tb.tb_distill_loss(r_["q"], r_["kc"], r_["qhat"], r_["kp"], pos, loss, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    toks = int((pos_np.astype(np.int64) + 1).sum()) * Hq
+    flops = 2 * toks * (D + dp)
+    ng = -(-R * (Hq // Hkv) // 256)
+    last = int(pos_np.max()) + 1
+    hbm = B * Hkv * ng * last * (D + dp) * 2
+    res = {
+        "metric": "distillation-loss calls/s at 64K ctx, %d query positions" % R,
+        "value": 1e6 / us, "unit": "calls/s", "n_gpus": 1, "steps": n, "warmup": len(reps),
+        "ms_per_step": us / 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (device-generated)",
+        "config": {"workload": "distillation loss: B=%d L=%d R=%d positions in the last quarter "
+                               "Hq=%d Hkv=%d D=%d d'=%d, %d rotated replicas"
+                               % (B, L, R, Hq, Hkv, D, dp, len(reps)),
+                   "global_batch": B, "seq_len": L},
+        "hbm": {"bytes": hbm, "gbps": hbm / us / 1e3, "frac": hbm / us / 1e3 / PEAK_HBM_GBS},
+        "mfma": {"flops": flops, "tflops": flops / us / 1e6, "frac_of_bf16_dense": flops / us / 1e6 / 2500.0},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,6 +482,9 @@ def main():
     ap.add_argument("--offload", action="store_true",
                     help="CPU-offload decoding on the 256K-context shape (with --config 4)")
     ap.add_argument("--offload-layers", type=int, default=4)
+    ap.add_argument("--distill", action="store_true",
+                    help="time the distillation loss on the 64K single-layer shape")
+    ap.add_argument("--distill-positions", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a 1 GiB device copy (for PMC byte-counter calibration) and exit")
     args = ap.parse_args()
@@ -455,6 +514,9 @@ def main():
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
         return
 
+    if args.distill:
+        run_distill(CONFIGS[2], args)
+        return
     if args.offload:
         run_offload(CONFIGS[4 if args.config == 2 else args.config], args)
         return

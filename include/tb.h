@@ -172,6 +172,29 @@ tb_status tb_offload_append(const void *k_new, const void *v_new, const void *wk
                             int buf_rows, int window, void *stream);
 
 /*
+ * Distillation loss ("Training": the predictor is trained on the frozen
+ * model's masked causal attention distribution, minimizing the cross entropy
+ * between the teacher's attention logits and the predictor's logits, with
+ * the loss taken at a subset of R query positions so the cost is O(R L)).
+ * Per (b, r, query head h), i = pos[b, r] clamped to [0, Lmax - 1], KV head
+ * h / (Hq / Hkv), over the causal tokens t <= i:
+ *   z_t = scale * q[b, r, h] . k_cache[b, h/g, t]   (teacher logits)
+ *   s_t = qhat[b, r, h] . kp[b, h/g, t]             (predictor logits)
+ *   loss[b, r, h] = logsumexp_t(s_t) - sum_t softmax(z)_t s_t     (fp32)
+ *   q    [B, R, Hq, D]  bf16      qhat [B, R, Hq, dp] fp32
+ *   k_cache [B, Hkv, Lmax, D] bf16, kp [B, Hkv, Lmax, dp] fp16
+ *   pos  [B, R] int32, device;    loss [B, R, Hq] fp32
+ * Limits: D in {64, 128}, dp in {16, 32}, Hq % Hkv == 0, B * Hkv <= 65535.
+ * The workspace (zero-filled once) holds per-split partials and arrival
+ * counters, which every call leaves at zero.
+ */
+size_t tb_distill_workspace_bytes(int B, int R, int Hq, int Hkv, int Lmax);
+tb_status tb_distill_loss(const void *q, const void *k_cache, const float *qhat, const void *kp,
+                          const int32_t *pos, int B, int R, int Hq, int Hkv, int Lmax, int D,
+                          int dp, float scale, float *loss, void *workspace, size_t ws_bytes,
+                          void *stream);
+
+/*
  * Scoring ("Core architecture", scoring): token importance is the dot product
  * of the predicted query with the projected key; query head h reads KV head
  * h / (Hq / Hkv):

@@ -66,6 +66,11 @@ def lib():
     L.tb_offload_append.restype = _i
     L.tb_offload_append.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp,
                                     _vp, _i, _i, _i, _vp]
+    L.tb_distill_workspace_bytes.restype = _sz
+    L.tb_distill_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+    L.tb_distill_loss.restype = _i
+    L.tb_distill_loss.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                  ctypes.c_float, _vp, _vp, _sz, _vp]
     L.tb_score.restype = _i
     L.tb_score.argtypes = [_vp, _i, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
     L.tb_select_workspace_bytes.restype = _sz
@@ -243,6 +248,31 @@ def tb_offload_append(k_new, v_new, wk, k_host, v_host, kp, ctx_len, proj_len, k
                                    _ptr(k_buf, torch.bfloat16, "k_buf", 4),
                                    _ptr(v_buf, torch.bfloat16, "v_buf", 4), Hq, buf_rows,
                                    int(window), _stream(stream)))
+
+
+def tb_distill_workspace_bytes(B, R, Hq, Hkv, Lmax):
+    return int(lib().tb_distill_workspace_bytes(B, R, Hq, Hkv, Lmax))
+
+
+def tb_distill_loss(q, k_cache, qhat, kp, pos, loss, workspace, scale=None, stream=None):
+    """loss[b, r, h] = cross entropy between softmax(scale q.k_t) and the
+    predictor's logits qhat.kp_t over the causal tokens t <= pos[b, r]."""
+    B, R, Hq, D = q.shape
+    _, Hkv, Lmax, _ = k_cache.shape
+    dp = kp.shape[-1]
+    if (tuple(k_cache.shape) != (B, Hkv, Lmax, D) or tuple(qhat.shape) != (B, R, Hq, dp)
+            or tuple(kp.shape) != (B, Hkv, Lmax, dp) or tuple(pos.shape) != (B, R)
+            or tuple(loss.shape) != (B, R, Hq)):
+        raise ValueError("tb_distill_loss: shape mismatch")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    wp, wn = _ws(workspace)
+    _check(lib().tb_distill_loss(_ptr(q, torch.bfloat16, "q", 4), _ptr(k_cache, torch.bfloat16, "k_cache", 4),
+                                 _ptr(qhat, torch.float32, "qhat", 4), _ptr(kp, torch.float16, "kp", 4),
+                                 _ptr(pos, torch.int32, "pos", 2), B, R, Hq, Hkv, Lmax, D, dp,
+                                 ctypes.c_float(scale), _ptr(loss, torch.float32, "loss", 3), wp, wn,
+                                 _stream(stream)))
+    return loss
 
 
 # ---------------------------------------------------------------- scoring

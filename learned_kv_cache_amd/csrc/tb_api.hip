@@ -193,6 +193,37 @@ tb_status tb_offload_append(const void *k_new, const void *v_new, const void *wk
                                      static_cast<hipStream_t>(stream));
 }
 
+size_t tb_distill_workspace_bytes(int B, int R, int Hq, int Hkv, int Lmax) {
+    if (B <= 0 || R <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || Hq % Hkv) return 0;
+    return tb::distill_ws_layout(B, R, Hq, Hkv, Lmax, nullptr, nullptr, nullptr);
+}
+
+tb_status tb_distill_loss(const void *q, const void *k_cache, const float *qhat, const void *kp,
+                          const int32_t *pos, int B, int R, int Hq, int Hkv, int Lmax, int D,
+                          int dp, float scale, float *loss, void *workspace, size_t ws_bytes,
+                          void *stream) {
+    TB_REQUIRE(q && k_cache && qhat && kp && pos && loss && workspace, TB_ERR_INVALID_ARGUMENT,
+               "tb_distill_loss: null pointer");
+    TB_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned4(qhat) && aligned16(kp) &&
+                   aligned4(pos) && aligned4(loss) && aligned16(workspace),
+               TB_ERR_INVALID_ARGUMENT, "tb_distill_loss: misaligned pointer");
+    TB_REQUIRE(B >= 1 && R >= 1 && Hq >= 1 && Hkv >= 1 && Lmax >= 1 &&
+                   (long long)B * Hkv <= 65535 && (long long)R * Hq <= (1LL << 24),
+               TB_ERR_INVALID_ARGUMENT, "tb_distill_loss: bad sizes");
+    TB_REQUIRE(Hq % Hkv == 0, TB_ERR_INVALID_ARGUMENT, "tb_distill_loss: Hq %% Hkv != 0");
+    TB_REQUIRE((D == 64 || D == 128) && (dp == 16 || dp == 32), TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_distill_loss: D must be 64 or 128 and dp 16 or 32");
+    TB_REQUIRE(scale == scale, TB_ERR_INVALID_ARGUMENT, "tb_distill_loss: scale is NaN");
+    const size_t need = tb_distill_workspace_bytes(B, R, Hq, Hkv, Lmax);
+    TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
+               "tb_distill_loss: workspace %zu < %zu bytes", ws_bytes, need);
+    float *part;
+    uint32_t *ctr;
+    tb::distill_ws_layout(B, R, Hq, Hkv, Lmax, workspace, &part, &ctr);
+    return tb::launch_distill(q, k_cache, qhat, kp, pos, B, R, Hq, Hkv, Lmax, D, dp, scale, part,
+                              ctr, loss, static_cast<hipStream_t>(stream));
+}
+
 // ---------------------------------------------------------------- scoring
 tb_status tb_score(const float *qhat, int n_slots, int slot, const void *kp,
                    const int32_t *proj_len, float *scores, int B, int Hq, int Hkv, int Lmax,

@@ -82,6 +82,12 @@ tb_status launch_append(const void *k_new, const void *v_new, void *kc, void *vc
                         const void *wk, int32_t *ctx, int32_t *plen, int B, int Hkv, int Lmax,
                         int D, int dp, int n_p, hipStream_t st);
 bool host_to_device(const void *ptr, const void **dev);
+size_t distill_ws_layout(int B, int R, int Hq, int Hkv, int Lmax, void *base, float **part,
+                         uint32_t **ctr);
+tb_status launch_distill(const void *q, const void *kc, const float *qhat, const void *kp,
+                         const int32_t *pos, int B, int R, int Hq, int Hkv, int Lmax, int D,
+                         int dp, float scale, float *part, uint32_t *ctr, float *loss,
+                         hipStream_t st);
 tb_status launch_offload_gather(const void *kh, const void *vh, int B, int Hkv, int Lmax, int D,
                                 const int32_t *idx, const int32_t *count, int cap, int Hq,
                                 void *kb, void *vb, int buf_rows, int slot0, int wrap,

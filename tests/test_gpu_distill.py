@@ -1,0 +1,58 @@
+"""GPU parity of the distillation loss (tb_distill_loss) against the oracle:
+ragged query positions (including the first and the last token), several
+row groups and token splits, both head sizes. Tolerance: the teacher logits
+are exact bf16 products summed in fp32 and the student logits fp32 products
+of fp32 and fp16 values; the softmax sums run over up to a few thousand
+terms in fp32, so |gpu - ref| <= 2e-4 * max(1, |ref|). A second call on the
+same workspace must give the same bits and leave its counters at zero."""
+import numpy as np
+import pytest
+import torch
+
+from synthetic import f16_bits, normal_bf16, rng_for
+from gpu_util import dev, dev32, host, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import learned_kv_cache_amd as tb
+    tb.lib()
+    return tb
+
+
+@pytest.mark.parametrize("B,R,Hq,Hkv,Lmax,D,dp", [
+    (2, 5, 8, 2, 3000, 128, 32),
+    (1, 70, 32, 8, 5000, 128, 32),     # 280 rows per KV head: two row groups
+    (2, 9, 4, 1, 2100, 64, 16),
+])
+def test_distill_matches_oracle(tb, orc, B, R, Hq, Hkv, Lmax, D, dp):
+    say("distill", B, R, Hq, Hkv, Lmax, D, dp)
+    rng = rng_for(110, R, Lmax)
+    q = normal_bf16(rng, (B, R, Hq, D))
+    kc = normal_bf16(rng, (B, Hkv, Lmax, D))
+    qhat = (rng.standard_normal((B, R, Hq, dp)) * 0.5).astype(np.float32)
+    kp = f16_bits(rng.standard_normal((B, Hkv, Lmax, dp)).astype(np.float32))
+    pos = np.sort(rng.integers(0, Lmax, size=(B, R)), axis=1).astype(np.int32)
+    pos[:, 0] = 0
+    pos[:, -1] = Lmax - 1
+    ref = orc.distill_loss(q, kc, qhat, kp, pos)
+    ws = tb.new_workspace(tb.tb_distill_workspace_bytes(B, R, Hq, Hkv, Lmax))
+    loss = torch.full((B, R, Hq), float("nan"), device="cuda")
+    args = (dev(q, torch.bfloat16), dev(kc, torch.bfloat16), dev32(qhat), dev(kp, torch.float16),
+            dev32(pos))
+    tb.tb_distill_loss(*args, loss, ws)
+    torch.cuda.synchronize()
+    got = host(loss).astype(np.float64)
+    err = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
+    assert np.isfinite(got).all()
+    assert err.max() <= 2e-4, (err.max(), np.unravel_index(err.argmax(), err.shape))
+    again = torch.full_like(loss, float("nan"))
+    tb.tb_distill_loss(*args, again, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(again), host(loss))
+    nctr = B * Hkv * (-(-R * (Hq // Hkv) // 256))
+    assert int(ws[-((nctr * 4 + 255) // 256 * 256):].count_nonzero()) == 0
