@@ -13,11 +13,11 @@
 //
 // Four launches, all integer work:
 //   bounds   eight 1024-thread workgroups per segment sample the pooled key32
-//            of every stride-th eligible token (every token when the region
-//            holds at most 8192); the last to arrive takes sample ranks on
-//            either side of the budget's rank, 5 sigma of the sample rank
-//            apart, as a band [T_lo, T_hi] that holds the K-th key with
-//            overwhelming odds;
+//            of every stride-th eligible token, stride = ceil((Lmax - S) /
+//            8192) (every token when that is 1); the last to arrive takes
+//            sample ranks on either side of the budget's rank, 5 sigma of the
+//            sample rank apart, as a band [T_lo, T_hi] that holds the K-th
+//            key with overwhelming odds;
 //   classify per (segment, 2048-token chunk): tokens above the band go
 //            straight into a selection bitmap (wave ballots); tokens in it are
 //            gathered in LDS and written to the chunk's own candidate slots;
@@ -277,33 +277,38 @@ __global__ __launch_bounds__(T3) void bounds_kernel(const float *__restrict__ sc
     __shared__ int s_sel[4];
     __shared__ bool s_last;
     const int seg = blockIdx.y, b = seg / Hq;
+    // the sample grid depends only on S and Lmax, so the scores are loaded
+    // before the lengths are known; neighbours outside E are dropped after
+    const int stride = Lmax > S + NSAMP ? (Lmax - S + NSAMP - 1) / NSAMP : 1;
+    const int off = stride / 2;
+    const float *sc = scores + (size_t)seg * Lmax;
+    const int j = blockIdx.x * T3 + threadIdx.x;
+    const int t = S + off + j * stride;
+    constexpr int NX = R >= 0 ? 2 * R + 1 : 1;
+    float x[NX];
+    if constexpr (R >= 0) {
+#pragma unroll
+        for (int u = 0; u < NX; ++u) {
+            int p = t - R + u;
+            p = p < S ? S : (p >= Lmax ? Lmax - 1 : p);
+            x[u] = t < Lmax ? sc[p] : 0.f;
+        }
+    }
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
     const int nE = g.e1 - g.e0;
     if (g.bad || g.need == 0 || g.need == nE) return;   // the same for every workgroup of seg
-    const int stride = (nE + NSAMP - 1) / NSAMP;
-    const int off = stride / 2;
-    const int ns = (nE - off + stride - 1) / stride;
-    const float *sc = scores + (size_t)seg * Lmax;
+    const int ns = nE > off ? (nE - off + stride - 1) / stride : 0;
     uint32_t *sp = samp + (size_t)seg * NSAMP;
-    const int j = blockIdx.x * T3 + threadIdx.x;
     if (j < ns) {
-        const int t = g.e0 + off + j * stride;
-        uint32_t key;
+        uint32_t key = 0u;
         if constexpr (R >= 0) {
-            // key32 of a pooled key = max order key over [t - R, t + R] within
-            // E; a neighbour outside E is clamped onto E's end, which is in range
-            float x[2 * R + 1];
+            // key32 of a pooled key = max order key over [t - R, t + R]
+            // within E (t itself is in E)
 #pragma unroll
-            for (int u = 0; u <= 2 * R; ++u) {
-                int p = t - R + u;
-                p = p < g.e0 ? g.e0 : (p >= g.e1 ? g.e1 - 1 : p);
-                x[u] = sc[p];
-            }
-            key = order_key(x[0]);
-#pragma unroll
-            for (int u = 1; u <= 2 * R; ++u) {
+            for (int u = 0; u < NX; ++u) {
+                const int p = t - R + u;
                 const uint32_t k = order_key(x[u]);
-                key = k > key ? k : key;
+                if (p >= g.e0 && p < g.e1 && k > key) key = k;
             }
         } else {
             key = (uint32_t)(pooled_key_g(sc, t, g.e0, g.e1, r) >> 32);

@@ -162,6 +162,26 @@ def test_select_c2_shapes(tb, orc, r):
     assert_same_selection(orc, tb, s, [65536], [65536], 64, 256, 7872, r, "c2 r=%d" % r)
 
 
+
+def test_select_c4_shape_heavy_tail(tb, orc):
+    # 256K context, radius 2, one percent of positions per head shifted up by
+    # 2.5 score standard deviations (the long-context workload's heavy tail)
+    rng = rng_for(65)
+    L = 262144
+    s = rng.standard_normal((1, 32, L)).astype(np.float32)
+    for h in range(32):
+        pos = rng.integers(64, L - 256, size=L // 100)
+        s[0, h, pos] += 2.5
+    assert_same_selection(orc, tb, s, [L], [L], 64, 256, 7872, 2, "c4 heavy tail")
+
+
+def test_select_c3_batch(tb, orc):
+    # the 32-layer workload's batch of 8 sequences: 256 segments in one call
+    rng = rng_for(66)
+    s = rng.standard_normal((8, 32, 65536)).astype(np.float32)
+    L = [65536, 65000, 64000, 50000, 65536, 30000, 65535, 40001]
+    assert_same_selection(orc, tb, s, L, L, 64, 256, 7872, 1, "c3 batch")
+
 def test_select_tie_heavy_and_large_candidate_groups(tb, orc):
     rng = rng_for(55)
     # integer scores: few distinct values, boundary bins hold thousands of tokens
@@ -205,11 +225,11 @@ def test_select_workspace_reuse(tb, orc):
         assert int(ws[: B * Hq * 4].count_nonzero()) == 0   # arrival counters back at zero
 
 
-def _sample_positions(e0, e1):
+def _sample_positions(e0, e1, Lmax):
     """Eligible positions whose pooled keys the band estimate samples: every
-    stride-th token from e0 + stride // 2, stride = ceil(|E| / 8192)."""
-    n = e1 - e0
-    stride = -(-n // 8192)
+    stride-th token from e0 + stride // 2, stride = ceil((Lmax - e0) / 8192)
+    (e0 = the sink size)."""
+    stride = max(1, -(-(Lmax - e0) // 8192))
     return np.arange(e0 + stride // 2, e1, stride), stride
 
 
@@ -256,7 +276,7 @@ def test_select_band_miss_takes_exact_path(tb, orc, r):
     rng = rng_for(58, r)
     B, Hq, L, S, W, K = 1, 3, 70000, 16, 64, 4000
     s = rng.standard_normal((B, Hq, L)).astype(np.float32)
-    pos, stride = _sample_positions(S, L - W)
+    pos, stride = _sample_positions(S, L - W, L)
     assert stride > 2 * r + 1
     s[0, 0, pos] += 100.0
     s[0, 1, _around(pos, r, S, L - W)] -= 100.0
@@ -269,7 +289,7 @@ def test_select_band_miss_with_ties(tb, orc):
     B, Hq, L, S, W, K = 1, 2, 70000, 8, 32, 2500
     for r in (0, 1, 2):
         s = integer_scores(rng, (B, Hq, L), -3, 4)
-        pos, _ = _sample_positions(S, L - W)
+        pos, _ = _sample_positions(S, L - W, L)
         s[0, 0, pos] = 9.0
         s[0, 1, _around(pos, r, S, L - W)] = -9.0
         assert_same_selection(orc, tb, s, [L], [L], S, W, K, r, "band miss ties r=%d" % r)
@@ -318,7 +338,7 @@ def test_select_dilate_band_miss(tb, orc):
     rng = rng_for(63)
     B, Hq, L, S, W, K = 1, 2, 70000, 16, 64, 3000
     s = rng.standard_normal((B, Hq, L)).astype(np.float32)
-    pos, _ = _sample_positions(S, L - W)
+    pos, _ = _sample_positions(S, L - W, L)
     s[0, 0, pos] += 100.0
     s[0, 1, pos] -= 100.0
     assert_same_selection(orc, tb, s, [L], [L], S, W, K, 2, "dilate band miss", dilate=True)
