@@ -475,6 +475,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also time each stage")
+    ap.add_argument("--core-only", action="store_true",
+                    help="time the decode step only (no whole-context projection or dilation-mode "
+                         "extras), e.g. under a profiler")
     ap.add_argument("--config", type=int, default=2,
                     help="2: the single-layer decode step (default); 3, 4, 5: the multi-layer "
                          "prediction-interval workloads")
@@ -545,18 +548,20 @@ def main():
     # whole-context key projection (the prefill step before the decode path),
     # timed over the rotated replicas
     pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(3 * R)]
+           for _ in range(0 if args.core_only else 3 * R)]
     for i, (e0, e1) in enumerate(pev):
         r_ = reps[i % R]
         e0.record()
         tb.tb_project_keys(r_["kc"], r_["wk"], r_["kp"], zeros, L - 1)
         e1.record()
     torch.cuda.synchronize()
-    proj_us = float(np.mean([a.elapsed_time(b) for a, b in pev[R:]])) * 1e3
-    proj_bytes = B * cfg.Hkv * (L - 1) * (cfg.D * 2 + cfg.dp * 2) + cfg.Hkv * cfg.dp * cfg.D * 2
-    prefill = {"tokens": (L - 1) * B, "kv_heads": cfg.Hkv, "us": round(proj_us, 2),
-               "bytes": proj_bytes, "gbps": proj_bytes / proj_us / 1e3,
-               "frac": proj_bytes / proj_us / 1e3 / PEAK_HBM_GBS}
+    prefill = None
+    if pev:
+        proj_us = float(np.mean([a.elapsed_time(b) for a, b in pev[R:]])) * 1e3
+        proj_bytes = B * cfg.Hkv * (L - 1) * (cfg.D * 2 + cfg.dp * 2) + cfg.Hkv * cfg.dp * cfg.D * 2
+        prefill = {"tokens": (L - 1) * B, "kv_heads": cfg.Hkv, "us": round(proj_us, 2),
+                   "bytes": proj_bytes, "gbps": proj_bytes / proj_us / 1e3,
+                   "frac": proj_bytes / proj_us / 1e3 / PEAK_HBM_GBS}
 
     ctx = torch.full((B,), L, dtype=torch.int32, device="cuda")
     pos_new = torch.full((B,), L - 1, dtype=torch.int32, device="cuda")
@@ -696,55 +701,57 @@ def main():
             torch.cuda.synchronize()
             stages[n] = round(e0.elapsed_time(e1) * 1e3 / (n_rep * R), 2)
 
-    # the other reading of neighbour fetching (neighbours beyond the budget),
-    # on the same scores: its list sizes, bytes and times beside the fill mode
-    cap_d = min(L, cfg.S + cfg.W + (2 * cfg.r + 1) * cfg.K)
-    idx_d = torch.zeros((B, cfg.Hq, cap_d), dtype=torch.int32, device="cuda")
-    cnt_d = torch.zeros((B, cfg.Hq), dtype=torch.int32, device="cuda")
-    out_d = torch.zeros((B, cfg.Hq, cfg.D), device="cuda")
-    ws_ad = tb.new_workspace(tb.tb_attn_workspace_bytes(B, cfg.Hq, cap_d, 0, cfg.D))
-    tb.tb_select(scores, ctx, ctx, cfg.S, cfg.W, cfg.K, cfg.r, idx_d, cnt_d, ws_s,
-                 mode=tb.TB_NF_DILATE)
-    torch.cuda.synchronize()
-    dcalls = []
-    for r_ in reps:
-        dcalls.append([
-            (L_.tb_select, (P(scores), P(ctx), P(ctx), B, cfg.Hq, L, cfg.S, cfg.W, cfg.K, cfg.r,
-                            tb.TB_NF_DILATE, P(idx_d), P(cnt_d), cap_d, P(ws_s), nb(ws_s), sp)),
-            (L_.tb_sparse_decode_attn, (P(r_["q"]), P(r_["kc"]), P(r_["vc"]), P(idx_d), P(cnt_d),
-                                        cap_d, None, 0, B, cfg.Hq, cfg.Hkv, L, cfg.D,
-                                        ctypes.c_float(1.0 / np.sqrt(cfg.D)), P(out_d), P(ws_ad),
-                                        nb(ws_ad), sp)),
-        ])
-    dil_us = []
-    for j in range(2):
-        def one_d(i, j=j):
-            fn, a = dcalls[i % R][j]
-            if fn(*a):
-                raise RuntimeError(L_.tb_last_error_detail().decode())
-        gd = capture(one_d, R)
-        gd.replay()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dilate = None
+    if not args.core_only:
+        # the other reading of neighbour fetching (neighbours beyond the budget),
+        # on the same scores: its list sizes, bytes and times beside the fill mode
+        cap_d = min(L, cfg.S + cfg.W + (2 * cfg.r + 1) * cfg.K)
+        idx_d = torch.zeros((B, cfg.Hq, cap_d), dtype=torch.int32, device="cuda")
+        cnt_d = torch.zeros((B, cfg.Hq), dtype=torch.int32, device="cuda")
+        out_d = torch.zeros((B, cfg.Hq, cfg.D), device="cuda")
+        ws_ad = tb.new_workspace(tb.tb_attn_workspace_bytes(B, cfg.Hq, cap_d, 0, cfg.D))
+        tb.tb_select(scores, ctx, ctx, cfg.S, cfg.W, cfg.K, cfg.r, idx_d, cnt_d, ws_s,
+                     mode=tb.TB_NF_DILATE)
         torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(20):
+        dcalls = []
+        for r_ in reps:
+            dcalls.append([
+                (L_.tb_select, (P(scores), P(ctx), P(ctx), B, cfg.Hq, L, cfg.S, cfg.W, cfg.K, cfg.r,
+                                tb.TB_NF_DILATE, P(idx_d), P(cnt_d), cap_d, P(ws_s), nb(ws_s), sp)),
+                (L_.tb_sparse_decode_attn, (P(r_["q"]), P(r_["kc"]), P(r_["vc"]), P(idx_d), P(cnt_d),
+                                            cap_d, None, 0, B, cfg.Hq, cfg.Hkv, L, cfg.D,
+                                            ctypes.c_float(1.0 / np.sqrt(cfg.D)), P(out_d), P(ws_ad),
+                                            nb(ws_ad), sp)),
+            ])
+        dil_us = []
+        for j in range(2):
+            def one_d(i, j=j):
+                fn, a = dcalls[i % R][j]
+                if fn(*a):
+                    raise RuntimeError(L_.tb_last_error_detail().decode())
+            gd = capture(one_d, R)
             gd.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dil_us.append(e0.elapsed_time(e1) * 1e3 / (20 * R))
-    di, dc = idx_d.cpu().numpy(), cnt_d.cpu().numpy()
-    d_union = 0
-    for kvh in range(cfg.Hkv):
-        su = set()
-        for h in range(kvh * cfg.g, (kvh + 1) * cfg.g):
-            su.update(di[0, h, :dc[0, h]].tolist())
-        d_union += len(su)
-    d_bytes = d_union * row_bytes + cfg.Hq * cfg.D * (2 + 4) + dc.size * 4 + int(dc.sum()) * 4
-    dilate = {"attended_per_head_mean": float(dc.mean()), "union_rows": d_union,
-              "per_head_rows": int(dc.sum()), "attn_bytes": d_bytes,
-              "select_us": round(dil_us[0], 2), "attention_us": round(dil_us[1], 2),
-              "attention_gbps": d_bytes / dil_us[1] / 1e3,
-              "fill_attended_per_head_mean": float(gc.mean()), "fill_attn_bytes": attn_bytes}
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(20):
+                gd.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            dil_us.append(e0.elapsed_time(e1) * 1e3 / (20 * R))
+        di, dc = idx_d.cpu().numpy(), cnt_d.cpu().numpy()
+        d_union = 0
+        for kvh in range(cfg.Hkv):
+            su = set()
+            for h in range(kvh * cfg.g, (kvh + 1) * cfg.g):
+                su.update(di[0, h, :dc[0, h]].tolist())
+            d_union += len(su)
+        d_bytes = d_union * row_bytes + cfg.Hq * cfg.D * (2 + 4) + dc.size * 4 + int(dc.sum()) * 4
+        dilate = {"attended_per_head_mean": float(dc.mean()), "union_rows": d_union,
+                  "per_head_rows": int(dc.sum()), "attn_bytes": d_bytes,
+                  "select_us": round(dil_us[0], 2), "attention_us": round(dil_us[1], 2),
+                  "attention_gbps": d_bytes / dil_us[1] / 1e3,
+                  "fill_attended_per_head_mean": float(gc.mean()), "fill_attn_bytes": attn_bytes}
 
     traffic = traffic_record()
     res = {
@@ -774,8 +781,8 @@ def main():
         "step_gbps": step_bytes / step_s / 1e9,
         "step_compulsory_bytes": step_bytes,
         "attended_rows": {"union": union_rows, "per_head": per_head_rows},
-        "dilate_mode": dilate,
-        "prefill_projection": prefill,
+        **({"dilate_mode": dilate} if dilate else {}),
+        **({"prefill_projection": prefill} if prefill else {}),
     }
     if stages:
         res["stages_us"] = stages
