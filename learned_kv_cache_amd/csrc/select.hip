@@ -790,6 +790,15 @@ __global__ __launch_bounds__(64) void compact_kernel(
     const uint32_t base = coff[(size_t)seg * nchunks + c];
     const uint32_t nraw = ccount[(size_t)seg * nchunks + c];
     const uint64_t thr_raw = thr_in[seg];
+    // so are the chunk's first 128 candidate slots (used if that many are filled)
+    constexpr int PF = 2;
+    const uint64_t *cl = cand + (size_t)seg * Lmax + (size_t)c * CHUNK;
+    uint64_t pk[PF];
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        const int i = lane + 64 * k;
+        pk[k] = c * CHUNK + i < Lmax ? cl[i] : 0ull;
+    }
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
     const int L = g.L;
     if (g.bad || c * CHUNK >= L) return;
@@ -809,8 +818,14 @@ __global__ __launch_bounds__(64) void compact_kernel(
     bits &= bits_below(L - t0);
     s_word[lane] = bits;
     __syncthreads();
-    const uint64_t *cl = cand + (size_t)seg * Lmax + (size_t)c * CHUNK;
-    for (uint32_t i = lane; i < n; i += 64) {
+#pragma unroll
+    for (int k = 0; k < PF; ++k) {
+        if ((uint32_t)(lane + 64 * k) < n && pk[k] >= thr) {
+            const int t = key_token(pk[k]) - c * CHUNK;
+            atomicOr(&s_word[t >> 5], 1u << (t & 31));
+        }
+    }
+    for (uint32_t i = lane + 64 * PF; i < n; i += 64) {
         const uint64_t key = cl[i];
         if (key >= thr) {
             const int t = key_token(key) - c * CHUNK;
