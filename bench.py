@@ -656,6 +656,20 @@ def main():
         g_rem.replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # per-step time distribution: one more pass of replays, each bracketed by events
+    rev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(min(full, 100))]
+    for a, b in rev:
+        a.record(stream)
+        g_all.replay()
+        b.record(stream)
+    torch.cuda.synchronize()
+    step_pct = None
+    if rev:
+        per = np.array([a.elapsed_time(b) * 1e3 / R for a, b in rev])
+        step_pct = {"p10": round(float(np.percentile(per, 10)), 2),
+                    "p50": round(float(np.percentile(per, 50)), 2),
+                    "p90": round(float(np.percentile(per, 90)), 2), "replays": len(rev)}
 
     # algorithmic bytes of one attention launch: each distinct (kv head, token)
     # row of the g heads' attended sets, K and V, bf16 -- counted from idx
@@ -778,6 +792,7 @@ def main():
                      "kernel": "sparse decode attention gather (attn_kernel<128>)",
                      "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6},
         "eager_steps_per_s": K / eager_elapsed,
+        "step_us": step_pct,
         "step_gbps": step_bytes / step_s / 1e9,
         "step_compulsory_bytes": step_bytes,
         "attended_rows": {"union": union_rows, "per_head": per_head_rows},
