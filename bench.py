@@ -671,6 +671,26 @@ def main():
                     "p50": round(float(np.percentile(per, 50)), 2),
                     "p90": round(float(np.percentile(per, 90)), 2), "replays": len(rev)}
 
+    # the dominant kernel alone: a graph of one attention launch per replica,
+    # replayed back to back between two events on its stream, so the average
+    # is the launch's own duration (no host gaps between launches)
+    def attn_only(i):
+        fn, a = calls[i % R][3]
+        if fn(*a):
+            raise RuntimeError(L_.tb_last_error_detail().decode())
+    g_attn = capture(attn_only, R)
+    g_attn.replay()
+    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n_attn = max(1, min(200, K // R))
+    torch.cuda.synchronize()
+    ea.record(stream)
+    for _ in range(n_attn):
+        g_attn.replay()
+    eb.record(stream)
+    torch.cuda.synchronize()
+    attn_eager_avg_s = attn_avg_s
+    attn_avg_s = ea.elapsed_time(eb) / 1e3 / (n_attn * R)
+
     # algorithmic bytes of one attention launch: each distinct (kv head, token)
     # row of the g heads' attended sets, K and V, bf16 -- counted from idx
     gi = idx.cpu().numpy()
@@ -790,7 +810,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "sparse decode attention gather (attn_kernel<128>)",
-                     "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6},
+                     "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6,
+                     "launches_timed": n_attn * R,
+                     "avg_launch_us_eager_events": attn_eager_avg_s * 1e6},
         "eager_steps_per_s": K / eager_elapsed,
         "step_us": step_pct,
         "step_gbps": step_bytes / step_s / 1e9,
