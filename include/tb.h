@@ -5,12 +5,16 @@
  * projected into the same space; a fixed budget of the best-scoring tokens,
  * widened by neighbour fetching, is kept on top of an always-kept sink and a
  * local window; decode attention then reads only those tokens' K/V rows.
+ * Around that path: the decode-step K/V append with batched key projection,
+ * CPU-offload decoding (host-resident cache, HBM buffers) and the predictor's
+ * distillation loss.
  *
  * Method source: "TokenButler" technical summary, sections "Core
  * architecture" (query prediction, key-cache projection, scoring),
  * "Inference strategy" (sink / local window / important buffers; batched key
- * projection; prediction interval; neighbour fetching) and "Significance"
- * (the full cache is kept, only the most relevant tokens are read).
+ * projection; prediction interval; neighbour fetching), "Training"
+ * (distillation loss) and "Significance" (the full cache is kept, only the
+ * most relevant tokens are read).
  *
  * Conventions for every call
  *  - Pointers are DEVICE pointers unless stated, owned by the caller, to

@@ -184,7 +184,7 @@ def test_select_c3_batch(tb, orc):
 
 def test_select_tie_heavy_and_large_candidate_groups(tb, orc):
     rng = rng_for(55)
-    # integer scores: few distinct values, boundary bins hold thousands of tokens
+    # integer scores: few distinct values, the band around the budget's key holds thousands of ties
     s = integer_scores(rng, (2, 4, 20000), -3, 4)
     s[:, :, ::7] = -0.0
     assert_same_selection(orc, tb, s, [20000, 15001], [20000, 14900], 16, 64, 3000, 1, "ints r1")
