@@ -2,15 +2,15 @@
 // cache ("TokenButler" summary, "Significance": keep the whole cache, read
 // only the most relevant tokens).
 //
-// Split-K gather: a workgroup owns CH consecutive entries of one query head's
-// ascending index list, staged in LDS. D/8 lanes share one K/V row (16 bytes
-// = 8 channels per lane), so a wave gathers 64/(D/8) rows per 16-byte load;
-// each lane group requests all of its CH/16 (D = 128) K rows at once, then
-// all of its V rows into the same registers, so a workgroup waits on memory
-// twice and stays small enough for the whole grid to be resident. Logits are reduced with
-// DPP, the softmax is fp32 base-2 in registers, and the workgroup writes one partial
-// (max, sum, o[D]). The last workgroup of a head to arrive merges the
-// partials by log-sum-exp into the fp32 output.
+// Split-K gather: a 512-thread workgroup owns CH consecutive entries of one
+// query head's ascending index list, staged in LDS. D/8 lanes share one K/V
+// row (16 bytes = 8 channels per lane), so a wave gathers 64/(D/8) rows per
+// 16-byte load; each lane group requests all of its K rows at once, then all
+// of its V rows once the logits are formed. Logits are reduced with DPP, the
+// softmax is fp32 base-2 in registers, the row groups' states are combined by
+// a lane butterfly and then across waves, and the workgroup writes one partial
+// (max, sum, o[D]). The last workgroup of a head to arrive merges the partials
+// by log-sum-exp into the fp32 output, with the same butterfly.
 //
 // Cross-workgroup handoff without device-scope fences (on this chip a fence at
 // agent scope writes back, and on acquire invalidates, the XCD's whole L2):
@@ -29,11 +29,30 @@
 namespace tb {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int CH = 256;  // index-list entries per workgroup
 // word 3 of a raw (untyped) buffer resource on gfx9-family parts
 constexpr int kRsrcWord3 = 0x00020000;
+
+// Log-sum-exp combine of the (max, sum, o[8]) states held by the lanes of a
+// wave that own the same 8 channels (lanes equal modulo LPR): a butterfly over
+// the lane bits at and above LPR, after which every lane holds the combined
+// state of its channels.
+template <int LPR>
+__device__ inline void combine_lanes(float &m, float &l, float (&o)[8]) {
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+        const float m2 = __shfl_xor(m, off);
+        const float l2 = __shfl_xor(l, off);
+        const float M = fmaxf(m, m2);
+        const float w1 = exp2f(m - M), w2 = exp2f(m2 - M);
+        l = l * w1 + l2 * w2;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = o[c] * w1 + __shfl_xor(o[c], off) * w2;
+        m = M;
+    }
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void attn_kernel(
@@ -49,10 +68,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     constexpr int STRIDE = NG;          // rows per workgroup pass
     constexpr int RPG = CH / NG;        // rows per row group
 
-    __shared__ float sm_o[NG][D];
-    __shared__ float sm_m[NG], sm_l[NG];
+    __shared__ float sm_o[kWaves][D];
+    __shared__ float sm_m[kWaves], sm_l[kWaves];
     __shared__ int sm_tok[CH];
-    __shared__ float sm_p[32 * (D + 2)];
     __shared__ int sm_last;
 
     const int nb = gridDim.x;
@@ -124,7 +142,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
 
     // all K rows of this row group are requested at once; their registers are
     // then reused for the V rows, which are requested as soon as the logits
-    // are formed
+    // are formed (a 512-thread workgroup then needs few enough registers that
+    // four fit on a CU)
     uint4 kv[RPG];
 #pragma unroll
     for (int u = 0; u < RPG; ++u) {
@@ -175,25 +194,29 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
         }
     }
 
-    // merge the row groups of this workgroup into one partial (wave 0 only)
+    // merge the row groups: within each wave by butterfly, then the waves'
+    // states through LDS (wave 0)
+    combine_lanes<LPR>(m, l, acc);
+    if (rg == 0) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) sm_o[grp][cl * 8 + c] = acc[c];
-    if (cl == 0) {
-        sm_m[grp] = m;
-        sm_l[grp] = l;
+        for (int c = 0; c < 8; ++c) sm_o[wave][cl * 8 + c] = acc[c];
+        if (cl == 0) {
+            sm_m[wave] = m;
+            sm_l[wave] = l;
+        }
     }
     __syncthreads();
     float *pp = part + ((size_t)bh * nsplit + split) * (D + 2);
     if (wave == 0) {
         float M = -1e30f;
 #pragma unroll
-        for (int i = 0; i < NG; ++i) M = fmaxf(M, sm_m[i]);
+        for (int i = 0; i < kWaves; ++i) M = fmaxf(M, sm_m[i]);
         float Ls = 0.f;
         float O[D / 64];
 #pragma unroll
         for (int j = 0; j < D / 64; ++j) O[j] = 0.f;
 #pragma unroll
-        for (int i = 0; i < NG; ++i) {
+        for (int i = 0; i < kWaves; ++i) {
             const float w = exp2f(sm_m[i] - M);
             Ls += sm_l[i] * w;
 #pragma unroll
@@ -218,41 +241,54 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
     __syncthreads();
     if (!sm_last) return;
 
-    // last arrival: merge all partials of this head (32 at a time through LDS)
+    // last arrival: merge all partials of this head, kThreads / LPR at a time:
+    // each row group of lanes loads one partial's (max, sum, 8 channels), the
+    // waves combine theirs by butterfly, and threads c < D fold the waves'
+    // states into a running (max, sum, o[c]) through LDS
     constexpr int PW = D + 2;
-    constexpr int CS = 32;
-    constexpr int PER = (CS * PW + kThreads - 1) / kThreads;
+    constexpr int PPC = kThreads / LPR;
     const float *base = part + (size_t)bh * nsplit * PW;
     float M = -1e30f, den = 0.f, num = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += CS) {
-        const int ns = nsplit - s0 < CS ? nsplit - s0 : CS;
-        const float *src = base + (size_t)s0 * PW;
-        float v[PER];
+    for (int s0 = 0; s0 < nsplit; s0 += PPC) {
+        const int sidx = s0 + wave * RPW + rg;
+        const bool valid = sidx < nsplit;
+        const float *src = base + (size_t)(valid ? sidx : 0) * PW;
+        float pm = valid ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : -1e30f;
+        float pl = valid ? __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0.f;
+        float po[8];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int i = threadIdx.x + k * kThreads;
-            v[k] = i < ns * PW ? __hip_atomic_load(src + i, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)
-                               : 0.f;
+        for (int c = 0; c < 8; ++c)
+            po[c] = valid ? __hip_atomic_load(src + 2 + cl * 8 + c, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT)
+                          : 0.f;
+        combine_lanes<LPR>(pm, pl, po);
+        __syncthreads();
+        if (rg == 0) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sm_o[wave][cl * 8 + c] = po[c];
+            if (cl == 0) {
+                sm_m[wave] = pm;
+                sm_l[wave] = pl;
+            }
         }
         __syncthreads();
+        if (threadIdx.x < D) {
+            float Mc = M;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int i = threadIdx.x + k * kThreads;
-            if (i < ns * PW) sm_p[i] = v[k];
+            for (int w = 0; w < kWaves; ++w) Mc = fmaxf(Mc, sm_m[w]);
+            const float r = exp2f(M - Mc);
+            den *= r;
+            num *= r;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float wt = exp2f(sm_m[w] - Mc);
+                den += sm_l[w] * wt;
+                num += sm_o[w][threadIdx.x] * wt;
+            }
+            M = Mc;
         }
-        __syncthreads();
-        float Mc = M;
-        for (int s = 0; s < ns; ++s) Mc = fmaxf(Mc, sm_p[s * PW]);
-        const float r = exp2f(M - Mc);
-        den *= r;
-        num *= r;
-        for (int s = 0; s < ns; ++s) {
-            const float w = exp2f(sm_p[s * PW] - Mc);
-            den += sm_p[s * PW + 1] * w;
-            if (threadIdx.x < D) num += sm_p[s * PW + 2 + threadIdx.x] * w;
-        }
-        M = Mc;
     }
     if (threadIdx.x < D) out[(size_t)bh * D + threadIdx.x] = den > 0.f ? num / den : 0.f;
     if (threadIdx.x == 0) __hip_atomic_store(ctr + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
