@@ -1,0 +1,152 @@
+"""GPU parity of one prediction interval at the full per-layer shapes of the
+multi-layer workloads (64K context at B 8; 256K context with r 2; the
+Qwen2.5-7B-shaped ragged batch of 4), in the launch sequence the interval
+benchmark times: predictor, score, selection with the window left out of the
+list (TB_SEL_OMIT_WINDOW), then I decode steps of tb_append_kv (which
+projects the pending keys once N_p have accumulated) and sparse attention
+with the sliding window. One consumer layer per workload, with planted
+high-affinity spans.
+
+Checked against the oracle on sampled (b, query head) slices, each computed
+on its own (projection of that KV head's whole context, predictor, score,
+selection): the attended list (equal, or differing only by tokens within the
+near-tie band of the K-th rank score), every step's attention output, the
+projections of the appended keys, the appended cache rows bit for bit and
+the lengths."""
+import numpy as np
+import pytest
+import torch
+
+from synthetic import CONFIGS, bits_to_f32_f16, normal_bf16, rng_for
+from synthetic.workload import make_layer
+from gpu_util import (assert_attn_close, assert_rel, bits, check_selection_band, dev, dev32, host,
+                      say)
+from workloads import oracle_direction
+
+pytestmark = pytest.mark.gpu
+
+# (b, query head) slices checked per workload
+SAMPLES = {
+    3: [(0, 0), (1, 5), (2, 10), (3, 15), (4, 20), (5, 25), (6, 30), (7, 31)],
+    4: [(0, 0), (0, 5), (0, 10), (0, 15), (0, 20), (0, 26), (0, 30), (0, 31)],
+    5: [(0, 0), (1, 6), (2, 13), (3, 20), (0, 27), (1, 14), (2, 7), (3, 1)],
+}
+T_NEW = 40   # tensor-kind tag of the appended rows
+
+
+@pytest.fixture(scope="module")
+def tb():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import learned_kv_cache_amd as tb
+    tb.lib()
+    return tb
+
+
+@pytest.mark.parametrize("cid", [3, 4, 5])
+def test_interval_full_shape(tb, orc, cid):
+    cfg = CONFIGS[cid]
+    B, Hq, Hkv, D, dp, g = cfg.B, cfg.Hq, cfg.Hkv, cfg.D, cfg.dp, cfg.g
+    S, W, K, r, I, Np = cfg.S, cfg.W, cfg.K, cfg.r, cfg.interval, cfg.n_proj
+    Lmax = cfg.L + I
+    say("interval full shape", cfg.name, "generating")
+    inp = make_layer(cfg, seed=0, Lmax=Lmax, direction_fn=oracle_direction(orc, cfg), n_spans=64,
+                     span_len=8, alpha=3.0)
+    L0 = inp["ctx_len"].astype(np.int32)
+    assert L0.max() + I <= Lmax
+    kn = normal_bf16(rng_for(cid * 1000, T_NEW, 0), (I, B, Hkv, D))
+    vn = normal_bf16(rng_for(cid * 1000, T_NEW, 1), (I, B, Hkv, D))
+
+    say("interval full shape", cfg.name, "gpu", L0.tolist())
+    kc, vc = dev(inp["kc"], torch.bfloat16), dev(inp["vc"], torch.bfloat16)
+    wk, q = dev(inp["wk"], torch.bfloat16), dev(inp["q"], torch.bfloat16)
+    kp = torch.zeros((B, Hkv, Lmax, dp), dtype=torch.float16, device="cuda")
+    tb.tb_project_keys(kc, wk, kp, dev32(np.zeros(B, np.int32)), int(L0.max()))
+    qhat = torch.empty((B, cfg.n_out), device="cuda")
+    tb.tb_predict_queries(dev(inp["x"], torch.bfloat16), dev(inp["w1"], torch.bfloat16),
+                          dev(inp["w2"], torch.bfloat16), qhat,
+                          tb.new_workspace(tb.tb_predict_workspace_bytes(B, cfg.E, cfg.Eh,
+                                                                         cfg.n_out)))
+    ctx0 = dev32(L0)
+    scores = torch.empty((B, Hq, Lmax), device="cuda")
+    tb.tb_score(qhat, kp, ctx0, scores)
+    cap = S + K
+    idx = torch.zeros((B, Hq, cap), dtype=torch.int32, device="cuda")
+    cnt = torch.zeros((B, Hq), dtype=torch.int32, device="cuda")
+    tb.tb_select(scores, ctx0, ctx0, S, W, K, r, idx, cnt,
+                 tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax)),
+                 mode=tb.TB_NF_FILL | tb.TB_SEL_OMIT_WINDOW)
+    ctx, plen = dev32(L0), dev32(L0)
+    out = torch.zeros((B, Hq, D), device="cuda")
+    ws = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, W, D))
+    outs = []
+    for j in range(I):
+        tb.tb_append_kv(dev(kn[j], torch.bfloat16), dev(vn[j], torch.bfloat16), kc, vc, kp, wk,
+                        ctx, plen, Np)
+        tb.tb_sparse_decode_attn(q, kc, vc, idx, cnt, out, ws, ctx_len=ctx, window=W)
+        outs.append(host(out).copy())
+    torch.cuda.synchronize()
+    g_idx, g_cnt = host(idx), host(cnt)
+    assert host(ctx).tolist() == (L0 + I).tolist()
+    assert host(plen).tolist() == (L0 + I).tolist()
+    for b in range(B):
+        rows = bits(kc[b, :, int(L0[b]):int(L0[b]) + I])            # [Hkv, I, D]
+        assert np.array_equal(rows, kn[:, b].transpose(1, 0, 2)), ("appended K", b)
+        rows = bits(vc[b, :, int(L0[b]):int(L0[b]) + I])
+        assert np.array_equal(rows, vn[:, b].transpose(1, 0, 2)), ("appended V", b)
+
+    say("interval full shape", cfg.name, "oracle slices")
+    _, o_qhat = orc.predict_queries(inp["x"], inp["w1"], inp["w2"])
+    assert_rel(host(qhat), o_qhat, 2e-3, "qhat")
+    kp_cache = {}
+    for (b, h) in SAMPLES[cid]:
+        kvh, Lb = h // g, int(L0[b])
+        # this KV head's cache with the interval's rows appended
+        kcs = inp["kc"][b:b + 1, kvh:kvh + 1].copy()
+        vcs = inp["vc"][b:b + 1, kvh:kvh + 1].copy()
+        kcs[0, 0, Lb:Lb + I] = kn[:, b, kvh]
+        vcs[0, 0, Lb:Lb + I] = vn[:, b, kvh]
+        wks = inp["wk"][kvh:kvh + 1].copy()
+        if (b, kvh) not in kp_cache:
+            kps = np.zeros((1, 1, Lmax, dp), np.uint16)
+            orc.project_keys(kcs, wks, kps, np.zeros(1, np.int32), Lb)
+            kp_cache[(b, kvh)] = kps
+        kps = kp_cache[(b, kvh)]
+        Ls = np.array([Lb], np.int32)
+        s = orc.score(o_qhat[b:b + 1, h * dp:(h + 1) * dp], kps, Ls, 1)
+        imp = orc.important_only(s, Ls, Ls, S, W, K, r)
+        lst = sorted(set(range(min(S, Lb))) | set(imp[0][0].tolist()))
+        o_idx = np.zeros((1, 1, cap), np.int32)
+        o_idx[0, 0, :len(lst)] = lst
+        o_cnt = np.array([[len(lst)]], np.int32)
+        what = "%s b=%d h=%d" % (cfg.name, b, h)
+        check_selection_band(g_idx[b:b + 1, h:h + 1], g_cnt[b:b + 1, h:h + 1], o_idx, o_cnt, s, Ls,
+                             Ls, S, W, K, r, what=what, window_in_list=False)
+        same = np.array_equal(g_idx[b, h, :g_cnt[b, h]], o_idx[0, 0, :o_cnt[0, 0]])
+        qs = inp["q"][b:b + 1, h:h + 1].copy()
+        got_out = {j: outs[j][b:b + 1, h:h + 1] for j in range(I)}
+        steps = range(I) if same else [I - 1]
+        if not same:
+            # stage-isolated: the kernel attends over the oracle's list at the last step
+            say(what, "selection differs within the tie band; attention on the oracle list")
+            iso_idx = np.zeros((B, Hq, cap), np.int32)
+            iso_cnt = np.zeros((B, Hq), np.int32)
+            iso_idx[b, h] = o_idx[0, 0]
+            iso_cnt[b, h] = o_cnt[0, 0]
+            tb.tb_sparse_decode_attn(q, kc, vc, dev32(iso_idx), dev32(iso_cnt), out, ws,
+                                     ctx_len=dev32(L0 + I), window=W)
+            torch.cuda.synchronize()
+            got_out[I - 1] = host(out)[b:b + 1, h:h + 1].copy()
+        for j in steps:
+            sets = orc.interval_attended(imp, [Lb + 1], j, S, W)
+            att = np.array(sets[0][0], np.int32)[None, None]
+            ref = orc.sparse_attention(qs, kcs, vcs, att, np.array([[att.shape[-1]]], np.int32))
+            assert_attn_close(got_out[j], ref, "%s step %d" % (what, j))
+        # the appended keys projected by the append once N_p had accumulated
+        kpa = np.zeros((1, 1, Lmax, dp), np.uint16)
+        orc.project_keys(kcs, wks, kpa, np.array([Lb], np.int32), Np)
+        got = bits(kp[b, kvh, Lb:Lb + Np])
+        assert_rel(bits_to_f32_f16(got), bits_to_f32_f16(kpa[0, 0, Lb:Lb + Np]), 2e-3,
+                   "%s appended K'" % what)
+    del kc, vc, kp, scores
+    torch.cuda.empty_cache()
