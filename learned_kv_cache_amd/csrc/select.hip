@@ -667,10 +667,31 @@ __global__ __launch_bounds__(T3) void thr_kernel(
                 const uint64_t mask = shift >= 64 ? 0ull : (~0ull << shift);
                 thr = kth_largest(visit_cand, need1, ((uint64_t)thi << 32) & mask, mask, shift,
                                   (int)nc, s_k);
-                for (int i = tid; i < (int)nc; i += T3) {
-                    const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
-                    if (key >= thr)
-                        atomicAdd(&s_chosen[lds ? (int)s_cc[i] : chunk_of(s_off, nchunks, i)], 1u);
+                // chosen candidates per chunk: candidates are chunk-major, so
+                // a wave's lanes form runs of one chunk; each run's first lane
+                // adds the run's count
+                const int lane = tid & 63;
+                for (int i0 = 0; i0 < (int)nc; i0 += T3) {
+                    const int i = i0 + tid;
+                    int c = -1;
+                    bool ch = false;
+                    if (i < (int)nc) {
+                        const uint64_t key = lds ? s_cand[i] : cand_at(cl, s_off, nchunks, i);
+                        c = lds ? (int)s_cc[i] : chunk_of(s_off, nchunks, i);
+                        ch = key >= thr;
+                    }
+                    const int prev = __shfl_up(c, 1);
+                    const bool head = c >= 0 && (lane == 0 || prev != c);
+                    const uint64_t hm = __ballot(head);
+                    const uint64_t cm = __ballot(ch);
+                    if (head) {
+                        const uint64_t later = lane == 63 ? 0ull : (hm >> (lane + 1)) << (lane + 1);
+                        const int nxt = later ? __ffsll((long long)later) - 1 : 64;
+                        const uint64_t run = (nxt == 64 ? ~0ull : ((1ull << nxt) - 1ull)) &
+                                             (~0ull << lane);
+                        const int n = __popcll(cm & run);
+                        if (n) atomicAdd(&s_chosen[c], (uint32_t)n);
+                    }
                 }
             }
         } else {
