@@ -360,8 +360,12 @@ def test_select_dilate_omit_window(tb, orc):
 
 # ------------------------------------------------------------------ attention
 
+# the last two: more split partials per head than one merge pass takes (32
+# at D = 128, 64 at D = 64)
 @pytest.mark.parametrize("B,Hq,Hkv,L,D,cap", [(1, 8, 2, 300, 64, 52), (2, 32, 8, 5000, 128, 700),
-                                              (1, 28, 4, 3000, 128, 3000), (1, 4, 1, 600, 64, 513)])
+                                              (1, 28, 4, 3000, 128, 3000), (1, 4, 1, 600, 64, 513),
+                                              (1, 8, 2, 30000, 128, 20000),
+                                              (1, 4, 2, 40000, 64, 33000)])
 def test_attention_random_sets(tb, orc, B, Hq, Hkv, L, D, cap):
     say("attn", B, Hq, Hkv, L, D, cap)
     rng = rng_for(58, B, Hq, L, D, cap)
