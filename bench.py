@@ -104,7 +104,9 @@ def run_interval(cfg, args):
     which projects the pending keys once N_p of them have accumulated) and
     running sparse attention on every layer with the sliding window. Every
     interval starts from the same lengths (the appended rows are rewritten).
-    steps/s = I / interval time. The caches are generated on the GPU
+    steps/s = I / interval time, with each interval replayed from one HIP
+    graph of the whole interval (the same intervals issued call by call are
+    timed too: eager_steps_per_s). The caches are generated on the GPU
     (torch.randn, bf16): they are far larger than the 256 MiB MALL."""
     import torch
     import learned_kv_cache_amd as tb
@@ -206,14 +208,40 @@ def run_interval(cfg, args):
     mk = lambda: [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(I)] for _ in range(n_int)]
     evs, aevs = mk(), mk()
+    iev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_int)]
     log("timing %d intervals of %d steps" % (n_int, I))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(n_int):
+        iev[k][0].record(stream)
         interval(evs[k], aevs[k])
+        iev[k][1].record(stream)
+    torch.cuda.synchronize()
+    el_eager = time.perf_counter() - t0
+    eager_ms = [a.elapsed_time(b) / I for a, b in iev]
+    attn_us = float(np.mean([a.elapsed_time(b) for row in evs for a, b in row])) * 1e3 / nl
+    # the same intervals replayed from one HIP graph of a whole interval
+    log("capturing one interval in a graph")
+    g_int = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_int, stream=stream):
+        interval()
+    g_int.replay()
+    torch.cuda.synchronize()
+    log("timing %d graph-replayed intervals" % n_int)
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_int)]
+    t0 = time.perf_counter()
+    for a, b in gev:
+        a.record(stream)
+        g_int.replay()
+        b.record(stream)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
-    attn_us = float(np.mean([a.elapsed_time(b) for row in evs for a, b in row])) * 1e3 / nl
+    graph_ms = [a.elapsed_time(b) / I for a, b in gev]
+    pct = lambda v: {"p10": round(float(np.percentile(v, 10)), 4),
+                     "p50": round(float(np.percentile(v, 50)), 4),
+                     "p90": round(float(np.percentile(v, 90)), 4), "intervals": len(v)}
     app = np.array([[a.elapsed_time(b) * 1e3 / nl for a, b in row] for row in aevs])
     proj_step = Np - 1 if Np <= I else None   # the step whose appends project the batch
     append = {"us_per_layer_call": round(float(np.median(app)), 2),
@@ -249,6 +277,9 @@ def run_interval(cfg, args):
                      "kernel": "sparse decode attention gather (one layer, one step)",
                      "bytes_per_launch": attn_bytes, "avg_launch_us": attn_us},
         "append": append,
+        "eager_steps_per_s": n_int * I / el_eager,
+        "ms_per_step_graph": pct(graph_ms),
+        "ms_per_step_eager": pct(eager_ms),
     }
     print(json.dumps(res), flush=True)
 
@@ -481,7 +512,7 @@ def main():
     ap.add_argument("--config", type=int, default=2,
                     help="2: the single-layer decode step (default); 3, 4, 5: the multi-layer "
                          "prediction-interval workloads")
-    ap.add_argument("--intervals", type=int, default=3)
+    ap.add_argument("--intervals", type=int, default=5)
     ap.add_argument("--offload", action="store_true",
                     help="CPU-offload decoding on the 256K-context shape (with --config 4)")
     ap.add_argument("--offload-layers", type=int, default=4)
