@@ -507,8 +507,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", action="store_true", help="also time each stage")
     ap.add_argument("--core-only", action="store_true",
-                    help="time the decode step only (no whole-context projection or dilation-mode "
-                         "extras), e.g. under a profiler")
+                    help="time the decode step only (no whole-context projection), e.g. under a "
+                         "profiler")
+    ap.add_argument("--dilate", action="store_true",
+                    help="also time the dilation reading of neighbour fetching on the same scores "
+                         "(its attention launches are of the same kernel, so they are kept out of "
+                         "the default run and its kernel trace)")
     ap.add_argument("--config", type=int, default=2,
                     help="2: the single-layer decode step (default); 3, 4, 5: the multi-layer "
                          "prediction-interval workloads")
@@ -767,7 +771,7 @@ def main():
             stages[n] = round(e0.elapsed_time(e1) * 1e3 / (n_rep * R), 2)
 
     dilate = None
-    if not args.core_only:
+    if args.dilate:
         # the other reading of neighbour fetching (neighbours beyond the budget),
         # on the same scores: its list sizes, bytes and times beside the fill mode
         cap_d = min(L, cfg.S + cfg.W + (2 * cfg.r + 1) * cfg.K)
