@@ -2,7 +2,8 @@
 context, sink, window, budget, radius, mode) combinations for the selection
 in both neighbour modes, with and without the window, ragged lengths and
 projection lag, bit-exact against the oracle; and projection + scoring +
-attention on random small shapes within their tolerances."""
+attention (over a list, and over a list plus the implicit local window at a
+random length) on random small shapes within their tolerances."""
 import numpy as np
 import pytest
 import torch
@@ -96,7 +97,35 @@ def test_project_score_attention_random_shapes(tb, orc):
         tb.tb_sparse_decode_attn(dev(q, torch.bfloat16), dev(kc, torch.bfloat16), dev(vc, torch.bfloat16),
                                  dev32(lists), dev32(cnt), g_o,
                                  tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, 0, D)))
+        # the same lists plus the implicit local window: for each sequence a
+        # length Lb and the window [max(Lb - W, last entry + 1, 0), Lb)
+        W = int(rng.integers(1, 300))
+        Lw = rng.integers(1, L + 1, size=B).astype(np.int32)
+        wl = np.zeros((B, Hq, cap), np.int32)
+        wc = np.zeros((B, Hq), np.int32)
+        sets = []
+        for b in range(B):
+            for h in range(Hq):
+                n = min(int(cnt[b, h]), int(Lw[b]))
+                lst = np.sort(rng.choice(int(Lw[b]), size=n, replace=False)).astype(np.int32)
+                wl[b, h, :n] = lst
+                wc[b, h] = n
+                w0 = max(int(Lw[b]) - W, (int(lst[-1]) + 1) if n else 0, 0)
+                sets.append((b, h, np.concatenate([lst, np.arange(w0, int(Lw[b]), dtype=np.int32)])))
+        n_max = max(len(x) for _, _, x in sets)
+        ref_idx = np.zeros((B, Hq, max(1, n_max)), np.int32)
+        ref_cnt = np.zeros((B, Hq), np.int32)
+        for b, h, x in sets:
+            ref_idx[b, h, :len(x)] = x
+            ref_cnt[b, h] = len(x)
+        ref_w = orc.sparse_attention(q, kc, vc, ref_idx, ref_cnt)
+        g_w = torch.zeros((B, Hq, D), device="cuda")
+        tb.tb_sparse_decode_attn(dev(q, torch.bfloat16), dev(kc, torch.bfloat16), dev(vc, torch.bfloat16),
+                                 dev32(wl), dev32(wc), g_w,
+                                 tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, W, D)),
+                                 ctx_len=dev32(Lw), window=W)
         torch.cuda.synchronize()
+        assert_attn_close(host(g_w), ref_w, "attention with window %d" % trial)
         assert_rel(bits_to_f32_f16(bits(g_kp)), bits_to_f32_f16(kp), 2e-3, "kp %d" % trial)
         gs = host(g_s)
         for b in range(B):
