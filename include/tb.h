@@ -150,7 +150,10 @@ tb_status tb_append_kv(const void *k_new, const void *v_new, void *k_cache, void
  * [0, cap]), the row t = idx[b, h, i] (clamped to [0, Lmax)) of KV head
  * h / (Hq / Hkv) is copied from the host cache to slot s of head h's
  * buffers, s = slot0 + i, or s = slot0 + t mod wrap when wrap > 0 (the
- * circular window); rows whose slot would reach buf_rows are skipped.
+ * circular window); rows whose slot would reach buf_rows are skipped. With
+ * wrap > 0, entries whose t mod wrap coincide write the same slot and which
+ * of them lands is unspecified; a list of at most wrap consecutive
+ * positions (the window) has no such entries.
  * Limits: D in {64, 128}; Hq % Hkv == 0; 0 <= slot0 < buf_rows;
  * slot0 + wrap <= buf_rows. Returns TB_ERR_INVALID_ARGUMENT if the caches
  * are not pinned host memory.
