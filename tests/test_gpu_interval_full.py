@@ -5,7 +5,8 @@ benchmark times: predictor, score, selection with the window left out of the
 list (TB_SEL_OMIT_WINDOW), then I decode steps of tb_append_kv (which
 projects the pending keys once N_p have accumulated) and sparse attention
 with the sliding window. One consumer layer per workload, with planted
-high-affinity spans.
+high-affinity spans. The interval is issued call by call and then replayed
+from one HIP graph, which must reproduce it bitwise.
 
 Checked against the oracle on sampled (b, query head) slices, each computed
 on its own (projection of that KV head's whole context, predictor, score,
@@ -62,31 +63,56 @@ def test_interval_full_shape(tb, orc, cid):
     wk, q = dev(inp["wk"], torch.bfloat16), dev(inp["q"], torch.bfloat16)
     kp = torch.zeros((B, Hkv, Lmax, dp), dtype=torch.float16, device="cuda")
     tb.tb_project_keys(kc, wk, kp, dev32(np.zeros(B, np.int32)), int(L0.max()))
+    x, w1, w2 = (dev(inp[k], torch.bfloat16) for k in ("x", "w1", "w2"))
+    kn_d = [dev(kn[j], torch.bfloat16) for j in range(I)]
+    vn_d = [dev(vn[j], torch.bfloat16) for j in range(I)]
     qhat = torch.empty((B, cfg.n_out), device="cuda")
-    tb.tb_predict_queries(dev(inp["x"], torch.bfloat16), dev(inp["w1"], torch.bfloat16),
-                          dev(inp["w2"], torch.bfloat16), qhat,
-                          tb.new_workspace(tb.tb_predict_workspace_bytes(B, cfg.E, cfg.Eh,
-                                                                         cfg.n_out)))
+    ws_p = tb.new_workspace(tb.tb_predict_workspace_bytes(B, cfg.E, cfg.Eh, cfg.n_out))
     ctx0 = dev32(L0)
     scores = torch.empty((B, Hq, Lmax), device="cuda")
-    tb.tb_score(qhat, kp, ctx0, scores)
     cap = S + K
     idx = torch.zeros((B, Hq, cap), dtype=torch.int32, device="cuda")
     cnt = torch.zeros((B, Hq), dtype=torch.int32, device="cuda")
-    tb.tb_select(scores, ctx0, ctx0, S, W, K, r, idx, cnt,
-                 tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax)),
-                 mode=tb.TB_NF_FILL | tb.TB_SEL_OMIT_WINDOW)
+    ws_s = tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax))
     ctx, plen = dev32(L0), dev32(L0)
     out = torch.zeros((B, Hq, D), device="cuda")
     ws = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, W, D))
-    outs = []
-    for j in range(I):
-        tb.tb_append_kv(dev(kn[j], torch.bfloat16), dev(vn[j], torch.bfloat16), kc, vc, kp, wk,
-                        ctx, plen, Np)
-        tb.tb_sparse_decode_attn(q, kc, vc, idx, cnt, out, ws, ctx_len=ctx, window=W)
-        outs.append(host(out).copy())
+    outs_d = torch.empty((I, B, Hq, D), device="cuda")
+
+    def interval():
+        # the interval as the benchmark issues it: predictor, score, selection
+        # without the window, then I steps of append + windowed attention
+        ctx.copy_(ctx0)
+        plen.copy_(ctx0)
+        tb.tb_predict_queries(x, w1, w2, qhat, ws_p)
+        tb.tb_score(qhat, kp, ctx0, scores)
+        tb.tb_select(scores, ctx0, ctx0, S, W, K, r, idx, cnt, ws_s,
+                     mode=tb.TB_NF_FILL | tb.TB_SEL_OMIT_WINDOW)
+        for j in range(I):
+            tb.tb_append_kv(kn_d[j], vn_d[j], kc, vc, kp, wk, ctx, plen, Np)
+            tb.tb_sparse_decode_attn(q, kc, vc, idx, cnt, out, ws, ctx_len=ctx, window=W)
+            outs_d[j].copy_(out)
+
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        interval()
+        torch.cuda.synchronize()
+        outs = [host(outs_d[j]).copy() for j in range(I)]
+        g_idx, g_cnt, g_kp = host(idx), host(cnt), bits(kp)
+        # the same interval replayed from one HIP graph equals the eager run
+        # bitwise (the appends rewrite the same rows)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=st):
+            interval()
+        for rep in range(2):
+            outs_d.fill_(float("nan"))
+            idx.fill_(-7)
+            graph.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(host(idx), g_idx) and np.array_equal(host(cnt), g_cnt)
+            assert np.array_equal(host(outs_d), np.stack(outs)), ("graph replay", rep)
+            assert np.array_equal(bits(kp), g_kp)
     torch.cuda.synchronize()
-    g_idx, g_cnt = host(idx), host(cnt)
     assert host(ctx).tolist() == (L0 + I).tolist()
     assert host(plen).tolist() == (L0 + I).tolist()
     for b in range(B):
@@ -148,5 +174,5 @@ def test_interval_full_shape(tb, orc, cid):
         got = bits(kp[b, kvh, Lb:Lb + Np])
         assert_rel(bits_to_f32_f16(got), bits_to_f32_f16(kpa[0, 0, Lb:Lb + Np]), 2e-3,
                    "%s appended K'" % what)
-    del kc, vc, kp, scores
+    del kc, vc, kp, scores, graph
     torch.cuda.empty_cache()
