@@ -143,3 +143,19 @@ def test_interval_dense_budget_drops_only_what_left_the_window(orc):
         ref = torch.nn.functional.scaled_dot_product_attention(
             qq, kk, vv, attn_mask=torch.from_numpy(mask)[:, :, None, :])[:, :, 0].numpy()
         np.testing.assert_allclose(out, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_interval_of_one_step_equals_per_step_selection(orc):
+    # I = 1: the interval's only step attends exactly to the per-step
+    # selection (sink U window U important at the same length)
+    rng = np.random.default_rng(10)
+    B, Hq, L, S, W, K = 2, 3, 700, 6, 40, 55
+    s = rng.standard_normal((B, Hq, L)).astype(np.float32)
+    Lb = np.array([700, 512], np.int32)
+    for r in (0, 1, 3):
+        imp = orc.important_only(s, Lb, Lb, S, W, K, r)
+        idx, cnt = orc.select(s, Lb, Lb, S, W, K, r)
+        sets = orc.interval_attended(imp, Lb, 0, S, W)
+        for b in range(B):
+            for h in range(Hq):
+                assert np.array_equal(sets[b][h], idx[b, h, :cnt[b, h]]), (r, b, h)
