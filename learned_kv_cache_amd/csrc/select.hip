@@ -352,18 +352,50 @@ __global__ __launch_bounds__(T3) void bounds_kernel(const float *__restrict__ sc
     }
 }
 
+// Pooled key of eligible token t with the radius fixed at compile time: the
+// 2R + 1 staged keys are read together (slots outside E hold 0, below the key
+// of every finite score), and the first maximum in position order is the
+// centre -- the same key as pooled_key.
+template <int R>
+__device__ __forceinline__ uint64_t pooled_key_r(const uint32_t *sk, int lo, int t) {
+    uint32_t k[2 * R + 1];
+#pragma unroll
+    for (int u = 0; u <= 2 * R; ++u) k[u] = sk[t - R + u - lo];
+    uint32_t best = 0u;
+    int c = t;
+#pragma unroll
+    for (int u = 0; u <= 2 * R; ++u) {
+        if (k[u] > best) {
+            best = k[u];
+            c = t - R + u;
+        }
+    }
+    const int d = t < c ? c - t : t - c;
+    const uint32_t low = ((uint32_t)(0xffffff - c) << 8) | ((uint32_t)(0x7f - d) << 1) |
+                         (uint32_t)(t <= c ? 1 : 0);
+    return ((uint64_t)best << 32) | low;
+}
+
+// R >= 0: the radius is R (pooled keys read their neighbours together);
+// R < 0: any radius, neighbours read one by one. Each wave handles CHUNK /
+// waves tokens and keeps its candidates in its own LDS region, so no slot is
+// claimed with an atomic; the regions are written out back to back.
+template <int R>
 __global__ __launch_bounds__(T1) void classify_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx,
     const int32_t *__restrict__ plen, int Hq, int Lmax, int S, int W, int K, int r,
     const uint32_t *__restrict__ info, uint32_t *__restrict__ ccount,
     uint32_t *__restrict__ acount, int nchunks, uint64_t *__restrict__ cand,
     uint32_t *__restrict__ bitmap, int nwords) {
+    constexpr int NWV = T1 / 64;          // waves
+    constexpr int WREG = CHUNK / NWV;     // tokens (and candidate slots) per wave
     __shared__ uint32_t sk[CHUNK + 2 * MAXR];
     __shared__ uint64_t s_cand[CHUNK];
-    __shared__ uint32_t s_nc, s_na;
+    __shared__ uint32_t s_wc[NWV], s_wa[NWV];
     const int seg = blockIdx.y, b = seg / Hq;
     const int c0 = blockIdx.x * CHUNK;
-    const int lo = c0 - r;   // LDS slot i holds position lo + i
+    const int rr = R >= 0 ? R : r;
+    const int lo = c0 - rr;   // LDS slot i holds position lo + i
     // the chunk's scores (with halo) and the band are loaded before the
     // lengths are known; positions outside E are masked when staged
     constexpr int PER = (CHUNK + 2 * MAXR + T1 - 1) / T1;
@@ -372,7 +404,7 @@ __global__ __launch_bounds__(T1) void classify_kernel(
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         const int t = lo + (int)threadIdx.x + k * T1;
-        v[k] = (t >= 0 && t < Lmax && t < c0 + CHUNK + r) ? sc[t] : 0.f;
+        v[k] = (t >= 0 && t < Lmax && t < c0 + CHUNK + rr) ? sc[t] : 0.f;
     }
     const uint32_t tlo = info[2 * seg], thi = info[2 * seg + 1];
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
@@ -384,60 +416,79 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     const int a = c0 > g.e0 ? c0 : g.e0;
     const int z = c0 + CHUNK < g.e1 ? c0 + CHUNK : g.e1;
     const bool touch = partial && a < z;
-    if (threadIdx.x == 0) {
-        s_nc = 0;
-        s_na = 0;
-    }
     if (touch) {
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int i = (int)threadIdx.x + k * T1;
             const int t = lo + i;
-            if (t < c0 + CHUNK + r) sk[i] = (t >= g.e0 && t < g.e1) ? order_key(v[k]) : 0u;
+            if (t < c0 + CHUNK + rr) sk[i] = (t >= g.e0 && t < g.e1) ? order_key(v[k]) : 0u;
         }
     }
     __syncthreads();
-    // every word of this chunk is written: 64 tokens per wave per step
-    for (int base = c0 + wave * 64; base < c0 + CHUNK; base += T1) {
-        if (base >= nwords * 32) break;
-        const int t = base + lane;
+    // every word of this chunk is written: 64 tokens per wave per step. The
+    // keys of all NIT steps are formed first (their LDS reads issued
+    // together), then each step's ballots and stores
+    constexpr int NIT = CHUNK / T1;
+    uint64_t *wcand = s_cand + wave * WREG;
+    uint32_t nc_w = 0, na_w = 0;   // this wave's candidates and above-band tokens
+    uint64_t keys[NIT];
+    bool sels[NIT], iscs[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int t = c0 + wave * 64 + it * T1 + lane;
         bool sel = false, isc = false;
         uint64_t key = 0;
         if (t >= g.e0 && t < g.e1 && !g.bad) {
             if (all) {
                 sel = true;
             } else if (touch) {
-                key = pooled_key(sk, lo, t, g.e0, g.e1, r);
+                if constexpr (R >= 0) key = pooled_key_r<R>(sk, lo, t);
+                else key = pooled_key(sk, lo, t, g.e0, g.e1, r);
                 const uint32_t k32 = (uint32_t)(key >> 32);
                 sel = k32 > thi;
                 isc = !sel && k32 >= tlo;
             }
         }
-        const uint64_t m = __ballot(sel);
+        keys[it] = key;
+        sels[it] = sel;
+        iscs[it] = isc;
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int base = c0 + wave * 64 + it * T1;
+        if (base >= nwords * 32) break;
+        const uint64_t m = __ballot(sels[it]);
         if (lane == 0) {
             const int w = base >> 5;
             bm[w] = (uint32_t)m;
             if (w + 1 < nwords) bm[w + 1] = (uint32_t)(m >> 32);
-            if (m) atomicAdd(&s_na, (uint32_t)__popcll(m));
         }
-        const uint64_t cm = __ballot(isc);
-        if (cm) {
-            uint32_t off = 0;
-            if (lane == 0) off = atomicAdd(&s_nc, (uint32_t)__popcll(cm));
-            off = __shfl(off, 0);
-            if (isc) s_cand[off + __popcll(cm & ((1ull << lane) - 1ull))] = key;
-        }
+        na_w += (uint32_t)__popcll(m);
+        const uint64_t cm = __ballot(iscs[it]);
+        if (iscs[it]) wcand[nc_w + __popcll(cm & ((1ull << lane) - 1ull))] = keys[it];
+        nc_w += (uint32_t)__popcll(cm);
+    }
+    if (lane == 0) {
+        s_wc[wave] = nc_w;
+        s_wa[wave] = na_w;
     }
     __syncthreads();
-    const uint32_t nc = s_nc;
+    uint32_t nc = 0, na = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+        nc += s_wc[w];
+        na += s_wa[w];
+        before += w < wave ? s_wc[w] : 0u;
+    }
     if (threadIdx.x == 0 && (int)blockIdx.x < nchunks) {
         ccount[(size_t)seg * nchunks + blockIdx.x] = nc;
-        acount[(size_t)seg * nchunks + blockIdx.x] = s_na;
+        acount[(size_t)seg * nchunks + blockIdx.x] = na;
     }
-    // the chunk owns candidate slots [c0, c0 + CHUNK) of its segment
+    // the chunk owns candidate slots [c0, c0 + CHUNK) of its segment; each
+    // wave writes its region at its offset
     uint64_t *cl = cand + (size_t)seg * Lmax + c0;
-    for (uint32_t i = threadIdx.x; i < nc; i += T1)
-        if (c0 + (int)i < Lmax) cl[i] = s_cand[i];
+    for (uint32_t i = lane; i < nc_w; i += 64)
+        if (c0 + (int)(before + i) < Lmax) cl[before + i] = wcand[i];
 }
 
 // Position of the k-th (0-based) set bit of v; requires k < popcount(v).
@@ -1018,9 +1069,10 @@ tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *
                        K, rk, ws.samp, ws.bctr, ws.info);
     tb_status e = check_launch("tb_select(bounds)");
     if (e) return e;
-    hipLaunchKernelGGL(classify_kernel, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
-                       K, rk, ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand, ws.bitmap,
-                       ws.nwords);
+    auto classify = rk == 0 ? classify_kernel<0> : rk == 1 ? classify_kernel<1>
+                                             : rk == 2 ? classify_kernel<2> : classify_kernel<-1>;
+    hipLaunchKernelGGL(classify, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W, K, rk,
+                       ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand, ws.bitmap, ws.nwords);
     e = check_launch("tb_select(classify)");
     if (e) return e;
     hipLaunchKernelGGL(thr_kernel, dim3(nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
