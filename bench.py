@@ -184,8 +184,8 @@ def run_interval(cfg, args):
         for p in range(npro):
             tb.tb_predict_queries(X[p], W1[p], W2[p], qhat[p], ws_p)
         for l in range(nl):
-            tb.tb_score(qhat[l // cfg.producer_stride], Kp[l], ctx0, scores)
-            tb.tb_select(scores, ctx0, ctx0, cfg.S, cfg.W, cfg.K, cfg.r, idx[l], cnt[l], ws_s, mode=mode)
+            tb.tb_score_select(qhat[l // cfg.producer_stride], Kp[l], ctx0, ctx0, scores, cfg.S,
+                               cfg.W, cfg.K, cfg.r, idx[l], cnt[l], ws_s, mode=mode)
         for j in range(I):
             if app_ev is not None:
                 app_ev[j][0].record(stream)
@@ -353,8 +353,8 @@ def run_offload(cfg, args):
             ctx, pl = lens[l, 0], lens[l, 1]
             e = [ev() for _ in range(3)]
             e[0].record()
-            tb.tb_score(qhat, kp[l], pl, scores)
-            tb.tb_select(scores, ctx, pl, cfg.S, W, cfg.K, cfg.r, idx, cnt, ws_s, mode=mode)
+            tb.tb_score_select(qhat, kp[l], ctx, pl, scores, cfg.S, W, cfg.K, cfg.r, idx, cnt, ws_s,
+                               mode=mode)
             e[1].record()
             tb.tb_offload_gather(kh[l], vh[l], idx, cnt, kb[l], vb[l])
             e[2].record()
@@ -617,6 +617,8 @@ def main():
                           reps[0]["wk"], reps[0]["kp"], pos_new, 1)
     tb.tb_score(qhat, reps[0]["kp"], ctx, scores)
     tb.tb_select(scores, ctx, ctx, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt, ws_s)
+    tb.tb_score_select(qhat, reps[0]["kp"], ctx, ctx, scores, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt,
+                       ws_s)
     tb.tb_sparse_decode_attn(reps[0]["q"], reps[0]["kc"], reps[0]["vc"], idx, cnt, out, ws_a)
     torch.cuda.synchronize()
 
@@ -631,10 +633,9 @@ def main():
             (L_.tb_predict_project, (P(r["x"]), P(r["w1"]), P(r["w2"]), P(qhat), B, cfg.E, cfg.Eh,
                                      cfg.n_out, P(ws_p), nb(ws_p), P(r["kc"]), P(r["wk"]),
                                      P(r["kp"]), P(pos_new), 1, cfg.Hkv, L, cfg.D, cfg.dp, sp)),
-            (L_.tb_score, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(scores), B, cfg.Hq, cfg.Hkv, L,
-                           cfg.dp, sp)),
-            (L_.tb_select, (P(scores), P(ctx), P(ctx), B, cfg.Hq, L, cfg.S, cfg.W, cfg.K, cfg.r,
-                            tb.TB_NF_FILL, P(idx), P(cnt), cap, P(ws_s), nb(ws_s), sp)),
+            (L_.tb_score_select, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(ctx), P(scores), B, cfg.Hq,
+                                  cfg.Hkv, L, cfg.dp, cfg.S, cfg.W, cfg.K, cfg.r, tb.TB_NF_FILL,
+                                  P(idx), P(cnt), cap, P(ws_s), nb(ws_s), sp)),
             (L_.tb_sparse_decode_attn, (P(r["q"]), P(r["kc"]), P(r["vc"]), P(idx), P(cnt), cap,
                                         None, 0, B, cfg.Hq, cfg.Hkv, L, cfg.D,
                                         ctypes.c_float(1.0 / np.sqrt(cfg.D)), P(out), P(ws_a),
@@ -644,7 +645,7 @@ def main():
     def run_step(i, ev=None):
         c = calls[i % R]
         for j, (fn, a) in enumerate(c):
-            if ev is not None and j == 3:
+            if ev is not None and j == len(c) - 1:   # the attention
                 ev[0].record(stream)
             st = fn(*a)
             if st:
@@ -710,7 +711,7 @@ def main():
     # replayed back to back between two events on its stream, so the average
     # is the launch's own duration (no host gaps between launches)
     def attn_only(i):
-        fn, a = calls[i % R][3]
+        fn, a = calls[i % R][-1]
         if fn(*a):
             raise RuntimeError(L_.tb_last_error_detail().decode())
     g_attn = capture(attn_only, R)
@@ -750,13 +751,20 @@ def main():
 
     stages = None
     if args.stages:
-        # each stage alone, as a graph of that stage over the R replicas
-        names = ["predict+project", "score", "select", "attention"]
+        # each stage alone, as a graph of that stage over the R replicas; the
+        # separate scoring and selection calls are timed beside the fused one
+        sep = [[(L_.tb_score, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(scores), B, cfg.Hq, cfg.Hkv,
+                               L, cfg.dp, sp)),
+                (L_.tb_select, (P(scores), P(ctx), P(ctx), B, cfg.Hq, L, cfg.S, cfg.W, cfg.K,
+                                cfg.r, tb.TB_NF_FILL, P(idx), P(cnt), cap, P(ws_s), nb(ws_s),
+                                sp))] for r in reps]
+        names = [("predict+project", calls, 0), ("score+select", calls, 1),
+                 ("attention", calls, 2), ("score", sep, 0), ("select", sep, 1)]
         stages = {}
         n_rep = 50
-        for j, n in enumerate(names):
-            def one(i, j=j):
-                fn, a = calls[i % R][j]
+        for n, cl, j in names:
+            def one(i, j=j, cl=cl):
+                fn, a = cl[i % R][j]
                 if fn(*a):
                     raise RuntimeError(L_.tb_last_error_detail().decode())
             g = capture(one, R)
@@ -859,7 +867,7 @@ def main():
     if stages:
         res["stages_us"] = stages
         # score + select + attention: compulsory bytes are the K' read and the union gather
-        span_us = stages["score"] + stages["select"] + stages["attention"]
+        span_us = stages["score+select"] + stages["attention"]
         span_bytes = kp_bytes + union_rows * row_bytes
         res["score_select_attn"] = {"us": round(span_us, 2), "bytes": span_bytes,
                                     "gbps": span_bytes / span_us / 1e3,

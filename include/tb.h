@@ -255,6 +255,23 @@ tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *
                     void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Scoring and selection in one call ("Core architecture": scoring, then
+ * selection under a fixed budget; "Inference strategy": the three buffers):
+ * exactly tb_score(qhat, n_slots, slot, kp, proj_len, scores, ...) followed
+ * by tb_select(scores, ctx_len, proj_len, ..., mode, idx, count, cap,
+ * workspace, ...) -- the same scores, idx and count -- with one launch fewer:
+ * the selection's sampled band is computed by extra workgroups of the
+ * scoring launch, from the projected keys directly, while the scores stream.
+ * Arguments, limits and workspace (tb_select_workspace_bytes) are those of
+ * the two calls; scores is still written (the selection reads it).
+ */
+tb_status tb_score_select(const float *qhat, int n_slots, int slot, const void *kp,
+                          const int32_t *ctx_len, const int32_t *proj_len, float *scores,
+                          int B, int Hq, int Hkv, int Lmax, int dp, int sink, int window,
+                          int budget, int radius, int mode, int32_t *idx, int32_t *count,
+                          int cap, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Sparse decode attention ("Significance": attend over the retained cache
  * reading only the selected tokens):
  *     out[b, h] = sum_{t in F} softmax_t( scale * q[b,h] . k[b, h/g, t] ) v[b, h/g, t]

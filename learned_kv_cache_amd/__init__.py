@@ -78,6 +78,9 @@ def lib():
     L.tb_select.restype = _i
     L.tb_select.argtypes = [_vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
                             _sz, _vp]
+    L.tb_score_select.restype = _i
+    L.tb_score_select.argtypes = [_vp, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
+                                  _i, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]
     L.tb_attn_workspace_bytes.restype = _sz
     L.tb_attn_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
     L.tb_sparse_decode_attn.restype = _i
@@ -309,6 +312,28 @@ def tb_select(scores, ctx_len, proj_len, sink, window, budget, radius, idx, coun
                            _ptr(proj_len, torch.int32, "proj_len"), B, Hq, Lmax, int(sink), int(window),
                            int(budget), int(radius), int(mode), _ptr(idx, torch.int32, "idx", 3),
                            _ptr(count, torch.int32, "count", 2), cap, wp, wn, _stream(stream)))
+    return idx, count
+
+
+def tb_score_select(qhat, kp, ctx_len, proj_len, scores, sink, window, budget, radius, idx, count,
+                    workspace, mode=TB_NF_FILL, n_slots=1, slot=0, stream=None):
+    """tb_score followed by tb_select (same results) with the selection's band
+    sampled inside the scoring launch."""
+    B, Hkv, Lmax, dp = kp.shape
+    Hq = scores.shape[1]
+    cap = idx.shape[-1]
+    if tuple(scores.shape) != (B, Hq, Lmax) or qhat.numel() != B * n_slots * Hq * dp:
+        raise ValueError("tb_score_select: shape mismatch")
+    if tuple(idx.shape) != (B, Hq, cap) or tuple(count.shape) != (B, Hq):
+        raise ValueError("tb_score_select: shape mismatch")
+    wp, wn = _ws(workspace)
+    _check(lib().tb_score_select(_ptr(qhat, torch.float32, "qhat"), int(n_slots), int(slot),
+                                 _ptr(kp, torch.float16, "kp", 4), _ptr(ctx_len, torch.int32, "ctx_len"),
+                                 _ptr(proj_len, torch.int32, "proj_len"),
+                                 _ptr(scores, torch.float32, "scores", 3), B, Hq, Hkv, Lmax, dp,
+                                 int(sink), int(window), int(budget), int(radius), int(mode),
+                                 _ptr(idx, torch.int32, "idx", 3), _ptr(count, torch.int32, "count", 2),
+                                 cap, wp, wn, _stream(stream)))
     return idx, count
 
 

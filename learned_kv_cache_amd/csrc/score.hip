@@ -6,7 +6,7 @@
 // the dot products of all g query heads that share the row's KV head, so every
 // key byte crosses HBM once and the g scores come out as coalesced fp32 rows.
 // The g*dp query values are wave-uniform and live in registers.
-#include "tb_common.h"
+#include "score_impl.h"
 
 namespace tb {
 namespace {
@@ -49,23 +49,8 @@ __global__ __launch_bounds__(kThreads) void score_kernel(
     for (int i = 0; i < kRowsPerThread; ++i) {
         const int t = t0 + i * kThreads;
         if (t >= P) continue;
-        float k[DP];
 #pragma unroll
-        for (int v = 0; v < V; ++v) {
-            const uint32_t w[4] = {raw[i][v].x, raw[i][v].y, raw[i][v].z, raw[i][v].w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                k[v * 8 + 2 * e] = f16_lo(w[e]);
-                k[v * 8 + 2 * e + 1] = f16_hi(w[e]);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < DP; ++c) acc = __builtin_fmaf(k[c], q[g][c], acc);
-            sb[(size_t)g * Lmax + t] = acc;
-        }
+        for (int g = 0; g < G; ++g) sb[(size_t)g * Lmax + t] = score_row<DP>(raw[i], q[g]);
     }
 }
 

@@ -31,7 +31,7 @@
 //   compact  one wave per chunk: bitmap words ORed with the chunk's chosen
 //            candidates and the sink / window bits, emitted as ascending
 //            positions with coalesced stores.
-#include "tb_common.h"
+#include "score_impl.h"
 
 namespace tb {
 namespace {
@@ -258,63 +258,20 @@ __device__ __forceinline__ void band_edges(const uint32_t (&v)[PER], int n, int 
     *t_lo = (db << (32 - QB)) | ((uint32_t)s_sel[2] << (32 - 2 * QB));
 }
 
-// Workgroup x of a segment samples j in [x * T3, (x + 1) * T3). R >= 0: the
-// radius is R (a thread's neighbour loads are all issued before any is used);
-// R < 0: any radius, read token by token. Samples go to samp[seg] with
-// agent-scope stores; the last workgroup to arrive reads them back with
-// agent-scope loads, resets the arrival counter and writes the band.
-template <int R>
-__global__ __launch_bounds__(T3) void bounds_kernel(const float *__restrict__ scores,
-                                                    const int32_t *__restrict__ ctx,
-                                                    const int32_t *__restrict__ plen, int Hq,
-                                                    int Lmax, int S, int W, int K, int r,
-                                                    uint32_t *__restrict__ samp,
-                                                    uint32_t *__restrict__ bctr,
-                                                    uint32_t *__restrict__ info) {
-    static_assert(BG * T3 == NSAMP, "one sample per thread");
+// Stores the key of sample j (when j < ns) with an agent-scope store, counts
+// the workgroup's arrival at segment seg and, in the last of its BG sampling
+// workgroups to arrive, reads the samples back with agent-scope loads, resets
+// the arrival counter and writes the band. Every thread of the block calls it.
+__device__ __forceinline__ void band_from_samples(int seg, int j, int ns, uint32_t key, int stride,
+                                                  const Region &g, uint32_t *__restrict__ samp,
+                                                  uint32_t *__restrict__ bctr,
+                                                  uint32_t *__restrict__ info) {
     __shared__ uint32_t s_hist[2 * QBINS];
     __shared__ uint32_t s_w[T3 / 64];
     __shared__ int s_sel[4];
     __shared__ bool s_last;
-    const int seg = blockIdx.y, b = seg / Hq;
-    // the sample grid depends only on S and Lmax, so the scores are loaded
-    // before the lengths are known; neighbours outside E are dropped after
-    const int stride = Lmax > S + NSAMP ? (Lmax - S + NSAMP - 1) / NSAMP : 1;
-    const int off = stride / 2;
-    const float *sc = scores + (size_t)seg * Lmax;
-    const int j = blockIdx.x * T3 + threadIdx.x;
-    const int t = S + off + j * stride;
-    constexpr int NX = R >= 0 ? 2 * R + 1 : 1;
-    float x[NX];
-    if constexpr (R >= 0) {
-#pragma unroll
-        for (int u = 0; u < NX; ++u) {
-            int p = t - R + u;
-            p = p < S ? S : (p >= Lmax ? Lmax - 1 : p);
-            x[u] = t < Lmax ? sc[p] : 0.f;
-        }
-    }
-    const Region g = region(ctx, plen, b, Lmax, S, W, K);
-    const int nE = g.e1 - g.e0;
-    if (g.bad || g.need == 0 || g.need == nE) return;   // the same for every workgroup of seg
-    const int ns = nE > off ? (nE - off + stride - 1) / stride : 0;
     uint32_t *sp = samp + (size_t)seg * NSAMP;
-    if (j < ns) {
-        uint32_t key = 0u;
-        if constexpr (R >= 0) {
-            // key32 of a pooled key = max order key over [t - R, t + R]
-            // within E (t itself is in E)
-#pragma unroll
-            for (int u = 0; u < NX; ++u) {
-                const int p = t - R + u;
-                const uint32_t k = order_key(x[u]);
-                if (p >= g.e0 && p < g.e1 && k > key) key = k;
-            }
-        } else {
-            key = (uint32_t)(pooled_key_g(sc, t, g.e0, g.e1, r) >> 32);
-        }
-        __hip_atomic_store(sp + j, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (j < ns) __hip_atomic_store(sp + j, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // every wave's sample stores complete before the arrival is counted
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -331,6 +288,7 @@ __global__ __launch_bounds__(T3) void bounds_kernel(const float *__restrict__ sc
         const int k = threadIdx.x + i * T3;
         v[i] = k < ns ? __hip_atomic_load(sp + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     }
+    const int nE = g.e1 - g.e0;
     // sample ranks (0-based from the top) on either side of the budget's rank
     int rhi, rlo;
     if (stride == 1) {
@@ -349,6 +307,164 @@ __global__ __launch_bounds__(T3) void bounds_kernel(const float *__restrict__ sc
     if (threadIdx.x == 0) {
         info[2 * seg] = tlo;
         info[2 * seg + 1] = thi;
+    }
+}
+
+// The sample grid of a segment depends only on S and Lmax: sample j sits at
+// position S + off + j * stride, stride = ceil((Lmax - S) / NSAMP) (every
+// position when that is 1), off = stride / 2. ns of them fall inside E.
+__device__ __forceinline__ int sample_stride(int Lmax, int S) {
+    return Lmax > S + NSAMP ? (Lmax - S + NSAMP - 1) / NSAMP : 1;
+}
+
+// Workgroup x of a segment samples j in [x * T3, (x + 1) * T3). R >= 0: the
+// radius is R (a thread's neighbour loads are all issued before any is used);
+// R < 0: any radius, read token by token.
+template <int R>
+__global__ __launch_bounds__(T3) void bounds_kernel(const float *__restrict__ scores,
+                                                    const int32_t *__restrict__ ctx,
+                                                    const int32_t *__restrict__ plen, int Hq,
+                                                    int Lmax, int S, int W, int K, int r,
+                                                    uint32_t *__restrict__ samp,
+                                                    uint32_t *__restrict__ bctr,
+                                                    uint32_t *__restrict__ info) {
+    static_assert(BG * T3 == NSAMP, "one sample per thread");
+    const int seg = blockIdx.y, b = seg / Hq;
+    // the scores are loaded before the lengths are known; neighbours outside
+    // E are dropped after
+    const int stride = sample_stride(Lmax, S);
+    const int off = stride / 2;
+    const float *sc = scores + (size_t)seg * Lmax;
+    const int j = blockIdx.x * T3 + threadIdx.x;
+    const int t = S + off + j * stride;
+    constexpr int NX = R >= 0 ? 2 * R + 1 : 1;
+    float x[NX];
+    if constexpr (R >= 0) {
+#pragma unroll
+        for (int u = 0; u < NX; ++u) {
+            int p = t - R + u;
+            p = p < S ? S : (p >= Lmax ? Lmax - 1 : p);
+            x[u] = t < Lmax ? sc[p] : 0.f;
+        }
+    }
+    const Region g = region(ctx, plen, b, Lmax, S, W, K);
+    const int nE = g.e1 - g.e0;
+    if (g.bad || g.need == 0 || g.need == nE) return;   // the same for every workgroup of seg
+    const int ns = nE > off ? (nE - off + stride - 1) / stride : 0;
+    uint32_t key = 0u;
+    if (j < ns) {
+        if constexpr (R >= 0) {
+            // key32 of a pooled key = max order key over [t - R, t + R]
+            // within E (t itself is in E)
+#pragma unroll
+            for (int u = 0; u < NX; ++u) {
+                const int p = t - R + u;
+                const uint32_t k = order_key(x[u]);
+                if (p >= g.e0 && p < g.e1 && k > key) key = k;
+            }
+        } else {
+            key = (uint32_t)(pooled_key_g(sc, t, g.e0, g.e1, r) >> 32);
+        }
+    }
+    band_from_samples(seg, j, ns, key, stride, g, samp, bctr, info);
+}
+
+// Scoring and the band's samples in one launch. Blocks [0, nsb), nsb = BG *
+// segments, sample: block (seg, x) = (blk / BG, blk % BG) recomputes the
+// scores of its sample positions and their neighbours straight from the
+// projected keys with score_row (the same bits as the scores written by the
+// other blocks) and proceeds as bounds_kernel. Blocks [nsb, ...) score T3
+// tokens of one (b, KV head) each, as the scoring kernel does. The sampling
+// blocks come first, so they are dispatched first and their band work
+// overlaps the scoring stream; block x of every segment lands on the same
+// XCD, so the g heads of a KV group read the same key rows through one L2.
+template <int G, int DP, int R>
+__global__ __launch_bounds__(T3, R >= 2 ? 1 : 8) void score_bounds_kernel(
+    const float *__restrict__ qhat, int q_bstride, int q_off, const uint16_t *__restrict__ kp,
+    const int32_t *__restrict__ ctx, const int32_t *__restrict__ plen,
+    float *__restrict__ scores, int Hq, int Hkv, int Lmax, int S, int W, int K, int nsb, int nxs,
+    uint32_t *__restrict__ samp, uint32_t *__restrict__ bctr, uint32_t *__restrict__ info) {
+    static_assert(BG * T3 == NSAMP, "one sample per thread");
+    constexpr int V = DP / 8;   // 16-byte vectors per key row
+    const int blk = blockIdx.x;
+    if (blk >= nsb) {
+        const int sbk = blk - nsb;
+        const int x = sbk % nxs, kvh = (sbk / nxs) % Hkv, b = sbk / (nxs * Hkv);
+        int P = plen[b];
+        P = P < 0 ? 0 : (P > Lmax ? Lmax : P);
+        if (x * T3 >= P) return;
+        const int t = x * T3 + (int)threadIdx.x;
+        const float *qb = qhat + (size_t)b * q_bstride + q_off + (size_t)kvh * G * DP;
+        float q[G][DP];
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi)
+#pragma unroll
+            for (int c = 0; c < DP; ++c) q[gi][c] = qb[gi * DP + c];
+        if (t >= P) return;
+        const uint4 *kb = reinterpret_cast<const uint4 *>(kp + (size_t)(b * Hkv + kvh) * Lmax * DP);
+        uint4 raw[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) raw[v] = kb[(size_t)t * V + v];
+        float *sb = scores + (size_t)(b * Hq + kvh * G) * Lmax;
+#pragma unroll
+        for (int gi = 0; gi < G; ++gi) sb[(size_t)gi * Lmax + t] = score_row<DP>(raw, q[gi]);
+        return;
+    }
+    const int seg = blk / BG, b = seg / Hq, h = seg - b * Hq, kvh = h / G;
+    const int stride = sample_stride(Lmax, S);
+    const int off = stride / 2;
+    const int j = (blk % BG) * T3 + (int)threadIdx.x;
+    const int t = S + off + j * stride;
+    constexpr int NX = 2 * R + 1;
+    const uint4 *kb = reinterpret_cast<const uint4 *>(kp + (size_t)(b * Hkv + kvh) * Lmax * DP);
+    // the key rows are loaded before the lengths are known; neighbours
+    // outside E are dropped after
+    uint4 raw[NX][V];
+    if (t < Lmax) {
+#pragma unroll
+        for (int u = 0; u < NX; ++u) {
+            int p = t - R + u;
+            p = p < S ? S : (p >= Lmax ? Lmax - 1 : p);
+#pragma unroll
+            for (int v = 0; v < V; ++v) raw[u][v] = kb[(size_t)p * V + v];
+        }
+    }
+    float q[DP];
+    const float *qh = qhat + (size_t)b * q_bstride + q_off + (size_t)h * DP;
+#pragma unroll
+    for (int c = 0; c < DP; ++c) q[c] = qh[c];
+    const Region g = region(ctx, plen, b, Lmax, S, W, K);
+    const int nE = g.e1 - g.e0;
+    if (g.bad || g.need == 0 || g.need == nE) return;   // the same for every workgroup of seg
+    const int ns = nE > off ? (nE - off + stride - 1) / stride : 0;
+    uint32_t key = 0u;
+    if (j < ns) {
+#pragma unroll
+        for (int u = 0; u < NX; ++u) {
+            const int p = t - R + u;
+            const uint32_t k = order_key(score_row<DP>(raw[u], q));
+            if (p >= g.e0 && p < g.e1 && k > key) key = k;
+        }
+    }
+    band_from_samples(seg, j, ns, key, stride, g, samp, bctr, info);
+}
+
+typedef void (*score_bounds_fn)(const float *, int, int, const uint16_t *, const int32_t *,
+                                const int32_t *, float *, int, int, int, int, int, int, int, int,
+                                uint32_t *, uint32_t *, uint32_t *);
+
+template <int DP, int R>
+score_bounds_fn score_bounds_pick(int g) {
+    switch (g) {
+        case 1: return score_bounds_kernel<1, DP, R>;
+        case 2: return score_bounds_kernel<2, DP, R>;
+        case 3: return score_bounds_kernel<3, DP, R>;
+        case 4: return score_bounds_kernel<4, DP, R>;
+        case 5: return score_bounds_kernel<5, DP, R>;
+        case 6: return score_bounds_kernel<6, DP, R>;
+        case 7: return score_bounds_kernel<7, DP, R>;
+        case 8: return score_bounds_kernel<8, DP, R>;
+        default: return nullptr;
     }
 }
 
@@ -1055,25 +1171,22 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
     return bctr_b + info_b + 3 * cc_b + thr_b + bm_b + cand_b + samp_b + dbm_b + dc_b;
 }
 
-tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
-                        int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
-                        bool omit_window, int32_t *idx, int32_t *count, int cap,
-                        const SelectWs &ws, hipStream_t st) {
+namespace {
+
+// classify, threshold, then compaction (or dilation and emission): every
+// launch of the selection after the band.
+tb_status launch_after_band(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
+                            int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
+                            bool omit_window, int32_t *idx, int32_t *count, int cap,
+                            const SelectWs &ws, hipStream_t st) {
     const int nseg = B * Hq;
     dim3 grid(ws.nchunks, nseg);
-    // dilation: the centres are the plain top-K (radius 0), widened afterwards
     const int rk = dilate ? 0 : r;
-    auto bounds = rk == 0 ? bounds_kernel<0> : rk == 1 ? bounds_kernel<1>
-                                         : rk == 2 ? bounds_kernel<2> : bounds_kernel<-1>;
-    hipLaunchKernelGGL(bounds, dim3(BG, nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
-                       K, rk, ws.samp, ws.bctr, ws.info);
-    tb_status e = check_launch("tb_select(bounds)");
-    if (e) return e;
     auto classify = rk == 0 ? classify_kernel<0> : rk == 1 ? classify_kernel<1>
                                              : rk == 2 ? classify_kernel<2> : classify_kernel<-1>;
     hipLaunchKernelGGL(classify, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W, K, rk,
                        ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand, ws.bitmap, ws.nwords);
-    e = check_launch("tb_select(classify)");
+    tb_status e = check_launch("tb_select(classify)");
     if (e) return e;
     hipLaunchKernelGGL(thr_kernel, dim3(nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
                        K, rk, omit_window ? 1 : 0, ws.info, ws.ccount, ws.acount, ws.nchunks,
@@ -1095,6 +1208,62 @@ tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *
                        omit_window ? 1 : 0, ws.dbm, ws.nwords, ws.dcount, ws.nchunks, idx, count,
                        cap);
     return check_launch("tb_select(emit dilated)");
+}
+
+}  // namespace
+
+tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
+                        int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
+                        bool omit_window, int32_t *idx, int32_t *count, int cap,
+                        const SelectWs &ws, hipStream_t st) {
+    const int nseg = B * Hq;
+    // dilation: the centres are the plain top-K (radius 0), widened afterwards
+    const int rk = dilate ? 0 : r;
+    auto bounds = rk == 0 ? bounds_kernel<0> : rk == 1 ? bounds_kernel<1>
+                                         : rk == 2 ? bounds_kernel<2> : bounds_kernel<-1>;
+    hipLaunchKernelGGL(bounds, dim3(BG, nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
+                       K, rk, ws.samp, ws.bctr, ws.info);
+    tb_status e = check_launch("tb_select(bounds)");
+    if (e) return e;
+    return launch_after_band(scores, ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window, idx,
+                             count, cap, ws, st);
+}
+
+tb_status launch_score_select(const float *qhat, int n_slots, int slot, const void *kp,
+                              const int32_t *ctx, const int32_t *plen, float *scores, int B,
+                              int Hq, int Hkv, int Lmax, int dp, int S, int W, int K, int r,
+                              bool dilate, bool omit_window, int32_t *idx, int32_t *count,
+                              int cap, const SelectWs &ws, hipStream_t st) {
+    const int rk = dilate ? 0 : r;
+    const int g = Hq / Hkv;
+    score_bounds_fn fn = nullptr;
+    if (dp == 16)
+        fn = rk == 0 ? score_bounds_pick<16, 0>(g) : rk == 1 ? score_bounds_pick<16, 1>(g)
+           : rk == 2 ? score_bounds_pick<16, 2>(g) : nullptr;
+    else if (dp == 32)
+        fn = rk == 0 ? score_bounds_pick<32, 0>(g) : rk == 1 ? score_bounds_pick<32, 1>(g)
+           : rk == 2 ? score_bounds_pick<32, 2>(g) : nullptr;
+    if (!fn) {
+        // radii above 2: the scores first, then the selection's own sampling
+        tb_status e = launch_score(qhat, n_slots, slot, kp, plen, scores, B, Hq, Hkv, Lmax, dp, st);
+        if (e) return e;
+        return launch_select(scores, ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window, idx,
+                             count, cap, ws, st);
+    }
+    const int nsb = BG * B * Hq;
+    const int nxs = (Lmax + T3 - 1) / T3;
+    const long long nblk = (long long)nsb + (long long)nxs * Hkv * B;
+    if (nblk > 0x7fffffffLL) {
+        set_error("tb_score_select: grid of %lld blocks too large", nblk);
+        return TB_ERR_UNSUPPORTED_SHAPE;
+    }
+    hipLaunchKernelGGL(fn, dim3((unsigned)nblk), dim3(T3), 0, st, qhat, n_slots * Hq * dp,
+                       slot * Hq * dp, static_cast<const uint16_t *>(kp), ctx, plen, scores, Hq, Hkv,
+                       Lmax, S, W, K, nsb, nxs, ws.samp, ws.bctr, ws.info);
+    tb_status e = check_launch("tb_score_select(score + band)");
+    if (e) return e;
+    return launch_after_band(scores, ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window, idx,
+                             count, cap, ws, st);
 }
 
 }  // namespace tb

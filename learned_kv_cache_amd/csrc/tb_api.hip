@@ -248,41 +248,86 @@ size_t tb_select_workspace_bytes(int B, int Hq, int Lmax) {
     return tb::select_ws_layout(B, Hq, Lmax, nullptr, nullptr);
 }
 
-tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *proj_len, int B,
-                    int Hq, int Lmax, int sink, int window, int budget, int radius, int mode,
-                    int32_t *idx, int32_t *count, int cap, void *workspace, size_t ws_bytes,
-                    void *stream) {
-    TB_REQUIRE(scores && ctx_len && proj_len && idx && count && workspace,
-               TB_ERR_INVALID_ARGUMENT, "tb_select: null pointer");
-    TB_REQUIRE(aligned4(scores) && aligned4(ctx_len) && aligned4(proj_len) && aligned4(idx) &&
-                   aligned4(count) && aligned16(workspace),
-               TB_ERR_INVALID_ARGUMENT, "tb_select: misaligned pointer");
+namespace {
+
+// Checks shared by tb_select and tb_score_select (fn names the caller in the
+// error detail); fills ws.
+tb_status check_select(const char *fn, const int32_t *ctx_len, const int32_t *proj_len, int B,
+                       int Hq, int Lmax, int sink, int window, int budget, int radius, int mode,
+                       int32_t *idx, int32_t *count, int cap, void *workspace, size_t ws_bytes,
+                       tb::SelectWs *ws) {
+    TB_REQUIRE(ctx_len && proj_len && idx && count && workspace, TB_ERR_INVALID_ARGUMENT,
+               "%s: null pointer", fn);
+    TB_REQUIRE(aligned4(ctx_len) && aligned4(proj_len) && aligned4(idx) && aligned4(count) &&
+                   aligned16(workspace),
+               TB_ERR_INVALID_ARGUMENT, "%s: misaligned pointer", fn);
     TB_REQUIRE(B >= 1 && Hq >= 1 && (long long)B * Hq <= 65535 && Lmax >= 1,
-               TB_ERR_INVALID_ARGUMENT, "tb_select: bad sizes B=%d Hq=%d Lmax=%d", B, Hq, Lmax);
-    TB_REQUIRE(Lmax <= (1 << 24), TB_ERR_UNSUPPORTED_SHAPE, "tb_select: Lmax > 2^24");
+               TB_ERR_INVALID_ARGUMENT, "%s: bad sizes B=%d Hq=%d Lmax=%d", fn, B, Hq, Lmax);
+    TB_REQUIRE(Lmax <= (1 << 24), TB_ERR_UNSUPPORTED_SHAPE, "%s: Lmax > 2^24", fn);
     TB_REQUIRE(sink >= 0 && window >= 0 && budget >= 0 && radius >= 0, TB_ERR_INVALID_ARGUMENT,
-               "tb_select: negative sink/window/budget/radius");
-    TB_REQUIRE(radius <= 64, TB_ERR_UNSUPPORTED_SHAPE, "tb_select: radius > 64");
+               "%s: negative sink/window/budget/radius", fn);
+    TB_REQUIRE(radius <= 64, TB_ERR_UNSUPPORTED_SHAPE, "%s: radius > 64", fn);
     TB_REQUIRE((mode & ~(0xff | TB_SEL_OMIT_WINDOW)) == 0, TB_ERR_INVALID_ARGUMENT,
-               "tb_select: unknown mode bits 0x%x", mode);
+               "%s: unknown mode bits 0x%x", fn, mode);
     TB_REQUIRE((mode & 0xff) == TB_NF_FILL || (mode & 0xff) == TB_NF_DILATE,
-               TB_ERR_INVALID_ARGUMENT, "tb_select: unknown neighbour mode %d", mode & 0xff);
+               TB_ERR_INVALID_ARGUMENT, "%s: unknown neighbour mode %d", fn, mode & 0xff);
     const bool omit = (mode & TB_SEL_OMIT_WINDOW) != 0;
     const bool dilate = (mode & 0xff) == TB_NF_DILATE;
     const long long imp = dilate ? (2LL * radius + 1) * budget : (long long)budget;
     const long long need_cap = (long long)sink + (omit ? 0 : window) + imp;
     const long long min_cap = need_cap < Lmax ? need_cap : Lmax;
     TB_REQUIRE(cap >= 1 && cap >= min_cap, TB_ERR_INVALID_ARGUMENT,
-               "tb_select: cap %d < min(Lmax, sink + important (+ window unless omitted)) = %lld",
+               "%s: cap %d < min(Lmax, sink + important (+ window unless omitted)) = %lld", fn,
                cap, min_cap);
     const size_t need = tb_select_workspace_bytes(B, Hq, Lmax);
-    TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
-               "tb_select: workspace %zu < %zu bytes", ws_bytes, need);
+    TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", fn,
+               ws_bytes, need);
+    tb::select_ws_layout(B, Hq, Lmax, workspace, ws);
+    return TB_OK;
+}
+
+}  // namespace
+
+tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *proj_len, int B,
+                    int Hq, int Lmax, int sink, int window, int budget, int radius, int mode,
+                    int32_t *idx, int32_t *count, int cap, void *workspace, size_t ws_bytes,
+                    void *stream) {
+    TB_REQUIRE(scores, TB_ERR_INVALID_ARGUMENT, "tb_select: null pointer");
+    TB_REQUIRE(aligned4(scores), TB_ERR_INVALID_ARGUMENT, "tb_select: misaligned pointer");
     tb::SelectWs ws;
-    tb::select_ws_layout(B, Hq, Lmax, workspace, &ws);
+    const tb_status e = check_select("tb_select", ctx_len, proj_len, B, Hq, Lmax, sink, window,
+                                     budget, radius, mode, idx, count, cap, workspace, ws_bytes,
+                                     &ws);
+    if (e) return e;
     return tb::launch_select(scores, ctx_len, proj_len, B, Hq, Lmax, sink, window, budget, radius,
-                             dilate, omit, idx, count, cap, ws,
-                             static_cast<hipStream_t>(stream));
+                             (mode & 0xff) == TB_NF_DILATE, (mode & TB_SEL_OMIT_WINDOW) != 0, idx,
+                             count, cap, ws, static_cast<hipStream_t>(stream));
+}
+
+tb_status tb_score_select(const float *qhat, int n_slots, int slot, const void *kp,
+                          const int32_t *ctx_len, const int32_t *proj_len, float *scores, int B,
+                          int Hq, int Hkv, int Lmax, int dp, int sink, int window, int budget,
+                          int radius, int mode, int32_t *idx, int32_t *count, int cap,
+                          void *workspace, size_t ws_bytes, void *stream) {
+    TB_REQUIRE(qhat && kp && scores, TB_ERR_INVALID_ARGUMENT, "tb_score_select: null pointer");
+    TB_REQUIRE(aligned4(qhat) && aligned16(kp) && aligned4(scores), TB_ERR_INVALID_ARGUMENT,
+               "tb_score_select: misaligned pointer");
+    TB_REQUIRE(Hkv >= 1 && Hkv <= 65535 && n_slots >= 1 && slot >= 0 && slot < n_slots,
+               TB_ERR_INVALID_ARGUMENT, "tb_score_select: bad sizes");
+    TB_REQUIRE(Hq >= 1 && Hq % Hkv == 0, TB_ERR_INVALID_ARGUMENT,
+               "tb_score_select: Hq %% Hkv != 0");
+    TB_REQUIRE(Hq / Hkv <= 8 && (dp == 16 || dp == 32), TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_score_select: need Hq/Hkv <= 8 and dp in {16, 32}");
+    tb::SelectWs ws;
+    const tb_status e = check_select("tb_score_select", ctx_len, proj_len, B, Hq, Lmax, sink,
+                                     window, budget, radius, mode, idx, count, cap, workspace,
+                                     ws_bytes, &ws);
+    if (e) return e;
+    return tb::launch_score_select(qhat, n_slots, slot, kp, ctx_len, proj_len, scores, B, Hq, Hkv,
+                                   Lmax, dp, sink, window, budget, radius,
+                                   (mode & 0xff) == TB_NF_DILATE,
+                                   (mode & TB_SEL_OMIT_WINDOW) != 0, idx, count, cap, ws,
+                                   static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------- attention

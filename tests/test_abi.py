@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(tb):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     lib = ctypes.CDLL(tb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -108,6 +108,19 @@ def test_validation_rejects_before_launch(tb):
     assert L.tb_sparse_decode_attn(*A(9, 64, ws)) == 1
     assert L.tb_sparse_decode_attn(*A(8, 64, ws, -1)) == 1
     assert L.tb_select(*args(4, 16, 32, 1, 0x200, 52, ws)) == 1
+    # score + select in one call: the checks of both
+    SS = lambda q, Hq, dp, K, r, cap, wsb: (q, 1, 0, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, Hq, 2,
+                                            300, dp, 4, 16, K, r, 0, vp(FAKE), vp(FAKE), cap, vp(FAKE),
+                                            wsb, None)
+    assert L.tb_score_select(*SS(None, 8, 16, 32, 1, 52, ws)) == 1
+    assert L.tb_score_select(*SS(vp(MIS), 8, 16, 32, 1, 52, ws)) == 1
+    assert L.tb_score_select(*SS(vp(FAKE), 9, 16, 32, 1, 52, ws)) == 1     # Hq % Hkv
+    assert L.tb_score_select(*SS(vp(FAKE), 18, 16, 32, 1, 52, ws)) == 2    # group of 9
+    assert L.tb_score_select(*SS(vp(FAKE), 8, 24, 32, 1, 52, ws)) == 2     # d' = 24
+    assert L.tb_score_select(*SS(vp(FAKE), 8, 16, -1, 1, 52, ws)) == 1
+    assert L.tb_score_select(*SS(vp(FAKE), 8, 16, 32, 65, 52, ws)) == 2
+    assert L.tb_score_select(*SS(vp(FAKE), 8, 16, 32, 1, 51, ws)) == 1
+    assert L.tb_score_select(*SS(vp(FAKE), 8, 16, 32, 1, 52, 100)) == 3
 
 
 def test_binding_rejects_cpu_tensors(tb):

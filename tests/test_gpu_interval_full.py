@@ -85,9 +85,8 @@ def test_interval_full_shape(tb, orc, cid):
         ctx.copy_(ctx0)
         plen.copy_(ctx0)
         tb.tb_predict_queries(x, w1, w2, qhat, ws_p)
-        tb.tb_score(qhat, kp, ctx0, scores)
-        tb.tb_select(scores, ctx0, ctx0, S, W, K, r, idx, cnt, ws_s,
-                     mode=tb.TB_NF_FILL | tb.TB_SEL_OMIT_WINDOW)
+        tb.tb_score_select(qhat, kp, ctx0, ctx0, scores, S, W, K, r, idx, cnt, ws_s,
+                           mode=tb.TB_NF_FILL | tb.TB_SEL_OMIT_WINDOW)
         for j in range(I):
             tb.tb_append_kv(kn_d[j], vn_d[j], kc, vc, kp, wk, ctx, plen, Np)
             tb.tb_sparse_decode_attn(q, kc, vc, idx, cnt, out, ws, ctx_len=ctx, window=W)
