@@ -259,11 +259,14 @@ tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *
  * selection under a fixed budget; "Inference strategy": the three buffers):
  * exactly tb_score(qhat, n_slots, slot, kp, proj_len, scores, ...) followed
  * by tb_select(scores, ctx_len, proj_len, ..., mode, idx, count, cap,
- * workspace, ...) -- the same scores, idx and count -- with one launch fewer:
- * the selection's sampled band is computed by extra workgroups of the
- * scoring launch, from the projected keys directly, while the scores stream.
- * Arguments, limits and workspace (tb_select_workspace_bytes) are those of
- * the two calls; scores is still written (the selection reads it).
+ * workspace, ...) -- the same scores, idx and count. For small problems
+ * (radius <= 1 -- 0 in TB_NF_DILATE mode -- and 8 B Hq at most the device's
+ * compute-unit count) it takes one launch fewer: the selection's sampled
+ * band is computed by extra workgroups of the scoring launch, from the
+ * projected keys directly, while the scores stream; otherwise it issues the
+ * two calls' launches. Arguments, limits and workspace
+ * (tb_select_workspace_bytes) are those of the two calls; scores is still
+ * written (the selection reads it).
  */
 tb_status tb_score_select(const float *qhat, int n_slots, int slot, const void *kp,
                           const int32_t *ctx_len, const int32_t *proj_len, float *scores,

@@ -378,13 +378,15 @@ __global__ __launch_bounds__(T3) void bounds_kernel(const float *__restrict__ sc
 // blocks come first, so they are dispatched first and their band work
 // overlaps the scoring stream; block x of every segment lands on the same
 // XCD, so the g heads of a KV group read the same key rows through one L2.
+// Used for radius <= 1 while the sampling blocks number at most one per CU.
 template <int G, int DP, int R>
-__global__ __launch_bounds__(T3, R >= 2 ? 1 : 8) void score_bounds_kernel(
+__global__ __launch_bounds__(T3, 8) void score_bounds_kernel(
     const float *__restrict__ qhat, int q_bstride, int q_off, const uint16_t *__restrict__ kp,
     const int32_t *__restrict__ ctx, const int32_t *__restrict__ plen,
     float *__restrict__ scores, int Hq, int Hkv, int Lmax, int S, int W, int K, int nsb, int nxs,
     uint32_t *__restrict__ samp, uint32_t *__restrict__ bctr, uint32_t *__restrict__ info) {
     static_assert(BG * T3 == NSAMP, "one sample per thread");
+    static_assert(R <= 1, "two blocks per CU need at most 64 registers");
     constexpr int V = DP / 8;   // 16-byte vectors per key row
     const int blk = blockIdx.x;
     if (blk >= nsb) {
@@ -1236,21 +1238,31 @@ tb_status launch_score_select(const float *qhat, int n_slots, int slot, const vo
                               int cap, const SelectWs &ws, hipStream_t st) {
     const int rk = dilate ? 0 : r;
     const int g = Hq / Hkv;
+    const int nsb = BG * B * Hq;
+    // The fused launch saves a launch but its sampling blocks re-read
+    // projected-key rows and hold CU slots while they wait on their band; it
+    // pays only while they take at most one block slot per CU next to the
+    // scoring stream (measured slower with more sampling blocks, and with
+    // the 2R + 1 = 5 rows of radius 2, whose registers allow one 1024-thread
+    // block per CU).
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        ncu = 0;
     score_bounds_fn fn = nullptr;
-    if (dp == 16)
-        fn = rk == 0 ? score_bounds_pick<16, 0>(g) : rk == 1 ? score_bounds_pick<16, 1>(g)
-           : rk == 2 ? score_bounds_pick<16, 2>(g) : nullptr;
-    else if (dp == 32)
-        fn = rk == 0 ? score_bounds_pick<32, 0>(g) : rk == 1 ? score_bounds_pick<32, 1>(g)
-           : rk == 2 ? score_bounds_pick<32, 2>(g) : nullptr;
+    if (nsb <= ncu) {
+        if (dp == 16)
+            fn = rk == 0 ? score_bounds_pick<16, 0>(g) : rk == 1 ? score_bounds_pick<16, 1>(g) : nullptr;
+        else if (dp == 32)
+            fn = rk == 0 ? score_bounds_pick<32, 0>(g) : rk == 1 ? score_bounds_pick<32, 1>(g) : nullptr;
+    }
     if (!fn) {
-        // radii above 2: the scores first, then the selection's own sampling
+        // the scores first, then the selection's own sampling launch
         tb_status e = launch_score(qhat, n_slots, slot, kp, plen, scores, B, Hq, Hkv, Lmax, dp, st);
         if (e) return e;
         return launch_select(scores, ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window, idx,
                              count, cap, ws, st);
     }
-    const int nsb = BG * B * Hq;
     const int nxs = (Lmax + T3 - 1) / T3;
     const long long nblk = (long long)nsb + (long long)nxs * Hkv * B;
     if (nblk > 0x7fffffffLL) {

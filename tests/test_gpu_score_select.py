@@ -1,7 +1,9 @@
-"""tb_score_select (the selection's band sampled by extra workgroups of the
-scoring launch, from the projected keys) equals tb_score followed by tb_select
-bit for bit -- scores, list and count -- over shapes covering every compiled
-(group size, d', radius) variant, both neighbour modes, the window left out,
+"""tb_score_select (for small problems the selection's band is sampled by
+extra workgroups of the scoring launch, from the projected keys; otherwise the
+two calls' launches) equals tb_score followed by tb_select bit for bit --
+scores, list and count -- over shapes covering every compiled (group size,
+d', radius) variant of the fused launch and the separate launches (radius 2
+and above, many heads), both neighbour modes, the window left out,
 ragged and lagging projections, short contexts, a budget covering the
 eligible region, an empty budget, invalid lengths and radii above the fused
 variants; and its list equals the oracle's selection on the same scores."""
@@ -93,8 +95,8 @@ def test_score_select_ragged_qwen_shape(tb, orc):
     _case(tb, 2, 4, 28, 4, 20000, 32, L, P, 32, 128, 3936, 2, orc=orc)
 
 
-@pytest.mark.parametrize("g,dp,r", [(1, 32, 0), (2, 16, 1), (3, 32, 2), (5, 16, 0), (6, 32, 1),
-                                    (8, 16, 2), (8, 32, 1), (4, 16, 5)])
+@pytest.mark.parametrize("g,dp,r", [(1, 32, 0), (2, 16, 1), (3, 32, 1), (5, 16, 0), (6, 32, 1),
+                                    (7, 16, 0), (8, 32, 1), (3, 32, 2), (8, 16, 2), (4, 16, 5)])
 def test_score_select_group_sizes(tb, orc, g, dp, r):
     Hkv = 2
     Lmax = 12000
