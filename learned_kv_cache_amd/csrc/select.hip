@@ -144,6 +144,17 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *s_w, u
     return before + x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (lane order).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
 // Pooled key of eligible token t read straight from the scores (global).
 __device__ __forceinline__ uint64_t pooled_key_g(const float *s, int t, int e0, int e1, int r) {
     const int a = t - r < e0 ? e0 : t - r;
@@ -746,10 +757,14 @@ __global__ __launch_bounds__(T3) void thr_kernel(
     __shared__ uint32_t s_off[MAX_CHUNKS];
     __shared__ uint32_t s_chosen[MAX_CHUNKS];
     __shared__ KthLds s_k;
+    __shared__ uint32_t s_tot[2];
 
     const int seg = blockIdx.x, b = seg / Hq;
     const int tid = threadIdx.x;
     constexpr int PC = MAX_CHUNKS / T3;
+    // chunk c's counts sit in thread c / PC: with at most 64 PC chunks they
+    // all sit in wave 0, whose shuffles then replace the block-wide scans
+    const bool small = nchunks <= 64 * PC;
     uint32_t cc[PC], ac[PC];
     // per-chunk counts and the band are loaded before the lengths are known
 #pragma unroll
@@ -783,14 +798,35 @@ __global__ __launch_bounds__(T3) void thr_kernel(
     const uint64_t *cl = cand + (size_t)seg * Lmax;
     if (partial) {
         uint32_t nc, above;
-        uint32_t run = block_incl_scan<T3>(csum, s_k.w, &nc) - csum;
+        if (small) {
+            if (tid < 64) {
+                const uint32_t incl = wave_incl_scan(csum);
+                uint32_t run = incl - csum;
 #pragma unroll
-        for (int j = 0; j < PC; ++j) {
-            const int c = tid * PC + j;
-            if (c < nchunks) s_off[c] = run;
-            run += cc[j];
+                for (int j = 0; j < PC; ++j) {
+                    const int c = tid * PC + j;
+                    if (c < nchunks) s_off[c] = run;
+                    run += cc[j];
+                }
+                const uint32_t a_incl = wave_incl_scan(asum);
+                if (tid == 63) {
+                    s_tot[0] = incl;
+                    s_tot[1] = a_incl;
+                }
+            }
+            __syncthreads();
+            nc = s_tot[0];
+            above = s_tot[1];
+        } else {
+            uint32_t run = block_incl_scan<T3>(csum, s_k.w, &nc) - csum;
+#pragma unroll
+            for (int j = 0; j < PC; ++j) {
+                const int c = tid * PC + j;
+                if (c < nchunks) s_off[c] = run;
+                run += cc[j];
+            }
+            block_incl_scan<T3>(asum, s_k.w, &above);
         }
-        block_incl_scan<T3>(asum, s_k.w, &above);
         const int need1 = g.need - (int)above;
         if (need1 >= 0 && need1 <= (int)nc) {
             if (need1 == (int)nc) {
@@ -913,6 +949,23 @@ __global__ __launch_bounds__(T3) void thr_kernel(
         if (c < nchunks)
             tot_c[j] = ac[j] + s_chosen[c] + (uint32_t)fixed_in(c * CHUNK, (c + 1) * CHUNK, slo, wlo, L);
         lsum += tot_c[j];
+    }
+    if (small) {
+        if (tid < 64) {
+            const uint32_t incl = wave_incl_scan(lsum);
+            uint32_t run = incl - lsum;
+#pragma unroll
+            for (int j = 0; j < PC; ++j) {
+                const int c = tid * PC + j;
+                if (c < nchunks) coff[(size_t)seg * nchunks + c] = run;
+                run += tot_c[j];
+            }
+            if (tid == 63) {
+                count[seg] = (int32_t)incl;
+                thr_out[seg] = thr;
+            }
+        }
+        return;
     }
     uint32_t total;
     uint32_t run = block_incl_scan<T3>(lsum, s_k.w, &total) - lsum;
