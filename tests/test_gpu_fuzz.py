@@ -1,7 +1,10 @@
 """Randomized GPU parity sweeps on small shapes (seeded): many (batch, heads,
 context, sink, window, budget, radius, mode) combinations for the selection
 in both neighbour modes, with and without the window, ragged lengths and
-projection lag, bit-exact against the oracle; and projection + scoring +
+projection lag, bit-exact against the oracle; the same for scoring and
+selection in one call (tb_score_select, either of its routes), its lists
+bit-exact against the oracle's selection on its scores and its scores within
+2e-3 of the oracle's; and projection + scoring +
 attention (over a list, and over a list plus the implicit local window at a
 random length) on random small shapes within their tolerances."""
 import numpy as np
@@ -52,6 +55,54 @@ def test_select_random_configs(tb, orc):
         tb.tb_select(dev32(s), dev32(L), dev32(P), S, W, K, r, idx, cnt, ws, mode=mode)
         torch.cuda.synchronize()
         gi, gc = host(idx), host(cnt)
+        for b in range(B):
+            for h in range(Hq):
+                ref = ri[b, h, :rc[b, h]]
+                if omit:
+                    ref = ref[(ref < S) | (ref < L[b] - W)]
+                assert gc[b, h] == len(ref), what
+                assert np.array_equal(gi[b, h, :gc[b, h]], ref), what
+
+
+def test_score_select_random_configs(tb, orc):
+    rng = rng_for(122)
+    for trial in range(40):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.integers(1, 9))
+        Hq = Hkv * g
+        dp = int(rng.choice([16, 32]))
+        Lmax = int(rng.choice([1, 64, 300, 2047, 2049, 5000, 12000]))
+        S, W = int(rng.integers(0, 40)), int(rng.integers(0, 300))
+        K = int(rng.integers(0, Lmax + 50))
+        r = int(rng.choice([0, 1, 1, 2, 3]))
+        dilate = bool(rng.integers(0, 2))
+        omit = bool(rng.integers(0, 2))
+        L = rng.integers(0, Lmax + 1, size=B).astype(np.int32)
+        P = np.minimum(L, rng.integers(0, Lmax + 1, size=B)).astype(np.int32)
+        kp = (rng.standard_normal((B, Hkv, Lmax, dp)) * 0.5).astype(np.float16).view(np.uint16)
+        qhat = rng.standard_normal((B, Hq * dp)).astype(np.float32)
+        imp = (2 * r + 1) * K if dilate else K
+        cap = max(1, min(Lmax, S + (0 if omit else W) + imp))
+        what = (trial, B, Hq, Hkv, dp, Lmax, S, W, K, r, dilate, omit, L.tolist(), P.tolist())
+        say("score_select fuzz", *what)
+        scores = torch.full((B, Hq, Lmax), float("nan"), device="cuda")
+        idx = torch.full((B, Hq, cap), -7, dtype=torch.int32, device="cuda")
+        cnt = torch.full((B, Hq), -7, dtype=torch.int32, device="cuda")
+        ws = tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax))
+        mode = (tb.TB_NF_DILATE if dilate else tb.TB_NF_FILL) | (tb.TB_SEL_OMIT_WINDOW if omit else 0)
+        tb.tb_score_select(dev32(qhat), dev(kp, torch.float16), dev32(L), dev32(P), scores, S, W,
+                           K, r, idx, cnt, ws, mode=mode)
+        torch.cuda.synchronize()
+        gs, gi, gc = host(scores), host(idx), host(cnt)
+        ref_s = orc.score(qhat, kp, P, Hq)
+        for b in range(B):
+            if P[b]:
+                assert_rel(gs[b, :, :P[b]], ref_s[b, :, :P[b]], 2e-3, "scores %s" % (what,))
+        # the oracle's selection on the GPU's scores (positions at or past the
+        # projected length are never read; give them a finite value)
+        s_in = np.where(np.isnan(gs), np.float32(0), gs).astype(np.float32)
+        ri, rc = orc.select(s_in, L, P, S, W, K, r, cap=min(Lmax, S + W + imp) or 1, dilate=dilate)
         for b in range(B):
             for h in range(Hq):
                 ref = ri[b, h, :rc[b, h]]
