@@ -31,6 +31,9 @@
 //   compact  one wave per chunk: bitmap words ORed with the chunk's chosen
 //            candidates and the sink / window bits, emitted as ascending
 //            positions with coalesced stores.
+// For small problems tb_score_select replaces the bounds launch by sampling
+// workgroups inside the scoring launch (score_bounds_kernel), which compute
+// the scores around their samples from the projected keys themselves.
 #include "score_impl.h"
 
 namespace tb {
