@@ -11,9 +11,12 @@ Inputs are resident in HBM before the timed region; R replicas of every
 per-step input are rotated so that each step reads cold memory (the working
 set of one step fits in the 256 MiB MALL). The timed steps replay a HIP graph
 that holds R consecutive steps (one per replica), as a serving loop would;
-the same steps issued call by call are timed too ("eager"). The dominant
-kernel (sparse attention gather) is timed live with HIP events on its launch
-stream during the eager pass.
+the same steps issued call by call are timed too ("eager"). The step's calls
+are tb_predict_project, tb_score_select with the list deferred, and
+tb_select_attn (the list written by the attention workgroups, which then
+attend over it). The dominant kernel (that compaction + attention launch)
+is timed live with HIP events on its launch stream, over back-to-back graph
+replays of it alone.
 
 Prints one JSON line. Run with --gpus 1 only.
 """
@@ -33,8 +36,17 @@ import numpy as np
 
 METRIC = "sparse decode steps/s at 64K ctx, 8K budget; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_gather_c2_traffic.txt")
-ATTN_SRC = os.path.join(ROOT, "learned_kv_cache_amd", "csrc", "attn.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compact_attn_c2_traffic.txt")
+# sources of the step's dominant kernel (compaction + attention)
+KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_amd", "csrc", f)
+               for f in ("select.hip", "attn_impl.h")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def log(*a):
@@ -57,8 +69,8 @@ def planting_direction(inp, cfg):
 
 
 def traffic_record():
-    """HBM bytes per attention launch from the committed rocprofv3 PMC
-    summary, if it was taken on the current attention source."""
+    """HBM bytes per launch of the step's dominant kernel from the committed
+    rocprofv3 PMC summary, if it was taken on the kernel's current sources."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     rec = {}
@@ -66,8 +78,8 @@ def traffic_record():
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    src_hash = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()[:16]
-    if rec.get("attn_source_sha256_16") != src_hash or "traffic_bytes_per_launch" not in rec:
+    if (rec.get("kernel_source_sha256_16") != kernel_source_hash()
+            or "traffic_bytes_per_launch" not in rec):
         return None
     return float(rec["traffic_bytes_per_launch"])
 
@@ -620,6 +632,11 @@ def main():
     tb.tb_score_select(qhat, reps[0]["kp"], ctx, ctx, scores, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt,
                        ws_s)
     tb.tb_sparse_decode_attn(reps[0]["q"], reps[0]["kc"], reps[0]["vc"], idx, cnt, out, ws_a)
+    defer = tb.TB_NF_FILL | tb.TB_SEL_DEFER_LIST
+    tb.tb_score_select(qhat, reps[0]["kp"], ctx, ctx, scores, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt,
+                       ws_s, mode=defer)
+    tb.tb_select_attn(ctx, ctx, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt, ws_s, reps[0]["q"],
+                      reps[0]["kc"], reps[0]["vc"], out, ws_a, mode=defer)
     torch.cuda.synchronize()
 
     L_ = tb.lib()
@@ -634,18 +651,19 @@ def main():
                                      cfg.n_out, P(ws_p), nb(ws_p), P(r["kc"]), P(r["wk"]),
                                      P(r["kp"]), P(pos_new), 1, cfg.Hkv, L, cfg.D, cfg.dp, sp)),
             (L_.tb_score_select, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(ctx), P(scores), B, cfg.Hq,
-                                  cfg.Hkv, L, cfg.dp, cfg.S, cfg.W, cfg.K, cfg.r, tb.TB_NF_FILL,
-                                  P(idx), P(cnt), cap, P(ws_s), nb(ws_s), sp)),
-            (L_.tb_sparse_decode_attn, (P(r["q"]), P(r["kc"]), P(r["vc"]), P(idx), P(cnt), cap,
-                                        None, 0, B, cfg.Hq, cfg.Hkv, L, cfg.D,
-                                        ctypes.c_float(1.0 / np.sqrt(cfg.D)), P(out), P(ws_a),
-                                        nb(ws_a), sp)),
+                                  cfg.Hkv, L, cfg.dp, cfg.S, cfg.W, cfg.K, cfg.r, defer, P(idx),
+                                  P(cnt), cap, P(ws_s), nb(ws_s), sp)),
+            (L_.tb_select_attn, (P(ctx), P(ctx), B, cfg.Hq, cfg.Hkv, L, cfg.S, cfg.W, cfg.K, cfg.r,
+                                 defer, P(idx), P(cnt), cap, P(ws_s), nb(ws_s), P(r["q"]),
+                                 P(r["kc"]), P(r["vc"]), cfg.D,
+                                 ctypes.c_float(1.0 / np.sqrt(cfg.D)), P(out), P(ws_a), nb(ws_a),
+                                 sp)),
         ])
 
     def run_step(i, ev=None):
         c = calls[i % R]
         for j, (fn, a) in enumerate(c):
-            if ev is not None and j == len(c) - 1:   # the attention
+            if ev is not None and j == len(c) - 1:   # the list + attention
                 ev[0].record(stream)
             st = fn(*a)
             if st:
@@ -707,7 +725,8 @@ def main():
                     "p50": round(float(np.percentile(per, 50)), 2),
                     "p90": round(float(np.percentile(per, 90)), 2), "replays": len(rev)}
 
-    # the dominant kernel alone: a graph of one attention launch per replica,
+    # the dominant kernel alone: a graph of one compaction + attention launch
+    # per replica (tb_select_attn on the selection state the last step left),
     # replayed back to back between two events on its stream, so the average
     # is the launch's own duration (no host gaps between launches)
     def attn_only(i):
@@ -758,8 +777,17 @@ def main():
                 (L_.tb_select, (P(scores), P(ctx), P(ctx), B, cfg.Hq, L, cfg.S, cfg.W, cfg.K,
                                 cfg.r, tb.TB_NF_FILL, P(idx), P(cnt), cap, P(ws_s), nb(ws_s),
                                 sp))] for r in reps]
+        # the list written by the selection, then the attention launch over it
+        lst = [[(L_.tb_score_select, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(ctx), P(scores), B,
+                                      cfg.Hq, cfg.Hkv, L, cfg.dp, cfg.S, cfg.W, cfg.K, cfg.r,
+                                      tb.TB_NF_FILL, P(idx), P(cnt), cap, P(ws_s), nb(ws_s), sp)),
+                (L_.tb_sparse_decode_attn, (P(r["q"]), P(r["kc"]), P(r["vc"]), P(idx), P(cnt),
+                                            cap, None, 0, B, cfg.Hq, cfg.Hkv, L, cfg.D,
+                                            ctypes.c_float(1.0 / np.sqrt(cfg.D)), P(out), P(ws_a),
+                                            nb(ws_a), sp))] for r in reps]
         names = [("predict+project", calls, 0), ("score+select", calls, 1),
-                 ("attention", calls, 2), ("score", sep, 0), ("select", sep, 1)]
+                 ("list+attention", calls, 2), ("score+select, list written", lst, 0),
+                 ("attention", lst, 1), ("score", sep, 0), ("select", sep, 1)]
         stages = {}
         n_rep = 50
         for n, cl, j in names:
@@ -852,7 +880,8 @@ def main():
                    "global_batch": B, "seq_len": L},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "sparse decode attention gather (attn_kernel<128>)",
+                     "kernel": "list compaction + sparse decode attention gather "
+                               "(compact_attn_kernel<128>)",
                      "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6,
                      "launches_timed": n_attn * R,
                      "avg_launch_us_eager_events": attn_eager_avg_s * 1e6},
@@ -867,7 +896,7 @@ def main():
     if stages:
         res["stages_us"] = stages
         # score + select + attention: compulsory bytes are the K' read and the union gather
-        span_us = stages["score+select"] + stages["attention"]
+        span_us = stages["score+select"] + stages["list+attention"]
         span_bytes = kp_bytes + union_rows * row_bytes
         res["score_select_attn"] = {"us": round(span_us, 2), "bytes": span_bytes,
                                     "gbps": span_bytes / span_us / 1e3,

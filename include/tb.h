@@ -58,6 +58,10 @@ typedef int tb_status;
  * sink U important); tb_sparse_decode_attn then adds the window itself from
  * ctx_len, so one selection serves every step of a prediction interval. */
 #define TB_SEL_OMIT_WINDOW 0x100
+/* mode flag of tb_select / tb_score_select (TB_NF_FILL only): stop before the
+ * list is written -- count is written, idx is not; the selection state stays
+ * in the workspace for tb_select_attn, which writes idx and attends. */
+#define TB_SEL_DEFER_LIST 0x200
 
 /* Human-readable text for a status code (static storage). */
 const char *tb_status_string(tb_status s);
@@ -273,6 +277,29 @@ tb_status tb_score_select(const float *qhat, int n_slots, int slot, const void *
                           int B, int Hq, int Hkv, int Lmax, int dp, int sink, int window,
                           int budget, int radius, int mode, int32_t *idx, int32_t *count,
                           int cap, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * The selection's list and the sparse attention over it in one launch
+ * ("Inference strategy": the three buffers; "Significance": attention reads
+ * only the selected tokens). Called after tb_select or tb_score_select with
+ * mode | TB_SEL_DEFER_LIST on the same workspace, arguments and stream, with
+ * the same mode here: writes idx exactly as the selection without the flag
+ * would, and out exactly as tb_sparse_decode_attn(q, k_cache, v_cache, idx,
+ * count, cap, NULL, 0, B, Hq, Hkv, Lmax, D, scale, out, attn_workspace, ...)
+ * would (bit for bit: the same splits through the same code). Each attention
+ * workgroup rebuilds its split's list rows from the selection's bitmap and
+ * candidates (one compaction launch fewer); with more than 64 chunks of 2048
+ * tokens (Lmax > 131072) it issues the compaction and attention launches
+ * instead. attn_workspace is sized by tb_attn_workspace_bytes(B, Hq, cap, 0,
+ * D). A selection state from any other call sequence gives unspecified
+ * results.
+ */
+tb_status tb_select_attn(const int32_t *ctx_len, const int32_t *proj_len, int B, int Hq, int Hkv,
+                         int Lmax, int sink, int window, int budget, int radius, int mode,
+                         int32_t *idx, int32_t *count, int cap, void *sel_workspace,
+                         size_t sel_ws_bytes, const void *q, const void *k_cache,
+                         const void *v_cache, int D, float scale, float *out,
+                         void *attn_workspace, size_t attn_ws_bytes, void *stream);
 
 /*
  * Sparse decode attention ("Significance": attend over the retained cache

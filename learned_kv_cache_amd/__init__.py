@@ -22,6 +22,7 @@ TB_ERR_HIP = 4
 TB_NF_FILL = 0
 TB_NF_DILATE = 1
 TB_SEL_OMIT_WINDOW = 0x100
+TB_SEL_DEFER_LIST = 0x200
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -81,6 +82,9 @@ def lib():
     L.tb_score_select.restype = _i
     L.tb_score_select.argtypes = [_vp, _i, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i,
                                   _i, _i, _i, _vp, _vp, _i, _vp, _sz, _vp]
+    L.tb_select_attn.restype = _i
+    L.tb_select_attn.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
+                                 _sz, _vp, _vp, _vp, _i, ctypes.c_float, _vp, _vp, _sz, _vp]
     L.tb_attn_workspace_bytes.restype = _sz
     L.tb_attn_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
     L.tb_sparse_decode_attn.restype = _i
@@ -335,6 +339,30 @@ def tb_score_select(qhat, kp, ctx_len, proj_len, scores, sink, window, budget, r
                                  _ptr(idx, torch.int32, "idx", 3), _ptr(count, torch.int32, "count", 2),
                                  cap, wp, wn, _stream(stream)))
     return idx, count
+
+
+def tb_select_attn(ctx_len, proj_len, sink, window, budget, radius, idx, count, sel_workspace, q,
+                   k_cache, v_cache, out, attn_workspace, mode=TB_NF_FILL | TB_SEL_DEFER_LIST,
+                   scale=None, stream=None):
+    """After a selection with TB_SEL_DEFER_LIST: write its list and attend over it."""
+    B, Hq, cap = idx.shape
+    Hkv, Lmax, D = k_cache.shape[1], k_cache.shape[2], k_cache.shape[3]
+    if (tuple(count.shape) != (B, Hq) or tuple(k_cache.shape) != (B, Hkv, Lmax, D)
+            or tuple(v_cache.shape) != (B, Hkv, Lmax, D) or tuple(q.shape) != (B, Hq, D)
+            or tuple(out.shape) != (B, Hq, D)):
+        raise ValueError("tb_select_attn: shape mismatch")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    sp, sn = _ws(sel_workspace)
+    ap, an = _ws(attn_workspace)
+    _check(lib().tb_select_attn(_ptr(ctx_len, torch.int32, "ctx_len"), _ptr(proj_len, torch.int32, "proj_len"),
+                                B, Hq, Hkv, Lmax, int(sink), int(window), int(budget), int(radius),
+                                int(mode), _ptr(idx, torch.int32, "idx", 3), _ptr(count, torch.int32, "count", 2),
+                                cap, sp, sn, _ptr(q, torch.bfloat16, "q", 3),
+                                _ptr(k_cache, torch.bfloat16, "k_cache", 4),
+                                _ptr(v_cache, torch.bfloat16, "v_cache", 4), D, ctypes.c_float(scale),
+                                _ptr(out, torch.float32, "out", 3), ap, an, _stream(stream)))
+    return idx, out
 
 
 # ---------------------------------------------------------------- attention

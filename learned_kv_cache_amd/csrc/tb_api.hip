@@ -267,10 +267,12 @@ tb_status check_select(const char *fn, const int32_t *ctx_len, const int32_t *pr
     TB_REQUIRE(sink >= 0 && window >= 0 && budget >= 0 && radius >= 0, TB_ERR_INVALID_ARGUMENT,
                "%s: negative sink/window/budget/radius", fn);
     TB_REQUIRE(radius <= 64, TB_ERR_UNSUPPORTED_SHAPE, "%s: radius > 64", fn);
-    TB_REQUIRE((mode & ~(0xff | TB_SEL_OMIT_WINDOW)) == 0, TB_ERR_INVALID_ARGUMENT,
-               "%s: unknown mode bits 0x%x", fn, mode);
+    TB_REQUIRE((mode & ~(0xff | TB_SEL_OMIT_WINDOW | TB_SEL_DEFER_LIST)) == 0,
+               TB_ERR_INVALID_ARGUMENT, "%s: unknown mode bits 0x%x", fn, mode);
     TB_REQUIRE((mode & 0xff) == TB_NF_FILL || (mode & 0xff) == TB_NF_DILATE,
                TB_ERR_INVALID_ARGUMENT, "%s: unknown neighbour mode %d", fn, mode & 0xff);
+    TB_REQUIRE(!((mode & TB_SEL_DEFER_LIST) && (mode & 0xff) == TB_NF_DILATE),
+               TB_ERR_INVALID_ARGUMENT, "%s: TB_SEL_DEFER_LIST needs TB_NF_FILL", fn);
     const bool omit = (mode & TB_SEL_OMIT_WINDOW) != 0;
     const bool dilate = (mode & 0xff) == TB_NF_DILATE;
     const long long imp = dilate ? (2LL * radius + 1) * budget : (long long)budget;
@@ -301,7 +303,8 @@ tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *
     if (e) return e;
     return tb::launch_select(scores, ctx_len, proj_len, B, Hq, Lmax, sink, window, budget, radius,
                              (mode & 0xff) == TB_NF_DILATE, (mode & TB_SEL_OMIT_WINDOW) != 0, idx,
-                             count, cap, ws, static_cast<hipStream_t>(stream));
+                             count, cap, ws, static_cast<hipStream_t>(stream),
+                             (mode & TB_SEL_DEFER_LIST) != 0);
 }
 
 tb_status tb_score_select(const float *qhat, int n_slots, int slot, const void *kp,
@@ -327,7 +330,44 @@ tb_status tb_score_select(const float *qhat, int n_slots, int slot, const void *
                                    Lmax, dp, sink, window, budget, radius,
                                    (mode & 0xff) == TB_NF_DILATE,
                                    (mode & TB_SEL_OMIT_WINDOW) != 0, idx, count, cap, ws,
-                                   static_cast<hipStream_t>(stream));
+                                   static_cast<hipStream_t>(stream),
+                                   (mode & TB_SEL_DEFER_LIST) != 0);
+}
+
+tb_status tb_select_attn(const int32_t *ctx_len, const int32_t *proj_len, int B, int Hq, int Hkv,
+                         int Lmax, int sink, int window, int budget, int radius, int mode,
+                         int32_t *idx, int32_t *count, int cap, void *sel_workspace,
+                         size_t sel_ws_bytes, const void *q, const void *k_cache,
+                         const void *v_cache, int D, float scale, float *out,
+                         void *attn_workspace, size_t attn_ws_bytes, void *stream) {
+    TB_REQUIRE(q && k_cache && v_cache && out && attn_workspace, TB_ERR_INVALID_ARGUMENT,
+               "tb_select_attn: null pointer");
+    TB_REQUIRE(aligned16(q) && aligned16(k_cache) && aligned16(v_cache) && aligned4(out) &&
+                   aligned16(attn_workspace),
+               TB_ERR_INVALID_ARGUMENT, "tb_select_attn: misaligned pointer");
+    TB_REQUIRE(Hkv >= 1 && Hq % Hkv == 0 && Hq / Hkv <= 65535, TB_ERR_INVALID_ARGUMENT,
+               "tb_select_attn: Hq %% Hkv != 0");
+    TB_REQUIRE(D == 64 || D == 128, TB_ERR_UNSUPPORTED_SHAPE, "tb_select_attn: D must be 64 or 128");
+    TB_REQUIRE((long long)Lmax * D * 2 <= 0x7fffffffLL, TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_select_attn: one head's cache must be below 2 GiB (Lmax * D * 2)");
+    TB_REQUIRE(scale == scale, TB_ERR_INVALID_ARGUMENT, "tb_select_attn: scale is NaN");
+    TB_REQUIRE((mode & TB_SEL_DEFER_LIST) != 0, TB_ERR_INVALID_ARGUMENT,
+               "tb_select_attn: mode must carry TB_SEL_DEFER_LIST, as the selection it follows");
+    tb::SelectWs ws;
+    const tb_status e = check_select("tb_select_attn", ctx_len, proj_len, B, Hq, Lmax, sink, window,
+                                     budget, radius, mode, idx, count, cap, sel_workspace,
+                                     sel_ws_bytes, &ws);
+    if (e) return e;
+    const size_t need = tb_attn_workspace_bytes(B, Hq, cap, 0, D);
+    TB_REQUIRE(attn_ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
+               "tb_select_attn: attention workspace %zu < %zu bytes", attn_ws_bytes, need);
+    float *part;
+    uint32_t *ctr;
+    tb::attn_ws_layout(B, Hq, cap, D, attn_workspace, &part, &ctr);
+    return tb::launch_select_attn(ctx_len, proj_len, B, Hq, Hkv, Lmax, sink, window, budget,
+                                  (mode & TB_SEL_OMIT_WINDOW) != 0, idx, count, cap, ws, q,
+                                  k_cache, v_cache, D, scale, out, part, ctr,
+                                  static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------------------------- attention

@@ -120,12 +120,18 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out);
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
                         int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
                         bool omit_window, int32_t *idx, int32_t *count, int cap,
-                        const SelectWs &ws, hipStream_t st);
+                        const SelectWs &ws, hipStream_t st, bool defer_list = false);
 tb_status launch_score_select(const float *qhat, int n_slots, int slot, const void *kp,
                               const int32_t *ctx, const int32_t *plen, float *scores, int B,
                               int Hq, int Hkv, int Lmax, int dp, int S, int W, int K, int r,
                               bool dilate, bool omit_window, int32_t *idx, int32_t *count,
-                              int cap, const SelectWs &ws, hipStream_t st);
+                              int cap, const SelectWs &ws, hipStream_t st,
+                              bool defer_list = false);
+tb_status launch_select_attn(const int32_t *ctx, const int32_t *plen, int B, int Hq, int Hkv,
+                             int Lmax, int S, int W, int K, bool omit_window, int32_t *idx,
+                             int32_t *count, int cap, const SelectWs &ws, const void *q,
+                             const void *kc, const void *vc, int D, float scale, float *out,
+                             float *part, uint32_t *ctr, hipStream_t st);
 int attn_nsplit(int rows);
 size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr);
 tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32_t *idx,

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(tb):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     lib = ctypes.CDLL(tb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -107,7 +107,15 @@ def test_validation_rejects_before_launch(tb):
     assert L.tb_sparse_decode_attn(*A(8, 64, 16)) == 3
     assert L.tb_sparse_decode_attn(*A(9, 64, ws)) == 1
     assert L.tb_sparse_decode_attn(*A(8, 64, ws, -1)) == 1
-    assert L.tb_select(*args(4, 16, 32, 1, 0x200, 52, ws)) == 1
+    assert L.tb_select(*args(4, 16, 32, 1, 0x400, 52, ws)) == 1   # unknown mode bit
+    assert L.tb_select(*args(4, 16, 32, 1, 0x201, 115, ws)) == 1  # deferred list with dilation
+    # list + attention after a deferred selection: its checks reject before launch
+    SA = lambda mode, D, wsa: (vp(FAKE), vp(FAKE), 1, 8, 2, 300, 4, 16, 32, 1, mode, vp(FAKE),
+                               vp(FAKE), 52, vp(FAKE), ws, vp(FAKE), vp(FAKE), vp(FAKE), D,
+                               ctypes.c_float(0.1), vp(FAKE), vp(FAKE), wsa, None)
+    assert L.tb_select_attn(*SA(0, 64, ws)) == 1             # mode without the deferral flag
+    assert L.tb_select_attn(*SA(0x200, 96, ws)) == 2         # unsupported D
+    assert L.tb_select_attn(*SA(0x200, 64, 16)) == 3         # attention workspace too small
     # score + select in one call: the checks of both
     SS = lambda q, Hq, dp, K, r, cap, wsb: (q, 1, 0, vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, Hq, 2,
                                             300, dp, 4, 16, K, r, 0, vp(FAKE), vp(FAKE), cap, vp(FAKE),

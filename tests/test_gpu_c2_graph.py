@@ -1,9 +1,11 @@
 """GPU parity of the full-size single-layer decode step (Llama-3.1-8B-shaped
 layer, 64K context, budget 7872, radius 1, planted spans) in the launch
 configuration the benchmark times: tb_predict_project (predictor + the
-newest key's projection in one launch), tb_score_select (scoring with the
-selection's band sampled in the same launch, then the selection) and
-tb_sparse_decode_attn captured in one HIP graph and replayed. Every replay,
+newest key's projection in one launch), tb_score_select with the list
+deferred (scoring with the selection's band sampled in the same launch, then
+the selection up to its threshold) and tb_select_attn (the list written by the
+attention workgroups, which attend over it) captured in one HIP graph and
+replayed. Every replay,
 with the outputs poisoned before it, is checked against the oracle's step
 on the same seeded inputs (predicted queries, sampled projected-key rows,
 scores, selection with the near-tie band rule, attention)."""
@@ -55,8 +57,11 @@ def test_c2_step_graph_replays_match_oracle(tb, orc):
 
     def step():
         tb.tb_predict_project(x, w1, w2, qhat, ws_p, kc, wk, kp, pos_new, 1)
-        tb.tb_score_select(qhat, kp, ctx, ctx, scores, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt, ws_s)
-        tb.tb_sparse_decode_attn(q, kc, vc, idx, cnt, out, ws_a)
+        defer = tb.TB_NF_FILL | tb.TB_SEL_DEFER_LIST
+        tb.tb_score_select(qhat, kp, ctx, ctx, scores, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt, ws_s,
+                           mode=defer)
+        tb.tb_select_attn(ctx, ctx, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt, ws_s, q, kc, vc, out,
+                          ws_a, mode=defer)
 
     def poison():
         qhat.fill_(float("nan"))
