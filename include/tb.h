@@ -292,7 +292,7 @@ tb_status tb_score_select(const float *qhat, int n_slots, int slot, const void *
  * tokens (Lmax > 131072) it issues the compaction and attention launches
  * instead. attn_workspace is sized by tb_attn_workspace_bytes(B, Hq, cap, 0,
  * D). A selection state from any other call sequence gives unspecified
- * results.
+ * results (every access stays inside the caller's buffers).
  */
 tb_status tb_select_attn(const int32_t *ctx_len, const int32_t *proj_len, int B, int Hq, int Hkv,
                          int Lmax, int sink, int window, int budget, int radius, int mode,

@@ -1202,7 +1202,8 @@ __global__ __launch_bounds__(kAttnThreads) void compact_attn_kernel(
             // second round trip: the chunk's words, candidate count and
             // first candidate slots, issued together
             uint32_t bits = (act && w < nwords) ? bitmap[(size_t)bh * nwords + w] : 0u;
-            const uint32_t nraw = act ? ccount[(size_t)bh * nchunks + c] : 0u;
+            uint32_t nraw = act ? ccount[(size_t)bh * nchunks + c] : 0u;
+            nraw = nraw < (uint32_t)CHUNK ? nraw : (uint32_t)CHUNK;
             uint64_t pk[PF];
 #pragma unroll
             for (int k = 0; k < PF; ++k) {
@@ -1224,17 +1225,20 @@ __global__ __launch_bounds__(kAttnThreads) void compact_attn_kernel(
             s_word[wave][lane] = bits;
             __syncthreads();
 #pragma unroll
+            // a candidate's position lies in its chunk after the selection
+            // this call follows; anything else (a state left by another call
+            // sequence) is ignored rather than written outside the chunk
             for (int k = 0; k < PF; ++k) {
                 if ((uint32_t)(lane + 64 * k) < nc && pk[k] >= thr) {
                     const int t = key_token(pk[k]) - c * CHUNK;
-                    atomicOr(&s_word[wave][t >> 5], 1u << (t & 31));
+                    if ((uint32_t)t < (uint32_t)CHUNK) atomicOr(&s_word[wave][t >> 5], 1u << (t & 31));
                 }
             }
-            for (uint32_t i = lane + 64 * PF; i < nc; i += 64) {
+            for (uint32_t i = lane + 64 * PF; i < nc && c * CHUNK + (int)i < Lmax; i += 64) {
                 const uint64_t key = cl[i];
                 if (key >= thr) {
                     const int t = key_token(key) - c * CHUNK;
-                    atomicOr(&s_word[wave][t >> 5], 1u << (t & 31));
+                    if ((uint32_t)t < (uint32_t)CHUNK) atomicOr(&s_word[wave][t >> 5], 1u << (t & 31));
                 }
             }
             __syncthreads();
