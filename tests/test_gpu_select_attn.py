@@ -6,8 +6,9 @@ count, list and output bit for bit -- after tb_score_select and after
 tb_select, on the fused launch (up to 64 chunks) and on the compaction +
 attention fallback (more chunks), with the window in the list or left out,
 budgets covering the region or empty, short contexts and flagged lengths,
-twice in a row on the same workspaces; and the output against the oracle's
-attention at the 64K shape."""
+a query group of 7, twice in a row on the same workspaces, and 30 random
+configurations; and the output against the oracle's attention at the 64K
+shape.""" 
 import numpy as np
 import pytest
 import torch
@@ -94,6 +95,26 @@ def test_deferred_list_shapes(tb):
     _case(tb, 5, 2, 8, 1, 131072, 64, 16, [131072, 99999], [131072, 99999], 32, 128, 3000, 0)
     _case(tb, 6, 1, 8, 2, 140000, 64, 16, [140000], [140000], 64, 256, 4000, 1)   # fallback
     _case(tb, 7, 1, 32, 8, 65536, 128, 32, [65536], [65536], 64, 256, 7872, 1, omit=True)
+    # Qwen-like group of 7, ragged, radius 2
+    _case(tb, 12, 2, 14, 2, 70000, 128, 32, [70000, 51234], [70000, 51230], 32, 128, 3936, 2)
+
+
+def test_deferred_list_random_configs(tb):
+    rng = rng_for(97)
+    for trial in range(30):
+        B = int(rng.integers(1, 4))
+        Hkv = int(rng.choice([1, 2, 4]))
+        g = int(rng.integers(1, 9))
+        Lmax = int(rng.choice([1, 64, 300, 2047, 2049, 5000, 40000, 131072, 131073]))
+        D = int(rng.choice([64, 128]))
+        dp = int(rng.choice([16, 32]))
+        S, W = int(rng.integers(0, 80)), int(rng.integers(0, 400))
+        K = int(rng.integers(0, min(Lmax + 50, 9000)))
+        r = int(rng.choice([0, 1, 2, 3]))
+        L = rng.integers(0, Lmax + 1, size=B).astype(np.int32)
+        P = np.minimum(L, rng.integers(0, Lmax + 1, size=B)).astype(np.int32)
+        _case(tb, 100 + trial, B, Hkv * g, Hkv, Lmax, D, dp, L.tolist(), P.tolist(), S, W, K, r,
+              omit=bool(rng.integers(0, 2)), via_scores=bool(rng.integers(0, 2)))
 
 
 def test_deferred_list_edges(tb):
