@@ -188,16 +188,15 @@ __device__ __forceinline__ uint64_t pooled_key_g(const float *s, int t, int e0, 
 // holds that key (two 12-bit histogram levels: top bits over all keys, then
 // bits 19..8 within each rank's top bin). The band only has to contain the
 // budget's key, so bin edges serve as well as the exact order statistics.
-// Block-wide, T3 threads; s_hist holds 2 * QBINS counters, s_w T3 / 64,
-// s_sel 4.
+// Block-wide, T3 threads; s_h1 holds QBINS and s_h2 2 * QBINS counters, both
+// zeroed by the caller before a barrier; s_w holds T3 / 64, s_sel 4.
 template <int PER>
 __device__ __forceinline__ void band_edges(const uint32_t (&v)[PER], int n, int ka, int kb,
-                                           uint32_t *s_hist, uint32_t *s_w, int *s_sel,
-                                           uint32_t *t_hi, uint32_t *t_lo) {
+                                           uint32_t *s_h1, uint32_t *s_h2, uint32_t *s_w,
+                                           int *s_sel, uint32_t *t_hi, uint32_t *t_lo) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t *s_hist = s_h1;
     // level 1: bins of the top QB bits, bin index = descending digit
-    for (int i = tid; i < QBINS; i += T3) s_hist[i] = 0u;
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < PER; ++i)
         if (i * T3 + tid < n) atomicAdd(&s_hist[QBINS - 1 - (v[i] >> (32 - QB))], 1u);
@@ -230,8 +229,7 @@ __device__ __forceinline__ void band_edges(const uint32_t (&v)[PER], int n, int 
     const uint32_t da = (uint32_t)s_sel[0], db = (uint32_t)s_sel[2];
     const int ka2 = s_sel[1], kb2 = s_sel[3];
     // level 2: bits 19..8 of the keys in each rank's top bin (histograms A, B)
-    for (int i = tid; i < 2 * QBINS; i += T3) s_hist[i] = 0u;
-    __syncthreads();
+    s_hist = s_h2;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const uint32_t key = v[i], top = key >> (32 - QB);
@@ -285,12 +283,16 @@ __device__ __forceinline__ void band_from_samples(int seg, int j, int ns, uint32
                                                   const Region &g, uint32_t *__restrict__ samp,
                                                   uint32_t *__restrict__ bctr,
                                                   uint32_t *__restrict__ info) {
-    __shared__ uint32_t s_hist[2 * QBINS];
+    __shared__ uint32_t s_h1[QBINS], s_h2[2 * QBINS];
     __shared__ uint32_t s_w[T3 / 64];
     __shared__ int s_sel[4];
     __shared__ bool s_last;
     uint32_t *sp = samp + (size_t)seg * NSAMP;
     if (j < ns) __hip_atomic_store(sp + j, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the band's histograms are cleared while the samples are stored and
+    // counted (the barrier below orders the clearing before their use)
+    for (int i = threadIdx.x; i < QBINS; i += T3) s_h1[i] = 0u;
+    for (int i = threadIdx.x; i < 2 * QBINS; i += T3) s_h2[i] = 0u;
     // every wave's sample stores complete before the arrival is counted
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -320,7 +322,8 @@ __device__ __forceinline__ void band_from_samples(int seg, int j, int ns, uint32
         rlo = (int)ceilf(p) - 1 + m;
     }
     uint32_t thi, tlo;
-    band_edges(v, ns, rhi < 0 ? 0 : rhi, rlo >= ns ? ns - 1 : rlo, s_hist, s_w, s_sel, &thi, &tlo);
+    band_edges(v, ns, rhi < 0 ? 0 : rhi, rlo >= ns ? ns - 1 : rlo, s_h1, s_h2, s_w, s_sel, &thi,
+               &tlo);
     if (rhi < 0) thi = 0xffffffffu;   // nothing is surely above the budget's key
     if (rlo >= ns) tlo = 0u;          // every key may be a candidate
     if (threadIdx.x == 0) {
@@ -874,12 +877,16 @@ __global__ __launch_bounds__(T3) void thr_kernel(
                     for (int i = tid; i < (int)nc; i += T3)
                         f(lds ? s_cand[i] : cand_at(cl, s_off, nchunks, (uint32_t)i));
                 };
-                // candidates share the key32 bits on which the band's ends agree
-                const uint32_t x = tlo ^ thi;
-                const int shift = 32 + (x ? 32 - __clz((int)x) : 0);
+                // ranked on the keys less the band's lower end: the order is
+                // kept (every candidate's key32 lies in [tlo, thi]) and the
+                // digits above the band's width are zero, so the radix passes
+                // start at that width
+                const uint64_t base = (uint64_t)tlo << 32;
+                auto visit_off = [&](auto f) { visit_cand([&](uint64_t key) { f(key - base); }); };
+                const uint32_t dx = thi - tlo;
+                const int shift = 32 + (dx ? 32 - __clz((int)dx) : 0);
                 const uint64_t mask = shift >= 64 ? 0ull : (~0ull << shift);
-                thr = kth_largest(visit_cand, need1, ((uint64_t)thi << 32) & mask, mask, shift,
-                                  (int)nc, s_k);
+                thr = kth_largest(visit_off, need1, 0ull, mask, shift, (int)nc, s_k) + base;
                 // chosen candidates per chunk: candidates are chunk-major, so
                 // a wave's lanes form runs of one chunk; each run's first lane
                 // adds the run's count
