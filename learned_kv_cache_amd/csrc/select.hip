@@ -784,6 +784,21 @@ __global__ __launch_bounds__(T3) void thr_kernel(
         cc[j] = c < nchunks ? ccount[(size_t)seg * nchunks + c] : 0u;
         ac[j] = c < nchunks ? acount[(size_t)seg * nchunks + c] : 0u;
     }
+    // with at most T3 / 32 chunks, 32 threads per chunk also fetch its first
+    // PFC candidate slots now (whatever the counts turn out to be), so that
+    // staging the candidates in LDS takes no round trip of its own
+    constexpr int PFC = 3;
+    const bool pre = nchunks <= T3 / 32;
+    const int pch = tid >> 5, pln = tid & 31;
+    const uint64_t *cl = cand + (size_t)seg * Lmax;
+    uint64_t pv[PFC];
+#pragma unroll
+    for (int u = 0; u < PFC; ++u) {
+        const int slot = pln + 32 * u;
+        pv[u] = (pre && pch < nchunks && pch * CHUNK + slot < Lmax)
+                    ? cl[(size_t)pch * CHUNK + slot]
+                    : 0ull;
+    }
     const uint32_t tlo = info[2 * seg], thi = info[2 * seg + 1];
     const Region g = region(ctx, plen, b, Lmax, S, W, K);
     if (g.bad) {
@@ -806,7 +821,6 @@ __global__ __launch_bounds__(T3) void thr_kernel(
         if (c < nchunks) s_chosen[c] = 0u;
     }
     uint64_t thr = ~0ull;   // candidates with key >= thr are chosen (none by default)
-    const uint64_t *cl = cand + (size_t)seg * Lmax;
     if (partial) {
         uint32_t nc, above;
         if (small) {
@@ -849,7 +863,27 @@ __global__ __launch_bounds__(T3) void thr_kernel(
                 }
             } else if (need1 > 0) {
                 const bool lds = nc <= (uint32_t)LDS_CAND;
-                if (lds) {
+                if (lds && pre) {
+                    // chunk pch's candidates go to LDS slots [s_off[pch], +n_c)
+                    if (pch < nchunks) {
+                        const uint32_t o = s_off[pch];
+                        const uint32_t n_c = (pch + 1 < nchunks ? s_off[pch + 1] : nc) - o;
+#pragma unroll
+                        for (int u = 0; u < PFC; ++u) {
+                            const uint32_t slot = (uint32_t)(pln + 32 * u);
+                            if (slot < n_c) {
+                                s_cand[o + slot] = pv[u];
+                                s_cc[o + slot] = (uint16_t)pch;
+                            }
+                        }
+                        for (uint32_t slot = pln + 32 * PFC;
+                             slot < n_c && slot < (uint32_t)CHUNK && pch * CHUNK + (int)slot < Lmax;
+                             slot += 32) {
+                            s_cand[o + slot] = cl[(size_t)pch * CHUNK + slot];
+                            s_cc[o + slot] = (uint16_t)pch;
+                        }
+                    }
+                } else if (lds) {
                     constexpr int PER = LDS_CAND / T3;
                     uint64_t v[PER];
                     int vc[PER];
