@@ -871,17 +871,12 @@ __global__ __launch_bounds__(T3) void thr_kernel(
 #pragma unroll
                         for (int u = 0; u < PFC; ++u) {
                             const uint32_t slot = (uint32_t)(pln + 32 * u);
-                            if (slot < n_c) {
-                                s_cand[o + slot] = pv[u];
-                                s_cc[o + slot] = (uint16_t)pch;
-                            }
+                            if (slot < n_c) s_cand[o + slot] = pv[u];
                         }
                         for (uint32_t slot = pln + 32 * PFC;
                              slot < n_c && slot < (uint32_t)CHUNK && pch * CHUNK + (int)slot < Lmax;
-                             slot += 32) {
+                             slot += 32)
                             s_cand[o + slot] = cl[(size_t)pch * CHUNK + slot];
-                            s_cc[o + slot] = (uint16_t)pch;
-                        }
                     }
                 } else if (lds) {
                     constexpr int PER = LDS_CAND / T3;
@@ -921,11 +916,29 @@ __global__ __launch_bounds__(T3) void thr_kernel(
                 const int shift = 32 + (dx ? 32 - __clz((int)dx) : 0);
                 const uint64_t mask = shift >= 64 ? 0ull : (~0ull << shift);
                 thr = kth_largest(visit_off, need1, 0ull, mask, shift, (int)nc, s_k) + base;
-                // chosen candidates per chunk: candidates are chunk-major, so
-                // a wave's lanes form runs of one chunk; each run's first lane
-                // adds the run's count
+                if (lds && pre) {
+                    // chosen candidates per chunk: each chunk's 32 threads
+                    // count the slots they staged and sum over the half wave
+                    if (pch < nchunks) {
+                        const uint32_t o = s_off[pch];
+                        const uint32_t n_c = (pch + 1 < nchunks ? s_off[pch + 1] : nc) - o;
+                        uint32_t n = 0;
+#pragma unroll
+                        for (int u = 0; u < PFC; ++u)
+                            n += ((uint32_t)(pln + 32 * u) < n_c && pv[u] >= thr) ? 1u : 0u;
+                        for (uint32_t slot = pln + 32 * PFC;
+                             slot < n_c && slot < (uint32_t)CHUNK && pch * CHUNK + (int)slot < Lmax;
+                             slot += 32)
+                            n += s_cand[o + slot] >= thr ? 1u : 0u;
+#pragma unroll
+                        for (int m = 16; m >= 1; m >>= 1) n += __shfl_xor(n, m);
+                        if (pln == 0) s_chosen[pch] = n;
+                    }
+                }
+                // otherwise: candidates are chunk-major, so a wave's lanes form
+                // runs of one chunk; each run's first lane adds the run's count
                 const int lane = tid & 63;
-                for (int i0 = 0; i0 < (int)nc; i0 += T3) {
+                for (int i0 = 0; i0 < ((lds && pre) ? 0 : (int)nc); i0 += T3) {
                     const int i = i0 + tid;
                     int c = -1;
                     bool ch = false;

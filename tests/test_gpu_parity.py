@@ -295,6 +295,26 @@ def test_select_band_miss_with_ties(tb, orc):
         assert_same_selection(orc, tb, s, [L], [L], S, W, K, r, "band miss ties r=%d" % r)
 
 
+@pytest.mark.parametrize("r", [0, 1])
+def test_select_threshold_staging_beyond_prefetched_slots(tb, orc, r):
+    """With at most 32 chunks per segment the threshold launch fetches each
+    chunk's first 96 candidate slots with the chunk counts and reads the rest
+    afterwards. Tie-heavy scores put every token of one score value in the
+    band (hundreds of candidates per chunk, a few thousand per segment, inside
+    the LDS limit); the lists must equal the oracle's, and the workspace must
+    show chunks beyond the prefetched slots."""
+    rng = rng_for(60, r)
+    B, Hq, L, S, W, K = 1, 2, 20000, 16, 64, 5000
+    s = integer_scores(rng, (B, Hq, L), -3, 4)
+    ws = assert_same_selection(orc, tb, s, [L], [L], S, W, K, r, "staging r=%d" % r)
+    up = lambda x: (x + 255) // 256 * 256
+    nseg, nchunks = B * Hq, -(-L // 2048)
+    off = up(nseg * 4) + up(nseg * 8)
+    cc = host(ws[off: off + nseg * nchunks * 4].view(torch.int32)).reshape(nseg, nchunks)
+    assert nchunks <= 32
+    assert (cc.max(axis=1) > 96).all() and (cc.sum(axis=1) <= 8192).all(), cc
+
+
 # ------------------------------------------------- selection, dilation mode
 
 @pytest.mark.parametrize("r", [0, 1, 2])
