@@ -695,7 +695,8 @@ struct KthLds {
 // to f exactly once, from any thread; every thread calls it and it may hold
 // barriers. grp: how many keys carry the prefix (anything above GMAX when
 // unknown). 10-bit radix passes narrow the group to at most GMAX keys, which
-// are ranked directly.
+// are ranked directly. sh.tile and sh.ng are zero on entry (cleared by the
+// caller before a barrier); each pass clears its bins again as it reads them.
 template <class Visit>
 __device__ __forceinline__ uint64_t kth_largest(const Visit &visit, int k, uint64_t prefix,
                                                 uint64_t mask, int shift, int grp, KthLds &sh) {
@@ -706,14 +707,13 @@ __device__ __forceinline__ uint64_t kth_largest(const Visit &visit, int k, uint6
         shift -= width;
         const uint32_t dmask = (1u << width) - 1u;
         // thread t counts digit (RBINS - 1 - t): thread order = descending digit
-        sh.tile[tid] = 0u;
-        __syncthreads();
         visit([&](uint64_t key) {
             if ((key & mask) == prefix)
                 atomicAdd(&sh.tile[RBINS - 1 - (int)((key >> shift) & dmask)], 1u);
         });
         __syncthreads();
         const uint32_t c = sh.tile[tid];
+        sh.tile[tid] = 0u;   // ordered before the next pass by the scan's barriers
         uint32_t tot;
         const uint32_t incl = block_incl_scan<T3>(c, sh.w, &tot);
         const uint32_t above = incl - c;
@@ -727,10 +727,8 @@ __device__ __forceinline__ uint64_t kth_largest(const Visit &visit, int k, uint6
         mask |= (uint64_t)dmask << shift;
         k = sh.sel[1];
         grp = sh.sel[2];
-        __syncthreads();
+        // sh.sel is written next only after the next pass's barriers
     }
-    if (tid == 0) sh.ng = 0u;
-    __syncthreads();
     visit([&](uint64_t key) {
         if ((key & mask) == prefix) {
             const uint32_t slot = atomicAdd(&sh.ng, 1u);
@@ -901,6 +899,8 @@ __global__ __launch_bounds__(T3) void thr_kernel(
                         }
                     }
                 }
+                s_k.tile[tid] = 0u;   // the exact select's state, zero on entry
+                if (tid == 0) s_k.ng = 0u;
                 __syncthreads();
                 auto visit_cand = [&](auto f) {
                     for (int i = tid; i < (int)nc; i += T3)
@@ -975,6 +975,9 @@ __global__ __launch_bounds__(T3) void thr_kernel(
                     for (int t = a + tid; t < z; t += T3) f(pooled_key(sk, a - r, t, g.e0, g.e1, r));
                 }
             };
+            s_k.tile[tid] = 0u;   // the exact select's state, zero on entry
+            if (tid == 0) s_k.ng = 0u;
+            __syncthreads();
             const uint64_t kth = kth_largest(visit_all, g.need, 0ull, 0ull, 64, nE, s_k);
             uint32_t *bm = bitmap + (size_t)seg * nwords;
             const int lane = tid & 63, wave = tid >> 6;
