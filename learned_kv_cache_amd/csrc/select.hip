@@ -127,8 +127,10 @@ __device__ __forceinline__ int key_token(uint64_t key) {
 }
 
 // Inclusive prefix sum over the threads of the block (thread order). s_w
-// holds NT / 64 slots. Two barriers; s_w may be reused after return.
-template <int NT>
+// holds NT / 64 slots. Two barriers, and s_w may be reused after return;
+// with TRAIL false only the first, and the caller must pass another barrier
+// before s_w is written again.
+template <int NT, bool TRAIL = true>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *s_w, uint32_t *total) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -147,7 +149,7 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *s_w, u
         before += w < wave ? t : 0u;
         tot += t;
     }
-    __syncthreads();
+    if constexpr (TRAIL) __syncthreads();
     *total = tot;
     return before + x;
 }
@@ -210,7 +212,8 @@ __device__ __forceinline__ void band_edges(const uint32_t (&v)[PER], int n, int 
             sum += c[u];
         }
         uint32_t tot;
-        uint32_t run = block_incl_scan<T3>(sum, s_w, &tot) - sum;
+        // s_w is written next after the barrier below
+        uint32_t run = block_incl_scan<T3, false>(sum, s_w, &tot) - sum;
 #pragma unroll
         for (int u = 0; u < PB; ++u) {
             const int d = QBINS - 1 - (tid * PB + u);
@@ -715,7 +718,8 @@ __device__ __forceinline__ uint64_t kth_largest(const Visit &visit, int k, uint6
         const uint32_t c = sh.tile[tid];
         sh.tile[tid] = 0u;   // ordered before the next pass by the scan's barriers
         uint32_t tot;
-        const uint32_t incl = block_incl_scan<T3>(c, sh.w, &tot);
+        // sh.w is written next after the barrier below
+        const uint32_t incl = block_incl_scan<T3, false>(c, sh.w, &tot);
         const uint32_t above = incl - c;
         if (c > 0 && above < (uint32_t)k && (uint32_t)k <= incl) {
             sh.sel[0] = RBINS - 1 - tid;
