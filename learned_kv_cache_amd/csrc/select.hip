@@ -576,6 +576,18 @@ __global__ __launch_bounds__(T1) void classify_kernel(
     uint32_t nc_w = 0, na_w = 0;   // this wave's candidates and above-band tokens
     uint64_t keys[NIT];
     bool sels[NIT], iscs[NIT];
+    // with the radius fixed, every lane forms its NIT keys from the staged
+    // slots (all written when the chunk is touched) in one branch-free loop,
+    // so their LDS reads are issued together; tokens outside E drop them
+    if constexpr (R >= 0) {
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) keys[it] = 0;
+        if (touch) {
+#pragma unroll
+            for (int it = 0; it < NIT; ++it)
+                keys[it] = pooled_key_r<R>(sk, lo, c0 + wave * 64 + it * T1 + lane);
+        }
+    }
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
         const int t = c0 + wave * 64 + it * T1 + lane;
@@ -585,7 +597,7 @@ __global__ __launch_bounds__(T1) void classify_kernel(
             if (all) {
                 sel = true;
             } else if (touch) {
-                if constexpr (R >= 0) key = pooled_key_r<R>(sk, lo, t);
+                if constexpr (R >= 0) key = keys[it];
                 else key = pooled_key(sk, lo, t, g.e0, g.e1, r);
                 const uint32_t k32 = (uint32_t)(key >> 32);
                 sel = k32 > thi;
