@@ -315,6 +315,22 @@ def test_select_threshold_staging_beyond_prefetched_slots(tb, orc, r):
     assert (cc.max(axis=1) > 96).all() and (cc.sum(axis=1) <= 8192).all(), cc
 
 
+def test_select_threshold_candidates_beyond_lds(tb, orc):
+    """At most 32 chunks but more candidates than the threshold launch holds
+    in LDS (three score values, about 20 K tokens tied on the budget's one):
+    the candidates are then read from global memory, not staged; the lists
+    must still equal the oracle's."""
+    rng = rng_for(61)
+    B, Hq, L, S, W, K = 1, 2, 60000, 16, 64, 30000
+    s = integer_scores(rng, (B, Hq, L), -1, 2)
+    ws = assert_same_selection(orc, tb, s, [L], [L], S, W, K, 0, "candidates beyond LDS")
+    up = lambda x: (x + 255) // 256 * 256
+    nseg, nchunks = B * Hq, -(-L // 2048)
+    off = up(nseg * 4) + up(nseg * 8)
+    cc = host(ws[off: off + nseg * nchunks * 4].view(torch.int32)).reshape(nseg, nchunks)
+    assert nchunks <= 32 and (cc.sum(axis=1) > 8192).all(), cc.sum(axis=1)
+
+
 # ------------------------------------------------- selection, dilation mode
 
 @pytest.mark.parametrize("r", [0, 1, 2])
