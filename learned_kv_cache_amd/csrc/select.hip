@@ -40,149 +40,22 @@
 // list rows it attends.
 #include "attn_impl.h"
 #include "score_impl.h"
+#include "select_impl.h"
 
 namespace tb {
 namespace {
 
-constexpr int CHUNK = 2048;          // tokens per classify workgroup
+using namespace sel;
+
 constexpr int T1 = 256;              // threads of classify
 constexpr int NSAMP = 8192;          // sample keys per segment (at most)
 constexpr int BG = 8;                // bounds workgroups per segment
 constexpr int QB = 12;               // bits per level of the band's histograms
 constexpr int QBINS = 1 << QB;
 constexpr float MARGIN_SIGMAS = 5.f; // half-width of the band in sample-rank std
-constexpr int MAXR = 64;
 constexpr int T3 = 1024;             // threads of the bounds and threshold kernels
 constexpr int LDS_CAND = 8192;       // candidates held in LDS by the threshold kernel
-constexpr int RBITS = 10;            // radix digit of the exact select
-constexpr int RBINS = 1 << RBITS;
-constexpr int GMAX = 64;             // boundary group size ranked directly
 constexpr int MAX_CHUNKS = (1 << 24) / CHUNK;   // chunks of the largest Lmax
-
-struct Region {
-    int L, P, e0, e1, need;
-    bool bad;
-};
-
-__device__ __forceinline__ Region region(const int32_t *ctx, const int32_t *plen, int b, int Lmax,
-                                         int S, int W, int K) {
-    Region g;
-    g.L = ctx[b];
-    g.P = plen[b];
-    g.bad = g.L < 0 || g.L > Lmax || g.P < 0 || g.P > Lmax;
-    g.e0 = S;
-    int e1 = g.L - W < g.P ? g.L - W : g.P;
-    g.e1 = e1 < S ? S : e1;
-    const int nE = g.e1 - g.e0;
-    g.need = K < nE ? K : nE;
-    return g;
-}
-
-// Stage order keys of scores for positions [lo, hi) (clipped to [e0, e1))
-// into LDS; slot i holds position lo + i. All loads of a thread are issued
-// before any is consumed.
-template <int NT>
-__device__ __forceinline__ void stage_keys(uint32_t *sk, const float *s, int lo, int hi, int e0,
-                                           int e1) {
-    constexpr int PER = (CHUNK + 2 * MAXR + NT - 1) / NT;
-    float v[PER];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int t = lo + (int)threadIdx.x + k * NT;
-        v[k] = (t < hi && t >= e0 && t < e1) ? s[t] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-        const int i = (int)threadIdx.x + k * NT;
-        const int t = lo + i;
-        if (t < hi) sk[i] = (t >= e0 && t < e1) ? order_key(v[k]) : 0u;
-    }
-}
-
-// Pooled key of eligible token t (slot base = lo).
-__device__ __forceinline__ uint64_t pooled_key(const uint32_t *sk, int lo, int t, int e0, int e1,
-                                               int r) {
-    const int a = t - r < e0 ? e0 : t - r;
-    const int z = t + r >= e1 ? e1 - 1 : t + r;
-    uint32_t best = sk[a - lo];
-    int c = a;
-    for (int u = a + 1; u <= z; ++u) {
-        const uint32_t k = sk[u - lo];
-        if (k > best) {
-            best = k;
-            c = u;
-        }
-    }
-    const int d = t < c ? c - t : t - c;
-    const uint32_t low = ((uint32_t)(0xffffff - c) << 8) | ((uint32_t)(0x7f - d) << 1) |
-                         (uint32_t)(t <= c ? 1 : 0);
-    return ((uint64_t)best << 32) | low;
-}
-
-__device__ __forceinline__ int key_token(uint64_t key) {
-    const uint32_t low = (uint32_t)key;
-    const int c = 0xffffff - (int)(low >> 8);
-    const int d = 0x7f - (int)((low >> 1) & 0x7f);
-    return (low & 1u) ? c - d : c + d;
-}
-
-// Inclusive prefix sum over the threads of the block (thread order). s_w
-// holds NT / 64 slots. Two barriers, and s_w may be reused after return;
-// with TRAIL false only the first, and the caller must pass another barrier
-// before s_w is written again.
-template <int NT, bool TRAIL = true>
-__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *s_w, uint32_t *total) {
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    if (lane == 63) s_w[wave] = x;
-    __syncthreads();
-    uint32_t before = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const uint32_t t = s_w[w];
-        before += w < wave ? t : 0u;
-        tot += t;
-    }
-    if constexpr (TRAIL) __syncthreads();
-    *total = tot;
-    return before + x;
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave (lane order).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
-
-// Pooled key of eligible token t read straight from the scores (global).
-__device__ __forceinline__ uint64_t pooled_key_g(const float *s, int t, int e0, int e1, int r) {
-    const int a = t - r < e0 ? e0 : t - r;
-    const int z = t + r >= e1 ? e1 - 1 : t + r;
-    uint32_t best = order_key(s[a]);
-    int c = a;
-    for (int u = a + 1; u <= z; ++u) {
-        const uint32_t k = order_key(s[u]);
-        if (k > best) {
-            best = k;
-            c = u;
-        }
-    }
-    const int d = t < c ? c - t : t - c;
-    const uint32_t low = ((uint32_t)(0xffffff - c) << 8) | ((uint32_t)(0x7f - d) << 1) |
-                         (uint32_t)(t <= c ? 1 : 0);
-    return ((uint64_t)best << 32) | low;
-}
 
 // Band edges from the n sample keys held PER to a thread (key i * T3 + tid in
 // v[i], zero past n): t_hi >= the key of rank ka and t_lo <= the key of rank
@@ -495,30 +368,6 @@ score_bounds_fn score_bounds_pick(int g) {
     }
 }
 
-// Pooled key of eligible token t with the radius fixed at compile time: the
-// 2R + 1 staged keys are read together (slots outside E hold 0, below the key
-// of every finite score), and the first maximum in position order is the
-// centre -- the same key as pooled_key.
-template <int R>
-__device__ __forceinline__ uint64_t pooled_key_r(const uint32_t *sk, int lo, int t) {
-    uint32_t k[2 * R + 1];
-#pragma unroll
-    for (int u = 0; u <= 2 * R; ++u) k[u] = sk[t - R + u - lo];
-    uint32_t best = 0u;
-    int c = t;
-#pragma unroll
-    for (int u = 0; u <= 2 * R; ++u) {
-        if (k[u] > best) {
-            best = k[u];
-            c = t - R + u;
-        }
-    }
-    const int d = t < c ? c - t : t - c;
-    const uint32_t low = ((uint32_t)(0xffffff - c) << 8) | ((uint32_t)(0x7f - d) << 1) |
-                         (uint32_t)(t <= c ? 1 : 0);
-    return ((uint64_t)best << 32) | low;
-}
-
 // R >= 0: the radius is R (pooled keys read their neighbours together);
 // R < 0: any radius, neighbours read one by one. Each wave handles CHUNK /
 // waves tokens and keeps its candidates in its own LDS region, so no slot is
@@ -646,123 +495,6 @@ __global__ __launch_bounds__(T1) void classify_kernel(
         if (c0 + (int)(before + i) < Lmax) cl[before + i] = wcand[i];
 }
 
-// Position of the k-th (0-based) set bit of v; requires k < popcount(v).
-__device__ __forceinline__ int select_bit(uint32_t v, uint32_t k) {
-    int pos = 0;
-    uint32_t c = (uint32_t)__popc(v & 0xffffu);
-    if (k >= c) { k -= c; pos += 16; v >>= 16; }
-    c = (uint32_t)__popc(v & 0xffu);
-    if (k >= c) { k -= c; pos += 8; v >>= 8; }
-    c = (uint32_t)__popc(v & 0xfu);
-    if (k >= c) { k -= c; pos += 4; v >>= 4; }
-    c = (uint32_t)__popc(v & 0x3u);
-    if (k >= c) { k -= c; pos += 2; v >>= 2; }
-    if (k >= (v & 1u)) pos += 1;
-    return pos;
-}
-
-__device__ __forceinline__ uint32_t bits_below(int n) {
-    return n <= 0 ? 0u : (n >= 32 ? 0xffffffffu : ((1u << n) - 1u));
-}
-
-// Chunk holding candidate i of the segment (chunk-major order): the last
-// chunk c with off[c] <= i; chunk c holds entries [off[c], off[c+1]).
-__device__ __forceinline__ int chunk_of(const uint32_t *s_off, int nchunks, uint32_t i) {
-    int lo = 0, hi = nchunks - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_off[mid] <= i) lo = mid;
-        else hi = mid - 1;
-    }
-    return lo;
-}
-
-// Candidate i of the segment, read from its chunk's slots.
-__device__ __forceinline__ uint64_t cand_at(const uint64_t *cl, const uint32_t *s_off, int nchunks,
-                                            uint32_t i) {
-    const int c = chunk_of(s_off, nchunks, i);
-    return cl[(size_t)c * CHUNK + (i - s_off[c])];
-}
-
-// How many of the tokens [t0, t1) lie in sink [0, slo) U window [wlo, L)
-// (the two ranges may overlap in short contexts).
-__device__ __forceinline__ int fixed_in(int t0, int t1, int slo, int wlo, int L) {
-    const int e = t1 < L ? t1 : L;
-    int n = 0;
-    if (t0 < slo) n += (e < slo ? e : slo) - t0;
-    int w0 = wlo > slo ? wlo : slo;
-    w0 = w0 > t0 ? w0 : t0;
-    if (e > w0) n += e - w0;
-    return n > 0 ? n : 0;
-}
-
-struct KthLds {
-    uint32_t tile[RBINS];
-    uint64_t grp[GMAX];
-    uint32_t w[T3 / 64];
-    int sel[3];
-    uint32_t ng;
-    uint64_t thr;
-};
-
-// The k-th largest (1 <= k <= count) of distinct 64-bit keys that all carry
-// `prefix` on `mask` (every bit at or above `shift`). visit(f) hands each key
-// to f exactly once, from any thread; every thread calls it and it may hold
-// barriers. grp: how many keys carry the prefix (anything above GMAX when
-// unknown). 10-bit radix passes narrow the group to at most GMAX keys, which
-// are ranked directly. sh.tile and sh.ng are zero on entry (cleared by the
-// caller before a barrier); each pass clears its bins again as it reads them.
-template <class Visit>
-__device__ __forceinline__ uint64_t kth_largest(const Visit &visit, int k, uint64_t prefix,
-                                                uint64_t mask, int shift, int grp, KthLds &sh) {
-    static_assert(RBINS == T3, "one radix bin per thread");
-    const int tid = threadIdx.x;
-    while (grp > GMAX && shift > 0) {
-        const int width = shift < RBITS ? shift : RBITS;
-        shift -= width;
-        const uint32_t dmask = (1u << width) - 1u;
-        // thread t counts digit (RBINS - 1 - t): thread order = descending digit
-        visit([&](uint64_t key) {
-            if ((key & mask) == prefix)
-                atomicAdd(&sh.tile[RBINS - 1 - (int)((key >> shift) & dmask)], 1u);
-        });
-        __syncthreads();
-        const uint32_t c = sh.tile[tid];
-        sh.tile[tid] = 0u;   // ordered before the next pass by the scan's barriers
-        uint32_t tot;
-        // sh.w is written next after the barrier below
-        const uint32_t incl = block_incl_scan<T3, false>(c, sh.w, &tot);
-        const uint32_t above = incl - c;
-        if (c > 0 && above < (uint32_t)k && (uint32_t)k <= incl) {
-            sh.sel[0] = RBINS - 1 - tid;
-            sh.sel[1] = k - (int)above;
-            sh.sel[2] = (int)c;
-        }
-        __syncthreads();
-        prefix |= (uint64_t)sh.sel[0] << shift;
-        mask |= (uint64_t)dmask << shift;
-        k = sh.sel[1];
-        grp = sh.sel[2];
-        // sh.sel is written next only after the next pass's barriers
-    }
-    visit([&](uint64_t key) {
-        if ((key & mask) == prefix) {
-            const uint32_t slot = atomicAdd(&sh.ng, 1u);
-            if (slot < (uint32_t)GMAX) sh.grp[slot] = key;
-        }
-    });
-    __syncthreads();
-    const int ng = sh.ng < (uint32_t)GMAX ? (int)sh.ng : GMAX;
-    if (tid < ng) {
-        const uint64_t mine = sh.grp[tid];
-        int rank = 0;
-        for (int j = 0; j < ng; ++j) rank += sh.grp[j] > mine ? 1 : 0;
-        if (rank == k - 1) sh.thr = mine;
-    }
-    __syncthreads();
-    return sh.thr;
-}
-
 // One workgroup per segment. With A tokens above the band and C candidates
 // in it, the band holds the budget's key iff 0 <= need - A <= C; then the
 // (need - A)-th largest candidate is the threshold and every chunk's output
@@ -781,7 +513,7 @@ __global__ __launch_bounds__(T3) void thr_kernel(
     __shared__ uint16_t s_cc[LDS_CAND];          // chunk of each LDS candidate
     __shared__ uint32_t s_off[MAX_CHUNKS];
     __shared__ uint32_t s_chosen[MAX_CHUNKS];
-    __shared__ KthLds s_k;
+    __shared__ KthLds<T3> s_k;
     __shared__ uint32_t s_tot[2];
 
     const int seg = blockIdx.x, b = seg / Hq;
@@ -1135,25 +867,28 @@ __global__ __launch_bounds__(64) void compact_kernel(
     uint64_t thr = 0;
     if (partial) {
         thr = thr_raw;
-        n = thr == ~0ull ? 0u : nraw;
+        n = thr == ~0ull ? 0u : (nraw < (uint32_t)CHUNK ? nraw : (uint32_t)CHUNK);
     }
     bits |= bits_below(slo - t0);
     bits |= bits_below(L - t0) & ~bits_below(wlo - t0);
     bits &= bits_below(L - t0);
     s_word[lane] = bits;
     __syncthreads();
+    // a candidate's position lies in its chunk after the selection this call
+    // follows; anything else (a state left by another call sequence) is
+    // ignored rather than written outside the chunk
 #pragma unroll
     for (int k = 0; k < PF; ++k) {
         if ((uint32_t)(lane + 64 * k) < n && pk[k] >= thr) {
             const int t = key_token(pk[k]) - c * CHUNK;
-            atomicOr(&s_word[t >> 5], 1u << (t & 31));
+            if ((uint32_t)t < (uint32_t)CHUNK) atomicOr(&s_word[t >> 5], 1u << (t & 31));
         }
     }
-    for (uint32_t i = lane + 64 * PF; i < n; i += 64) {
+    for (uint32_t i = lane + 64 * PF; i < n && c * CHUNK + (int)i < Lmax; i += 64) {
         const uint64_t key = cl[i];
         if (key >= thr) {
             const int t = key_token(key) - c * CHUNK;
-            atomicOr(&s_word[t >> 5], 1u << (t & 31));
+            if ((uint32_t)t < (uint32_t)CHUNK) atomicOr(&s_word[t >> 5], 1u << (t & 31));
         }
     }
     __syncthreads();
@@ -1363,9 +1098,10 @@ __global__ __launch_bounds__(64) void dilate_kernel(
     if (thr != ~0ull) {
         for (int cc = c - 1; cc <= c + 1; ++cc) {
             if (cc < 0 || cc >= nchunks) continue;
-            const uint32_t n = ccount[(size_t)seg * nchunks + cc];
+            uint32_t n = ccount[(size_t)seg * nchunks + cc];
+            n = n < (uint32_t)CHUNK ? n : (uint32_t)CHUNK;
             const uint64_t *cl = cand + (size_t)seg * Lmax + (size_t)cc * CHUNK;
-            for (uint32_t i = lane; i < n; i += 64) {
+            for (uint32_t i = lane; i < n && cc * CHUNK + (int)i < Lmax; i += 64) {
                 const uint64_t key = cl[i];
                 if (key >= thr) {
                     const int t = key_token(key);
