@@ -25,9 +25,10 @@
  *  - Host-side arguments are validated before anything is enqueued; on any
  *    error the call returns a non-zero tb_status and enqueues nothing.
  *    Device-resident lengths are checked by the kernels where noted.
- *  - The library keeps no mutable global state; calls are reentrant. Calls
- *    that share a workspace must be ordered on one stream (they race
- *    otherwise).
+ *  - The library keeps no mutable global state (the one exception is the
+ *    fixed scratch array of tb_sparse_decode_attn_noalloc); calls are
+ *    reentrant. Calls that share a workspace must be ordered on one stream
+ *    (they race otherwise).
  *  - Workspaces: size them with the matching *_workspace_bytes() query and
  *    zero-fill them once before first use (e.g. torch.zeros). Every call
  *    that takes a workspace leaves whatever must start at zero (the
@@ -326,6 +327,27 @@ tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *
                                 const int32_t *ctx_len, int window,
                                 int B, int Hq, int Hkv, int Lmax, int D, float scale,
                                 float *out, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * tb_sparse_decode_attn for callers that cannot allocate device memory (code
+ * under graph capture that must not call hipMalloc, tight serving loops,
+ * harnesses that forbid allocation): the same computation, arguments and
+ * results as tb_sparse_decode_attn, without the workspace. The split partials
+ * and arrival counters live in a fixed 8 MiB device array per GPU, held until
+ * the process ends: counters of up to 65536 heads (B * Hq) and at most
+ * 8 MiB - 256 KiB of partials, i.e. B * Hq * ceil((cap + window) / 256) *
+ * (D + 2) * 4 bytes; larger calls return TB_ERR_UNSUPPORTED_SHAPE and enqueue
+ * nothing. Every call on a GPU shares that GPU's array: calls that may
+ * overlap on one GPU (several streams, several threads) race and give
+ * unspecified results; order them on one stream. The call allocates nothing;
+ * on its first use on a device it looks up the array's address (and, outside
+ * a graph capture, clears its counters with a small kernel on `stream`).
+ */
+tb_status tb_sparse_decode_attn_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                                        const int32_t *idx, const int32_t *count, int cap,
+                                        const int32_t *ctx_len, int window,
+                                        int B, int Hq, int Hkv, int Lmax, int D, float scale,
+                                        float *out, void *stream);
 
 #ifdef __cplusplus
 }

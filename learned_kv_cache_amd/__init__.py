@@ -90,6 +90,9 @@ def lib():
     L.tb_sparse_decode_attn.restype = _i
     L.tb_sparse_decode_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i,
                                         ctypes.c_float, _vp, _vp, _sz, _vp]
+    L.tb_sparse_decode_attn_noalloc.restype = _i
+    L.tb_sparse_decode_attn_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i,
+                                                _i, _i, ctypes.c_float, _vp, _vp]
     _lib = L
     return L
 
@@ -390,4 +393,25 @@ def tb_sparse_decode_attn(q, k_cache, v_cache, idx, count, out, workspace, scale
                                        _ptr(count, torch.int32, "count", 2), cap, ctx, int(window),
                                        B, Hq, Hkv, Lmax, D, float(scale), _ptr(out, torch.float32, "out", 3),
                                        wp, wn, _stream(stream)))
+    return out
+
+
+def tb_sparse_decode_attn_noalloc(q, k_cache, v_cache, idx, count, out, scale=None, ctx_len=None,
+                                  window=0, stream=None):
+    """tb_sparse_decode_attn without a workspace: the library's fixed per-GPU
+    scratch array holds the partials (calls that overlap on one GPU race)."""
+    B, Hkv, Lmax, D = k_cache.shape
+    Hq = q.shape[1]
+    cap = idx.shape[-1]
+    if (tuple(q.shape) != (B, Hq, D) or tuple(v_cache.shape) != (B, Hkv, Lmax, D)
+            or tuple(idx.shape) != (B, Hq, cap) or tuple(out.shape) != (B, Hq, D)):
+        raise ValueError("tb_sparse_decode_attn_noalloc: shape mismatch")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    ctx = None if ctx_len is None else _ptr(ctx_len, torch.int32, "ctx_len")
+    _check(lib().tb_sparse_decode_attn_noalloc(
+        _ptr(q, torch.bfloat16, "q", 3), _ptr(k_cache, torch.bfloat16, "k_cache", 4),
+        _ptr(v_cache, torch.bfloat16, "v_cache", 4), _ptr(idx, torch.int32, "idx", 3),
+        _ptr(count, torch.int32, "count", 2), cap, ctx, int(window), B, Hq, Hkv, Lmax, D,
+        float(scale), _ptr(out, torch.float32, "out", 3), _stream(stream)))
     return out
