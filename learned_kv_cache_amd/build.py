@@ -21,20 +21,35 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose=False):
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + ["-o", tmp] + srcs
+NOISE = "packed-fp32-ops' is not a recognized feature"
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    err = "\n".join(l for l in r.stderr.splitlines() if NOISE not in l)
     if r.returncode != 0:
         sys.stderr.write(err + "\n")
-        raise RuntimeError("hipcc failed building libtb.so")
+        raise RuntimeError("hipcc failed: %s" % " ".join(cmd[-3:]))
     if err.strip() and verbose:
         sys.stderr.write(err + "\n")
+
+
+def build(verbose=False, jobs=None):
+    """Compile every csrc/*.hip to an object (in parallel), then link libtb.so."""
+    from concurrent.futures import ThreadPoolExecutor
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2) - 1), 8)
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _run([hipcc()] + flags + ["-c", so[0], "-o", so[1]], verbose),
+                    zip(srcs, objs)))
+    tmp = LIB + ".tmp"
+    _run([hipcc()] + HIPCC_FLAGS + ["-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
     return LIB
 

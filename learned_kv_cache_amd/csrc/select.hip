@@ -508,7 +508,7 @@ __global__ __launch_bounds__(T3) void thr_kernel(
     int omit_window, const uint32_t *__restrict__ info, const uint32_t *__restrict__ ccount,
     const uint32_t *__restrict__ acount, int nchunks, const uint64_t *__restrict__ cand,
     uint32_t *__restrict__ bitmap, int nwords, uint64_t *__restrict__ thr_out,
-    uint32_t *__restrict__ coff, int32_t *__restrict__ count) {
+    uint32_t *__restrict__ coff, int32_t *__restrict__ count, uint32_t *__restrict__ hist) {
     __shared__ uint64_t s_cand[LDS_CAND];
     __shared__ uint16_t s_cc[LDS_CAND];          // chunk of each LDS candidate
     __shared__ uint32_t s_off[MAX_CHUNKS];
@@ -518,6 +518,13 @@ __global__ __launch_bounds__(T3) void thr_kernel(
 
     const int seg = blockIdx.x, b = seg / Hq;
     const int tid = threadIdx.x;
+    if (hist != nullptr) {
+        // after the histogram route: its histogram back to zero for the next
+        // call (the classification launch before this one has read it)
+        uint4 *hz = reinterpret_cast<uint4 *>(hist + (size_t)seg * 4096);
+        hz[tid] = make_uint4(0, 0, 0, 0);
+        static_assert(T3 * 4 == 4096, "one 16-byte store per thread");
+    }
     constexpr int PC = MAX_CHUNKS / T3;
     // chunk c's counts sit in thread c / PC: with at most 64 PC chunks they
     // all sit in wave 0, whose shuffles then replace the block-wide scans
@@ -1185,6 +1192,7 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
     const size_t samp_b = up(nseg * (size_t)NSAMP * 4);
     const size_t dbm_b = bm_b;
     const size_t dc_b = cc_b;
+    const size_t hist_b = up(hist_ws_bytes(B, Hq, Lmax));
     if (base && out) {
         char *p = static_cast<char *>(base);
         out->bctr = reinterpret_cast<uint32_t *>(p);
@@ -1208,13 +1216,24 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
         out->dbm = reinterpret_cast<uint32_t *>(p);
         p += dbm_b;
         out->dcount = reinterpret_cast<uint32_t *>(p);
+        p += dc_b;
+        out->hist = hist_b ? reinterpret_cast<uint32_t *>(p) : nullptr;
         out->nwords = nwords;
         out->nchunks = nchunks;
     }
-    return bctr_b + info_b + 3 * cc_b + thr_b + bm_b + cand_b + samp_b + dbm_b + dc_b;
+    return bctr_b + info_b + 3 * cc_b + thr_b + bm_b + cand_b + samp_b + dbm_b + dc_b + hist_b;
 }
 
 namespace {
+
+tb_status launch_after_thr(const int32_t *ctx, const int32_t *plen, int B, int Hq, int Lmax,
+                           int S, int W, int K, int r, bool dilate, bool omit_window,
+                           int32_t *idx, int32_t *count, int cap, const SelectWs &ws,
+                           hipStream_t st, bool defer_list);
+tb_status launch_thr_after(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
+                           int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
+                           bool omit_window, int32_t *idx, int32_t *count, int cap,
+                           const SelectWs &ws, hipStream_t st, bool defer_list, uint32_t *hist);
 
 // classify, threshold, then compaction (or dilation and emission): every
 // launch of the selection after the band.
@@ -1229,13 +1248,37 @@ tb_status launch_after_band(const float *scores, const int32_t *ctx, const int32
                                              : rk == 2 ? classify_kernel<2> : classify_kernel<-1>;
     hipLaunchKernelGGL(classify, grid, dim3(T1), 0, st, scores, ctx, plen, Hq, Lmax, S, W, K, rk,
                        ws.info, ws.ccount, ws.acount, ws.nchunks, ws.cand, ws.bitmap, ws.nwords);
-    tb_status e = check_launch("tb_select(classify)");
+    const tb_status e = check_launch("tb_select(classify)");
     if (e) return e;
+    return launch_thr_after(scores, ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window, idx,
+                            count, cap, ws, st, defer_list, nullptr);
+}
+
+// threshold (clearing the histogram of the histogram route when hist is
+// given), then the list.
+tb_status launch_thr_after(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
+                           int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
+                           bool omit_window, int32_t *idx, int32_t *count, int cap,
+                           const SelectWs &ws, hipStream_t st, bool defer_list, uint32_t *hist) {
+    const int nseg = B * Hq;
+    const int rk = dilate ? 0 : r;
     hipLaunchKernelGGL(thr_kernel, dim3(nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
                        K, rk, omit_window ? 1 : 0, ws.info, ws.ccount, ws.acount, ws.nchunks,
-                       ws.cand, ws.bitmap, ws.nwords, ws.thr, ws.coff, count);
-    e = check_launch("tb_select(threshold)");
+                       ws.cand, ws.bitmap, ws.nwords, ws.thr, ws.coff, count, hist);
+    const tb_status e = check_launch("tb_select(threshold)");
     if (e) return e;
+    return launch_after_thr(ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window, idx, count,
+                            cap, ws, st, defer_list);
+}
+
+// compaction (or dilation and emission) after the threshold: the list.
+tb_status launch_after_thr(const int32_t *ctx, const int32_t *plen, int B, int Hq, int Lmax,
+                           int S, int W, int K, int r, bool dilate, bool omit_window,
+                           int32_t *idx, int32_t *count, int cap, const SelectWs &ws,
+                           hipStream_t st, bool defer_list) {
+    const int nseg = B * Hq;
+    dim3 grid(ws.nchunks, nseg);
+    tb_status e;
     if (defer_list) return TB_OK;   // the list is written by tb_select_attn
     if (!dilate) {
         hipLaunchKernelGGL(compact_kernel, grid, dim3(64), 0, st, ctx, plen, Hq, Lmax, S, W, K,
@@ -1278,6 +1321,16 @@ tb_status launch_score_select(const float *qhat, int n_slots, int slot, const vo
                               int Hq, int Hkv, int Lmax, int dp, int S, int W, int K, int r,
                               bool dilate, bool omit_window, int32_t *idx, int32_t *count,
                               int cap, const SelectWs &ws, hipStream_t st, bool defer_list) {
+    if (hist_route_fits(Lmax, Hq / Hkv, r, dilate) && ws.hist) {
+        // scoring with an exact histogram of the pooled keys, then
+        // classification against the bin that holds the budget's key
+        const tb_status e = launch_score_hist_classify(qhat, n_slots, slot, kp, ctx, plen, scores,
+                                                       B, Hq, Hkv, Lmax, dp, S, W, K, r, dilate,
+                                                       ws, st);
+        if (e) return e;
+        return launch_thr_after(scores, ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window,
+                                idx, count, cap, ws, st, defer_list, ws.hist);
+    }
     const int rk = dilate ? 0 : r;
     const int g = Hq / Hkv;
     const int nsb = BG * B * Hq;

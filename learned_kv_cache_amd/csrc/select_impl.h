@@ -279,11 +279,19 @@ __device__ __forceinline__ uint64_t kth_largest(const Visit &visit, int k, uint6
     });
     __syncthreads();
     const int ng = sh.ng < (uint32_t)GMAX ? (int)sh.ng : GMAX;
-    if (tid < ng) {
-        const uint64_t mine = sh.grp[tid];
+    if (tid < 64) {
+        // wave 0 ranks the group: lane l holds key l, and every key is read
+        // from its lane in turn (register reads, no LDS round trip per key)
+        const uint64_t mine = tid < ng ? sh.grp[tid] : 0ull;
+        const uint32_t mlo = (uint32_t)mine, mhi = (uint32_t)(mine >> 32);
         int rank = 0;
-        for (int j = 0; j < ng; ++j) rank += sh.grp[j] > mine ? 1 : 0;
-        if (rank == k - 1) sh.thr = mine;
+        for (int j = 0; j < ng; ++j) {
+            const uint64_t o =
+                ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mhi, j) << 32) |
+                (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)mlo, j);
+            rank += o > mine ? 1 : 0;
+        }
+        if (tid < ng && rank == k - 1) sh.thr = mine;
     }
     __syncthreads();
     return sh.thr;

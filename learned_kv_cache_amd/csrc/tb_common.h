@@ -113,10 +113,23 @@ struct SelectWs {
     uint32_t *samp;      // [nseg][8192] sampled pooled key32
     uint32_t *dbm;       // [nseg][nwords] widened bitmap (dilation mode)
     uint32_t *dcount;    // [nseg][nchunks] widened tokens per chunk (dilation mode)
+    uint32_t *hist;      // [nseg][4096] threshold histogram, zero at rest (null when
+                         // Lmax <= kHistMinL)
     int nwords;
     int nchunks;
 };
 size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out);
+// The histogram route of tb_score_select (select_hist.hip): contexts above
+// kHistMinL tokens (below it the sampled band holds every token and is exact)
+// up to 64 chunks of 2048 tokens, radius <= 2 (0 in the dilation mode), at
+// most 4 query heads per KV head.
+constexpr int kHistMinL = 8192;
+bool hist_route_fits(int Lmax, int g, int r, bool dilate);
+size_t hist_ws_bytes(int B, int Hq, int Lmax);
+tb_status launch_score_hist_classify(const float *qhat, int n_slots, int slot, const void *kp,
+                                     const int32_t *ctx, const int32_t *plen, float *scores,
+                                     int B, int Hq, int Hkv, int Lmax, int dp, int S, int W, int K,
+                                     int r, bool dilate, const SelectWs &ws, hipStream_t st);
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
                         int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
                         bool omit_window, int32_t *idx, int32_t *count, int cap,
