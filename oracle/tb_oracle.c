@@ -1,11 +1,14 @@
 /*
  * TokenButler decode-path ORACLE -- test infrastructure only.
  *
- * A plain, slow, single-threaded CPU implementation of what the decode-time
- * hot path computes, written from the method description in "TokenButler"
- * (technical summary, sections "Core architecture" and "Inference strategy").
- * It accumulates in double precision and applies exactly the storage
- * roundings listed below. Only the tests, the smoke check and the benchmark's
+ * A plain, slow CPU implementation of what the decode-time hot path
+ * computes, written from the method description in "TokenButler" (technical
+ * summary, sections "Core architecture" and "Inference strategy"). It
+ * accumulates in double precision and applies exactly the storage roundings
+ * listed below. Loops over independent outputs (hidden units, query heads,
+ * sequences) are spread over OpenMP threads when built with -fopenmp; every
+ * output is still computed by one thread in the order written here, so the
+ * results do not depend on the thread count. Only the tests, the smoke check and the benchmark's
  * cpu_baseline leg may load this library; the GPU library never does, and the
  * two share no code, header or table.
  *
@@ -27,10 +30,24 @@
  *
  * Parity pins for every function live in tests/test_oracle_*.py.
  */
+#define _GNU_SOURCE   /* qsort_r */
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the parallel loops use (1 without OpenMP). */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------ */
 /* IEEE-754 storage formats, written from their definitions.           */
@@ -129,12 +146,14 @@ void orc_predict_queries(const uint16_t *x, const uint16_t *w1, const uint16_t *
 {
     uint16_t *h = h_out ? h_out : (uint16_t *)malloc(sizeof(uint16_t) * (size_t)B * Eh);
     for (int b = 0; b < B; ++b) {
+#pragma omp parallel for schedule(static)
         for (int j = 0; j < Eh; ++j) {
             double z = 0.0;
             for (int i = 0; i < E; ++i)
                 z += bf16_value(x[(size_t)b * E + i]) * bf16_value(w1[(size_t)j * E + i]);
             h[(size_t)b * Eh + j] = bf16_bits_rne(silu(z));
         }
+#pragma omp parallel for schedule(static)
         for (int n = 0; n < Nout; ++n) {
             double acc = 0.0;
             for (int j = 0; j < Eh; ++j)
@@ -156,6 +175,7 @@ void orc_project_keys(const uint16_t *kc, const uint16_t *wk, uint16_t *kp,
                       const int *pos0, int ntok,
                       int B, int Hkv, int Lmax, int D, int dp)
 {
+#pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < B; ++b)
         for (int j = 0; j < Hkv; ++j)
             for (int t = pos0[b]; t < pos0[b] + ntok && t < Lmax; ++t) {
@@ -217,6 +237,7 @@ void orc_score(const float *qhat, int n_slots, int slot, const uint16_t *kp,
                int B, int Hq, int Hkv, int Lmax, int dp)
 {
     int g = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(static)
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < Hq; ++h) {
             const float *qv = qhat + (((size_t)b * n_slots + slot) * Hq + h) * dp;
@@ -241,7 +262,6 @@ void orc_score(const float *qhat, int n_slots, int slot, const uint16_t *kp,
 
 /* Candidate order: higher score first in IEEE totalOrder (so -0 ranks
  * below +0), and among equal scores the lower position first. */
-static const float *g_cmp_scores;
 
 static int score_above(float a, float b)
 {
@@ -250,10 +270,11 @@ static int score_above(float a, float b)
     return !signbit(a) && signbit(b);  /* +0 above -0 */
 }
 
-static int cmp_candidates(const void *pa, const void *pb)
+static int cmp_candidates(const void *pa, const void *pb, void *scores)
 {
     int a = *(const int *)pa, b = *(const int *)pb;
-    float sa = g_cmp_scores[a], sb = g_cmp_scores[b];
+    const float *s = (const float *)scores;
+    float sa = s[a], sb = s[b];
     if (score_above(sa, sb))
         return -1;
     if (score_above(sb, sa))
@@ -292,16 +313,16 @@ int orc_select(const float *scores, const int *ctx_len, const int *proj_len,
             e1 = e0;
         int nE = e1 - e0;
         int need = K < nE ? K : nE;
-        unsigned char *keep = (unsigned char *)calloc((size_t)(L > 0 ? L : 1), 1);
-        int *order = (int *)malloc(sizeof(int) * (size_t)(nE > 0 ? nE : 1));
+        int over = 0;   /* some head's count exceeded cap */
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : over)
         for (int h = 0; h < Hq; ++h) {
             const float *s = scores + ((size_t)b * Hq + h) * Lmax;
-            memset(keep, 0, (size_t)(L > 0 ? L : 1));
+            unsigned char *keep = (unsigned char *)calloc((size_t)(L > 0 ? L : 1), 1);
+            int *order = (int *)malloc(sizeof(int) * (size_t)(nE > 0 ? nE : 1));
 
             for (int i = 0; i < nE; ++i)
                 order[i] = e0 + i;
-            g_cmp_scores = s;
-            qsort(order, (size_t)nE, sizeof(int), cmp_candidates);
+            qsort_r(order, (size_t)nE, sizeof(int), cmp_candidates, (void *)s);
 
             int taken = 0;
             for (int i = 0; i < nE && taken < need; ++i) {
@@ -331,13 +352,15 @@ int orc_select(const float *scores, const int *ctx_len, const int *proj_len,
                     if (n < cap)
                         dst[n] = t;
                     else
-                        status = -1;
+                        over = 1;
                     ++n;
                 }
             count[(size_t)b * Hq + h] = n;
+            free(order);
+            free(keep);
         }
-        free(order);
-        free(keep);
+        if (over)
+            status = -1;
     }
     return status;
 }
@@ -374,16 +397,16 @@ int orc_select_dilate(const float *scores, const int *ctx_len, const int *proj_l
             e1 = e0;
         int nE = e1 - e0;
         int need = K < nE ? K : nE;
-        unsigned char *keep = (unsigned char *)calloc((size_t)(L > 0 ? L : 1), 1);
-        int *order = (int *)malloc(sizeof(int) * (size_t)(nE > 0 ? nE : 1));
+        int over = 0;   /* some head's count exceeded cap */
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : over)
         for (int h = 0; h < Hq; ++h) {
             const float *s = scores + ((size_t)b * Hq + h) * Lmax;
-            memset(keep, 0, (size_t)(L > 0 ? L : 1));
+            unsigned char *keep = (unsigned char *)calloc((size_t)(L > 0 ? L : 1), 1);
+            int *order = (int *)malloc(sizeof(int) * (size_t)(nE > 0 ? nE : 1));
 
             for (int i = 0; i < nE; ++i)
                 order[i] = e0 + i;
-            g_cmp_scores = s;
-            qsort(order, (size_t)nE, sizeof(int), cmp_candidates);
+            qsort_r(order, (size_t)nE, sizeof(int), cmp_candidates, (void *)s);
 
             for (int i = 0; i < need; ++i) {
                 int c = order[i];
@@ -404,13 +427,15 @@ int orc_select_dilate(const float *scores, const int *ctx_len, const int *proj_l
                     if (n < cap)
                         dst[n] = t;
                     else
-                        status = -1;
+                        over = 1;
                     ++n;
                 }
             count[(size_t)b * Hq + h] = n;
+            free(order);
+            free(keep);
         }
-        free(order);
-        free(keep);
+        if (over)
+            status = -1;
     }
     return status;
 }
@@ -488,15 +513,15 @@ void orc_sparse_attention(const uint16_t *q, const uint16_t *kc, const uint16_t 
                           float *out)
 {
     int g = Hq / Hkv;
-    double *z = NULL;
-    double *o = (double *)malloc(sizeof(double) * (size_t)D);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
     for (int b = 0; b < B; ++b)
         for (int h = 0; h < Hq; ++h) {
             int n = count[(size_t)b * Hq + h];
             const int *ix = idx + ((size_t)b * Hq + h) * cap;
             const uint16_t *qv = q + ((size_t)b * Hq + h) * D;
             int kvh = h / g;
-            z = (double *)realloc(z, sizeof(double) * (size_t)(n > 0 ? n : 1));
+            double *z = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+            double *o = (double *)malloc(sizeof(double) * (size_t)D);
             double m = -INFINITY;
             for (int i = 0; i < n; ++i) {
                 const uint16_t *kr = kc + (((size_t)b * Hkv + kvh) * Lmax + ix[i]) * D;
@@ -520,7 +545,7 @@ void orc_sparse_attention(const uint16_t *q, const uint16_t *kc, const uint16_t 
             float *dst = out + ((size_t)b * Hq + h) * D;
             for (int c = 0; c < D; ++c)
                 dst[c] = n > 0 ? (float)(o[c] / l) : 0.0f;
+            free(z);
+            free(o);
         }
-    free(z);
-    free(o);
 }

@@ -2,7 +2,14 @@
 and "Results": a synthetic co-referential retrieval task at 300 tokens where
 the method is near-oracle). Stand-in: three 4-token spans whose keys are moved
 along their head's predicted-query direction by 3 score standard deviations;
-a span is recovered when every token of it is in its head's attended set."""
+a span is recovered when every token of it is in its head's attended set.
+
+The recovery rate over 1000 seeds is reported for the fixed-budget fill at
+radius 0 (plain top-K), 1 and 2, and for the dilation reading of neighbour
+fetching at radius 1 (the neighbours beyond the budget). No figure on the
+pages applies to this stand-in, so the rates are measured, not pinned; the
+pinned facts are that neighbour fetching raises the rate over plain top-K and
+that the budget is respected."""
 import numpy as np
 
 from synthetic import CONFIGS
@@ -10,6 +17,7 @@ from synthetic.workload import make_layer
 from workloads import oracle_direction, oracle_step, recovered
 
 C1 = CONFIGS[1]
+N_SEEDS = 1000
 
 
 def test_fixed_seed_recovers_all_spans(orc):
@@ -21,16 +29,27 @@ def test_fixed_seed_recovers_all_spans(orc):
     assert (res["count"] <= C1.S + C1.W + C1.K).all()
 
 
-def test_recovery_rate_and_neighbour_fetching(orc):
-    n_seeds = 60
-    full = {0: 0, 1: 0}
-    for seed in range(n_seeds):
+def recovery_rates(orc, seeds):
+    """Full-recovery rate (all three spans) per reading over the given seeds."""
+    full = {"fill r0": 0, "fill r1": 0, "fill r2": 0, "dilate r1": 0}
+    for seed in seeds:
         inp = make_layer(C1, seed=seed, direction_fn=oracle_direction(orc, C1))
-        for r in (0, 1):
+        for r in (0, 1, 2):
             res = oracle_step(orc, C1, inp, r=r)
-            full[r] += all(recovered(res, inp["spans"]))
-    rate = {r: full[r] / n_seeds for r in full}
-    print("planted-span full recovery rate over %d seeds: %s" % (n_seeds, rate))
+            full["fill r%d" % r] += all(recovered(res, inp["spans"]))
+            assert (res["count"] <= C1.S + C1.W + C1.K).all()
+        L = inp["ctx_len"]
+        kp = oracle_step(orc, C1, inp)["kp"]
+        s = orc.score(orc.predict_queries(inp["x"], inp["w1"], inp["w2"])[1], kp, L, C1.Hq)
+        idx, cnt = orc.select(s, L, L, C1.S, C1.W, C1.K, 1, dilate=True)
+        full["dilate r1"] += all(recovered(dict(idx=idx, count=cnt), inp["spans"]))
+    return {k: v / len(seeds) for k, v in full.items()}
+
+
+def test_recovery_rate_over_1000_seeds(orc):
+    rate = recovery_rates(orc, range(N_SEEDS))
+    print("planted-span full recovery rate over %d seeds (oracle): %s" % (N_SEEDS, rate))
     # neighbour fetching exists to cover multi-token entities
-    assert rate[1] > rate[0]
-    assert rate[1] >= 0.6
+    assert rate["fill r1"] > rate["fill r0"]
+    assert rate["dilate r1"] >= rate["fill r1"]
+    assert rate["fill r1"] >= 0.6
