@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compact_attn_c2_traffic.txt")
 # sources of the step's dominant kernel (compaction + attention)
 KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_amd", "csrc", f)
-               for f in ("select.hip", "attn_impl.h")]
+               for f in ("select.hip", "select_impl.h", "attn_impl.h")]
 
 
 def kernel_source_hash():
@@ -84,9 +84,20 @@ def traffic_record():
     return float(rec["traffic_bytes_per_launch"])
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, cfg, seconds):
-    """The oracle (plain C, fp64, single thread) on full decode steps of the
-    same workload, repeated for about `seconds` of CPU time."""
+    """The oracle (plain C, fp64, OpenMP over independent heads and hidden
+    units) on full decode steps of the same workload, repeated for about
+    `seconds` of wall time on the host's cores."""
     import oracle as orc
     B, L = 1, cfg.L
     kp = np.zeros((B, cfg.Hkv, L, cfg.dp), np.uint16)
@@ -102,13 +113,20 @@ def cpu_baseline(inp, cfg, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": n / el, "unit": "steps/s", "cores": 1, "kind": "oracle",
+    threads = orc.num_threads()
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count()
+    return {"value": n / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": nproc,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "sample": "%d full decode steps of the same workload (predict, project 1 token, "
-                      "score 65536 tokens x 32 heads, select, attend), single-threaded C, "
-                      "%.1f s" % (n, el)}
+                      "score 65536 tokens x 32 heads, select, attend), C with OpenMP over heads "
+                      "and hidden units on %d threads, %.1f s" % (n, threads, el)}
 
 
-def run_interval(cfg, args):
+def run_interval(cfg, args, emit=True):
     """Prediction-interval pipeline over all layers of a multi-layer workload:
     once per interval, run every producer's predictor, score and select every
     consumer layer (the window left out of the list); then I decode steps,
@@ -293,7 +311,19 @@ def run_interval(cfg, args):
         "ms_per_step_graph": pct(graph_ms),
         "ms_per_step_eager": pct(eager_ms),
     }
-    print(json.dumps(res), flush=True)
+    # compulsory bytes of one interval: every layer's union gather at every
+    # step, plus the K' read, predictor weights and projections once
+    kp_bytes = nl * int(L0.sum()) * Hkv * dp * 2
+    mlp_bytes = npro * (E * Eh + Eh * Hq * dp) * 2
+    proj_bytes = nl * B * Hkv * I * (D * 2 + dp * 2)
+    interval_bytes = I * nl * attn_bytes + kp_bytes + mlp_bytes + proj_bytes
+    res["compulsory_bytes_per_step"] = interval_bytes / I
+    res["gbps"] = interval_bytes / (el / n_int) / 1e9
+    res["frac_of_peak"] = res["gbps"] / PEAK_HBM_GBS
+    if emit:
+        print(json.dumps(res), flush=True)
+    del K, V, Kp, Wk, Q
+    return res
 
 
 def run_offload(cfg, args):
@@ -509,6 +539,55 @@ def run_distill(cfg, args):
     print(json.dumps(res), flush=True)
 
 
+def measure_ceilings(tb, reps, idx, cnt, cfg, union_rows, row_bytes, stream, capture):
+    """Bandwidth ceilings of this part in the same process: a plain streaming
+    read of 2 GiB, and a gather of exactly the K/V rows the step's attention
+    reads (its launch shape, K and V rows requested together, no arithmetic),
+    over the rotated replicas."""
+    import torch
+    R = len(reps)
+    nbytes = 2 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda")
+    tb.tb_probe_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record(stream)
+    for _ in range(n):
+        tb.tb_probe_stream_read(buf, sink)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_us = e0.elapsed_time(e1) * 1e3 / n
+    del buf
+    B, Hq, cap = idx.shape
+    gsink = torch.zeros(tb.tb_probe_row_gather_sink_words(B, Hq, cap), dtype=torch.int32,
+                        device="cuda")
+
+    def one(i):
+        r = reps[i % R]
+        tb.tb_probe_row_gather(r["kc"], r["vc"], idx, cnt, gsink)
+    g = capture(one, R)
+    g.replay()
+    torch.cuda.synchronize()
+    n = 50
+    e0.record(stream)
+    for _ in range(n):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gather_us = e0.elapsed_time(e1) * 1e3 / (n * R)
+    gather_bytes = union_rows * row_bytes
+    return {"stream_read": {"bytes": nbytes, "us": round(read_us, 2),
+                            "gbps": nbytes / read_us / 1e3,
+                            "frac": nbytes / read_us / 1e3 / PEAK_HBM_GBS},
+            "attention_row_gather": {"bytes": gather_bytes, "us": round(gather_us, 2),
+                                     "gbps": gather_bytes / gather_us / 1e3,
+                                     "frac": gather_bytes / gather_us / 1e3 / PEAK_HBM_GBS,
+                                     "note": "the step's attention rows (per-head lists, union "
+                                             "bytes counted), its launch shape, no arithmetic"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -516,8 +595,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--replicas", type=int, default=8)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-intervals", action="store_true",
+                    help="skip the C3 and C5 interval lines of the default run")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured streaming-read and row-gather ceilings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--stages", action="store_true", help="also time each stage")
+    ap.add_argument("--stages", action="store_true",
+                    help="also time the other call sequences' stages (list written by the "
+                         "selection, separate score and select)")
     ap.add_argument("--core-only", action="store_true",
                     help="time the decode step only (no whole-context projection), e.g. under a "
                          "profiler")
@@ -768,16 +853,18 @@ def main():
     step_bytes = union_rows * row_bytes + kp_bytes + mlp_bytes + proj_bytes
     step_s = elapsed / K
 
-    stages = None
+    # each stage alone, as a graph of that stage over the R replicas: the
+    # step's three calls always; with --stages also the other call sequence
+    # on the same inputs (the list written by the selection, then the
+    # attention launch over it) and the separate score and select calls
+    names = [("predict+project", calls, 0), ("score+select", calls, 1),
+             ("list+attention", calls, 2)]
     if args.stages:
-        # each stage alone, as a graph of that stage over the R replicas; the
-        # separate scoring and selection calls are timed beside the fused one
         sep = [[(L_.tb_score, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(scores), B, cfg.Hq, cfg.Hkv,
                                L, cfg.dp, sp)),
                 (L_.tb_select, (P(scores), P(ctx), P(ctx), B, cfg.Hq, L, cfg.S, cfg.W, cfg.K,
                                 cfg.r, tb.TB_NF_FILL, P(idx), P(cnt), cap, P(ws_s), nb(ws_s),
                                 sp))] for r in reps]
-        # the list written by the selection, then the attention launch over it
         lst = [[(L_.tb_score_select, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(ctx), P(scores), B,
                                       cfg.Hq, cfg.Hkv, L, cfg.dp, cfg.S, cfg.W, cfg.K, cfg.r,
                                       tb.TB_NF_FILL, P(idx), P(cnt), cap, P(ws_s), nb(ws_s), sp)),
@@ -785,26 +872,33 @@ def main():
                                             cap, None, 0, B, cfg.Hq, cfg.Hkv, L, cfg.D,
                                             ctypes.c_float(1.0 / np.sqrt(cfg.D)), P(out), P(ws_a),
                                             nb(ws_a), sp))] for r in reps]
-        names = [("predict+project", calls, 0), ("score+select", calls, 1),
-                 ("list+attention", calls, 2), ("score+select, list written", lst, 0),
-                 ("attention", lst, 1), ("score", sep, 0), ("select", sep, 1)]
-        stages = {}
-        n_rep = 50
-        for n, cl, j in names:
-            def one(i, j=j, cl=cl):
-                fn, a = cl[i % R][j]
-                if fn(*a):
-                    raise RuntimeError(L_.tb_last_error_detail().decode())
-            g = capture(one, R)
+        names += [("score+select, list written", lst, 0), ("attention", lst, 1),
+                  ("score", sep, 0), ("select", sep, 1)]
+    stages = {}
+    n_rep = 50
+    for n, cl, j in names:
+        def one(i, j=j, cl=cl):
+            fn, a = cl[i % R][j]
+            if fn(*a):
+                raise RuntimeError(L_.tb_last_error_detail().decode())
+        g = capture(one, R)
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n_rep):
             g.replay()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(n_rep):
-                g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            stages[n] = round(e0.elapsed_time(e1) * 1e3 / (n_rep * R), 2)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        stages[n] = round(e0.elapsed_time(e1) * 1e3 / (n_rep * R), 2)
+    # the last stage graphs leave the step's selection state in place again
+    for i in range(R):
+        run_step(i)
+    torch.cuda.synchronize()
+
+    ceilings = None
+    if not args.no_ceilings:
+        ceilings = measure_ceilings(tb, reps, idx, cnt, cfg, union_rows, row_bytes, stream, capture)
 
     dilate = None
     if args.dilate:
@@ -893,17 +987,42 @@ def main():
         **({"dilate_mode": dilate} if dilate else {}),
         **({"prefill_projection": prefill} if prefill else {}),
     }
-    if stages:
-        res["stages_us"] = stages
-        # score + select + attention: compulsory bytes are the K' read and the union gather
-        span_us = stages["score+select"] + stages["list+attention"]
-        span_bytes = kp_bytes + union_rows * row_bytes
-        res["score_select_attn"] = {"us": round(span_us, 2), "bytes": span_bytes,
-                                    "gbps": span_bytes / span_us / 1e3,
-                                    "frac": span_bytes / span_us / 1e3 / PEAK_HBM_GBS}
+    res["stages_us"] = stages
+    # the target span, score + select + attention: its compulsory bytes are
+    # the K' read and the union gather
+    span_us = stages["score+select"] + stages["list+attention"]
+    span_bytes = kp_bytes + union_rows * row_bytes
+    res["score_select_attn"] = {"us": round(span_us, 2), "bytes": span_bytes,
+                                "gbps": span_bytes / span_us / 1e3,
+                                "frac": span_bytes / span_us / 1e3 / PEAK_HBM_GBS}
+    if ceilings:
+        res["ceilings"] = ceilings
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle), ~%.0f s" % args.cpu_seconds)
         res["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+    if not args.no_intervals:
+        # the multi-layer prediction-interval workloads on the Llama-3.1-8B
+        # (C3) and Qwen2.5-7B (C5) shapes, after the single-layer step's
+        # buffers are released
+        del calls, reps, base, g_all, g_rem, g_attn
+        import gc
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        res["interval_workloads"] = {}
+        for cid in (3, 5):
+            a2 = argparse.Namespace(**vars(args))
+            a2.intervals = 3
+            r_ = run_interval(CONFIGS[cid], a2, emit=False)
+            res["interval_workloads"]["C%d" % cid] = {
+                "workload": r_["config"]["workload"], "steps_per_s": r_["value"],
+                "ms_per_step_graph": r_["ms_per_step_graph"],
+                "compulsory_bytes_per_step": r_["compulsory_bytes_per_step"],
+                "gbps": r_["gbps"], "frac_of_peak": r_["frac_of_peak"],
+                "attention_gbps_per_launch": r_["roofline"]["achieved"]}
+            gc.collect()
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 

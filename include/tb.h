@@ -329,6 +329,27 @@ tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *
                                 float *out, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Measurement: bandwidth ceilings of this part, reported beside the HBM peak
+ * ("Significance": the method's premise is that reading only the selected
+ * tokens relieves the memory-bandwidth bottleneck).
+ * tb_probe_stream_read reads `bytes` (a multiple of 16) from src once, in
+ * 16-byte loads spread over at most sink_words workgroups (4 per compute
+ * unit), and writes one XOR word per workgroup to sink.
+ * tb_probe_row_gather requests exactly the K and V rows that
+ * tb_sparse_decode_attn(q, k_cache, v_cache, idx, count, cap, NULL, 0, ...)
+ * reads (the same workgroups, list splits and order; K and V rows of a split
+ * requested together) and writes one XOR word per workgroup to sink, which
+ * holds tb_probe_row_gather_sink_words(B, Hq, cap) words; no arithmetic on
+ * the rows. Limits as tb_sparse_decode_attn.
+ */
+tb_status tb_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, int sink_words,
+                               void *stream);
+size_t tb_probe_row_gather_sink_words(int B, int Hq, int cap);
+tb_status tb_probe_row_gather(const void *k_cache, const void *v_cache, const int32_t *idx,
+                              const int32_t *count, int cap, int B, int Hq, int Hkv, int Lmax,
+                              int D, uint32_t *sink, size_t sink_words, void *stream);
+
+/*
  * tb_sparse_decode_attn for callers that cannot allocate device memory (code
  * under graph capture that must not call hipMalloc, tight serving loops,
  * harnesses that forbid allocation): the same computation, arguments and

@@ -90,6 +90,12 @@ def lib():
     L.tb_sparse_decode_attn.restype = _i
     L.tb_sparse_decode_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i, _i, _i,
                                         ctypes.c_float, _vp, _vp, _sz, _vp]
+    L.tb_probe_stream_read.restype = _i
+    L.tb_probe_stream_read.argtypes = [_vp, _sz, _vp, _i, _vp]
+    L.tb_probe_row_gather_sink_words.restype = _sz
+    L.tb_probe_row_gather_sink_words.argtypes = [_i, _i, _i]
+    L.tb_probe_row_gather.restype = _i
+    L.tb_probe_row_gather.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _sz, _vp]
     L.tb_sparse_decode_attn_noalloc.restype = _i
     L.tb_sparse_decode_attn_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _vp, _i, _i, _i, _i,
                                                 _i, _i, ctypes.c_float, _vp, _vp]
@@ -415,3 +421,29 @@ def tb_sparse_decode_attn_noalloc(q, k_cache, v_cache, idx, count, out, scale=No
         _ptr(count, torch.int32, "count", 2), cap, ctx, int(window), B, Hq, Hkv, Lmax, D,
         float(scale), _ptr(out, torch.float32, "out", 3), _stream(stream)))
     return out
+
+
+def tb_probe_stream_read(src, sink, stream=None):
+    """Read every byte of src once (bandwidth probe); one XOR word per workgroup to sink."""
+    if not src.is_cuda or not src.is_contiguous() or (src.numel() * src.element_size()) % 16:
+        raise ValueError("src must be a contiguous GPU tensor of a multiple of 16 bytes")
+    _check(lib().tb_probe_stream_read(ctypes.c_void_p(src.data_ptr()),
+                                      src.numel() * src.element_size(),
+                                      _ptr(sink, torch.int32, "sink", 1), sink.numel(),
+                                      _stream(stream)))
+
+
+def tb_probe_row_gather_sink_words(B, Hq, cap):
+    return int(lib().tb_probe_row_gather_sink_words(B, Hq, cap))
+
+
+def tb_probe_row_gather(k_cache, v_cache, idx, count, sink, stream=None):
+    """Request the K/V rows the sparse attention over (idx, count) reads (bandwidth probe)."""
+    B, Hkv, Lmax, D = k_cache.shape
+    _, Hq, cap = idx.shape
+    _check(lib().tb_probe_row_gather(_ptr(k_cache, torch.bfloat16, "k_cache", 4),
+                                     _ptr(v_cache, torch.bfloat16, "v_cache", 4),
+                                     _ptr(idx, torch.int32, "idx", 3),
+                                     _ptr(count, torch.int32, "count", 2), cap, B, Hq, Hkv, Lmax,
+                                     D, _ptr(sink, torch.int32, "sink", 1), sink.numel(),
+                                     _stream(stream)))
