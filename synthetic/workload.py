@@ -13,11 +13,11 @@ from .gen import (add_direction_bf16, normal_bf16, ragged_lengths, rng_for,
                   span_starts, xavier_bf16)
 
 # tensor-kind tags for rng_for(cid, kind, layer, b)
-T_X, T_W1, T_W2, T_WK, T_K, T_V, T_Q, T_LEN, T_SPAN = range(9)
+T_X, T_W1, T_W2, T_WK, T_K, T_V, T_Q, T_LEN, T_SPAN, T_HEAVY = range(10)
 
 
 def make_layer(cfg, layer=0, seed=0, L=None, B=None, direction_fn=None,
-               n_spans=None, span_len=None, alpha=None, Lmax=None):
+               n_spans=None, span_len=None, alpha=None, Lmax=None, heavy=False):
     """Inputs of one decode step of one consumer layer.
 
     Returns a dict of numpy arrays: x [B,E], w1 [Eh,E], w2 [Nout,Eh],
@@ -26,6 +26,10 @@ def make_layer(cfg, layer=0, seed=0, L=None, B=None, direction_fn=None,
 
     direction_fn(inputs) -> float64 [B, Hq, D], when given, is used to plant
     spans: each span row of KV head h // g becomes bf16(k + alpha * v / |v|).
+    With heavy=True (and cfg.heavy_frac > 0) it also draws the heavy tail of
+    the long-context workload first: for every query head, heavy_frac of the
+    positions in [S, L_b - W) (drawn with replacement) get their KV head's key
+    moved by heavy_shift along that head's direction.
     """
     B = cfg.B if B is None else B
     L = cfg.L if L is None else L
@@ -52,10 +56,22 @@ def make_layer(cfg, layer=0, seed=0, L=None, B=None, direction_fn=None,
     n_spans = cfg.n_spans if n_spans is None else n_spans
     span_len = cfg.span_len if span_len is None else span_len
     alpha = cfg.alpha if alpha is None else alpha
-    if direction_fn is not None and n_spans > 0:
+    dirs = None
+    g = Hq // Hkv
+    if direction_fn is not None and heavy and cfg.heavy_frac > 0:
         dirs = np.asarray(direction_fn(out), np.float64)     # [B, Hq, D]
+        for b in range(B):
+            Lb = int(out["ctx_len"][b])
+            n = int(cfg.heavy_frac * (Lb - cfg.W - cfg.S))
+            for h in range(Hq):
+                rng = rng_for(cid, T_HEAVY, layer, b, h)
+                pos = rng.integers(cfg.S, Lb - cfg.W, size=n)
+                kv = h // g
+                kc[b, kv, pos] = add_direction_bf16(kc[b, kv, pos], dirs[b, h], cfg.heavy_shift)
+    if direction_fn is not None and n_spans > 0:
+        if dirs is None:
+            dirs = np.asarray(direction_fn(out), np.float64)     # [B, Hq, D]
         rng = rng_for(cid, T_SPAN, layer)
-        g = Hq // Hkv
         for b in range(B):
             Lb = int(out["ctx_len"][b])
             lo, hi = cfg.S + cfg.r, Lb - cfg.W - cfg.r

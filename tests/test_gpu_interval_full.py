@@ -1,6 +1,8 @@
 """GPU parity of one prediction interval at the full per-layer shapes of the
-multi-layer workloads (64K context at B 8; 256K context with r 2; the
-Qwen2.5-7B-shaped ragged batch of 4), in the launch sequence the interval
+multi-layer workloads (64K context at B 8; 256K context with r 2 and its
+heavy tail: 1 % of each query head's positions moved 2.5 along that head's
+predicted-query direction; the Qwen2.5-7B-shaped ragged batch of 4), in the
+launch sequence the interval
 benchmark times: predictor, score, selection with the window left out of the
 list (TB_SEL_OMIT_WINDOW), then I decode steps of tb_append_kv (which
 projects the pending keys once N_p have accumulated) and sparse attention
@@ -52,7 +54,7 @@ def test_interval_full_shape(tb, orc, cid):
     Lmax = cfg.L + I
     say("interval full shape", cfg.name, "generating")
     inp = make_layer(cfg, seed=0, Lmax=Lmax, direction_fn=oracle_direction(orc, cfg), n_spans=64,
-                     span_len=8, alpha=3.0)
+                     span_len=8, alpha=3.0, heavy=True)
     L0 = inp["ctx_len"].astype(np.int32)
     assert L0.max() + I <= Lmax
     kn = normal_bf16(rng_for(cid * 1000, T_NEW, 0), (I, B, Hkv, D))

@@ -345,6 +345,22 @@ def test_select_dilate_c2_shape(tb, orc):
     s = rng.standard_normal((1, 32, 65536)).astype(np.float32)
     assert_same_selection(orc, tb, s, [65536], [65536], 64, 256, 7872, 1, "dilate c2",
                           dilate=True)
+    assert_same_selection(orc, tb, s, [65536], [65536], 64, 256, 7872, 2, "dilate c2 r=2",
+                          dilate=True)
+
+
+def test_select_dilate_c4_shape_heavy_tail(tb, orc):
+    # the 256K-context segment with radius 2 and its heavy tail (one percent of
+    # positions per head shifted up by 2.5), a full-length and a ragged sequence
+    rng = rng_for(67)
+    L = 262144
+    s = rng.standard_normal((2, 32, L)).astype(np.float32)
+    for b in range(2):
+        for h in range(32):
+            pos = rng.integers(64, L - 256, size=L // 100)
+            s[b, h, pos] += 2.5
+    assert_same_selection(orc, tb, s, [L, 200001], [L, 199990], 64, 256, 7872, 2,
+                          "dilate c4 heavy tail", dilate=True)
 
 
 def test_select_dilate_ties_edges_and_max_radius(tb, orc):
