@@ -30,7 +30,9 @@
  *    reentrant. Calls that share a workspace must be ordered on one stream
  *    (they race otherwise).
  *  - Workspaces: size them with the matching *_workspace_bytes() query and
- *    zero-fill them once before first use (e.g. torch.zeros). Every call
+ *    zero-fill them once before first use (e.g. torch.zeros). A query
+ *    returns 0 for sizes its call rejects (sizes are checked before any
+ *    product is formed, so no size wraps around). Every call
  *    that takes a workspace leaves whatever must start at zero (the
  *    attention's arrival counters) at zero again when its kernels complete,
  *    so a workspace can be reused without clearing.

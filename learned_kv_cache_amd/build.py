@@ -36,22 +36,33 @@ def _run(cmd, verbose):
         sys.stderr.write(err + "\n")
 
 
-def build(verbose=False, jobs=None):
-    """Compile every csrc/*.hip to an object (in parallel), then link libtb.so."""
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for a CPU-only
+# check of the library's argument validation; device code is built as usual.
+HOST_SANITIZE_FLAGS = [
+    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-g",
+]
+
+
+def build(verbose=False, jobs=None, lib=None, objdir=None, extra_flags=()):
+    """Compile every csrc/*.hip to an object (in parallel), then link libtb.so
+    (or `lib`, with objects under `objdir` and `extra_flags` on every line)."""
     from concurrent.futures import ThreadPoolExecutor
+    lib = lib or LIB
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objdir = os.path.join(HERE, "_build")
+    objdir = objdir or os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = [os.path.join(objdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
-    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra_flags)
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2) - 1), 8)
     with ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda so: _run([hipcc()] + flags + ["-c", so[0], "-o", so[1]], verbose),
                     zip(srcs, objs)))
-    tmp = LIB + ".tmp"
-    _run([hipcc()] + HIPCC_FLAGS + ["-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = lib + ".tmp"
+    _run([hipcc()] + HIPCC_FLAGS + list(extra_flags) + ["-o", tmp] + objs, verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -86,7 +86,10 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(
 
 }  // namespace
 
-int attn_nsplit(int rows) { return (rows + CH - 1) / CH > 0 ? (rows + CH - 1) / CH : 1; }
+int attn_nsplit(int rows) {
+    const long long n = ((long long)rows + CH - 1) / CH;
+    return n > 0 ? (int)n : 1;
+}
 
 size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr) {
     const size_t nbh = (size_t)B * Hq;

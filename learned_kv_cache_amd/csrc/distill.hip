@@ -276,8 +276,8 @@ __global__ __launch_bounds__(kDThreads) void distill_kernel(
 
 }  // namespace
 
-int distill_nsplit(int Lmax) { return (Lmax + kDSplit - 1) / kDSplit; }
-int distill_ngroups(int R, int g) { return (R * g + kDRows - 1) / kDRows; }
+int distill_nsplit(int Lmax) { return (int)(((long long)Lmax + kDSplit - 1) / kDSplit); }
+int distill_ngroups(int R, int g) { return (int)(((long long)R * g + kDRows - 1) / kDRows); }
 
 size_t distill_ws_layout(int B, int R, int Hq, int Hkv, int Lmax, void *base, float **part,
                          uint32_t **ctr) {

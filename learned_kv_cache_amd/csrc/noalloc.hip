@@ -68,14 +68,16 @@ extern "C" tb_status tb_sparse_decode_attn_noalloc(const void *q, const void *k_
                "tb_sparse_decode_attn_noalloc: scale is NaN");
     const int win = ctx_len ? window : 0;
     const long long heads = (long long)B * Hq;
-    const long long part_bytes = heads * attn_nsplit(cap + win) * (D + 2) * (long long)sizeof(float);
-    TB_REQUIRE(heads * 4 <= (long long)kCtrBytes &&
-                   part_bytes <= (long long)(kScratchBytes - kCtrBytes),
-               TB_ERR_UNSUPPORTED_SHAPE,
+    const long long rows = (long long)cap + win;
+    TB_REQUIRE(heads <= (long long)(kCtrBytes / 4) && rows <= 0x7fffffffLL, TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_sparse_decode_attn_noalloc: %lld heads (at most %zu) or cap + window beyond "
+               "INT_MAX (use tb_sparse_decode_attn with a workspace)",
+               heads, kCtrBytes / 4);
+    const long long part_bytes = heads * attn_nsplit((int)rows) * (D + 2) * (long long)sizeof(float);
+    TB_REQUIRE(part_bytes <= (long long)(kScratchBytes - kCtrBytes), TB_ERR_UNSUPPORTED_SHAPE,
                "tb_sparse_decode_attn_noalloc: needs %lld bytes of partials for %lld heads; the "
-               "fixed scratch holds %zu bytes for at most %zu heads (use tb_sparse_decode_attn "
-               "with a workspace)",
-               part_bytes, heads, kScratchBytes - kCtrBytes, kCtrBytes / 4);
+               "fixed scratch holds %zu bytes (use tb_sparse_decode_attn with a workspace)",
+               part_bytes, heads, kScratchBytes - kCtrBytes);
     int dev = 0;
     const hipError_t he = hipGetDevice(&dev);
     TB_REQUIRE(he == hipSuccess, TB_ERR_HIP, "tb_sparse_decode_attn_noalloc: hipGetDevice: %s",

@@ -134,9 +134,9 @@ tb_status tb_probe_stream_read(const void *src, size_t bytes, uint32_t *sink, in
 }
 
 size_t tb_probe_row_gather_sink_words(int B, int Hq, int cap) {
-    if (B <= 0 || Hq <= 0 || cap <= 0) return 0;
+    if (B <= 0 || Hq <= 0 || cap <= 0 || (long long)B * Hq > 0x7fffffffLL) return 0;
     const long long items = (long long)B * Hq * tb::attn_nsplit(cap);
-    return (size_t)((items + 7) / 8 * 8);
+    return items > 0x7fffffffLL - 7 ? 0 : (size_t)((items + 7) / 8 * 8);
 }
 
 tb_status tb_probe_row_gather(const void *k_cache, const void *v_cache, const int32_t *idx,
@@ -154,7 +154,8 @@ tb_status tb_probe_row_gather(const void *k_cache, const void *v_cache, const in
     TB_REQUIRE((long long)Lmax * D * 2 <= 0x7fffffffLL, TB_ERR_UNSUPPORTED_SHAPE,
                "tb_probe_row_gather: one head's cache must be below 2 GiB");
     const size_t nb = tb_probe_row_gather_sink_words(B, Hq, cap);
-    TB_REQUIRE(nb <= 0x7fffffff && sink_words >= nb, TB_ERR_WORKSPACE_TOO_SMALL,
+    TB_REQUIRE(nb > 0, TB_ERR_UNSUPPORTED_SHAPE, "tb_probe_row_gather: grid beyond INT_MAX");
+    TB_REQUIRE(sink_words >= nb, TB_ERR_WORKSPACE_TOO_SMALL,
                "tb_probe_row_gather: sink holds %zu words, needs %zu", sink_words, nb);
     const int nsplit = tb::attn_nsplit(cap);
     const int items = B * Hq * nsplit;

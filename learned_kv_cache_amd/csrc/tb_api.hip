@@ -62,7 +62,7 @@ int tb_abi_version(void) { return 1; }
 // ---------------------------------------------------------------- predictor
 size_t tb_predict_workspace_bytes(int B, int E, int Eh, int n_out) {
     (void)n_out;
-    if (B <= 0 || E <= 0 || Eh <= 0 || E % 128 || Eh % 128) return 0;
+    if (B <= 0 || B > 64 || E <= 0 || Eh <= 0 || Eh > 1536 || E % 128 || Eh % 128) return 0;
     return (size_t)tb::predict_nsplit(E, Eh) * B * Eh * sizeof(float);
 }
 
@@ -195,6 +195,10 @@ tb_status tb_offload_append(const void *k_new, const void *v_new, const void *wk
 
 size_t tb_distill_workspace_bytes(int B, int R, int Hq, int Hkv, int Lmax) {
     if (B <= 0 || R <= 0 || Hq <= 0 || Hkv <= 0 || Lmax <= 0 || Hq % Hkv) return 0;
+    // the sizes tb_distill_loss accepts (its grid: splits x row groups x B * Hkv)
+    if ((long long)B * Hkv > 65535 || (long long)R * Hq > (1LL << 24) || Lmax > (1 << 30) ||
+        tb::distill_ngroups(R, Hq / Hkv) > 65535)
+        return 0;
     return tb::distill_ws_layout(B, R, Hq, Hkv, Lmax, nullptr, nullptr, nullptr);
 }
 
@@ -214,6 +218,8 @@ tb_status tb_distill_loss(const void *q, const void *k_cache, const float *qhat,
     TB_REQUIRE((D == 64 || D == 128) && (dp == 16 || dp == 32), TB_ERR_UNSUPPORTED_SHAPE,
                "tb_distill_loss: D must be 64 or 128 and dp 16 or 32");
     TB_REQUIRE(scale == scale, TB_ERR_INVALID_ARGUMENT, "tb_distill_loss: scale is NaN");
+    TB_REQUIRE(Lmax <= (1 << 30) && tb::distill_ngroups(R, Hq / Hkv) <= 65535,
+               TB_ERR_UNSUPPORTED_SHAPE, "tb_distill_loss: Lmax > 2^30 or more than 65535 row groups");
     const size_t need = tb_distill_workspace_bytes(B, R, Hq, Hkv, Lmax);
     TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
                "tb_distill_loss: workspace %zu < %zu bytes", ws_bytes, need);
@@ -244,7 +250,8 @@ tb_status tb_score(const float *qhat, int n_slots, int slot, const void *kp,
 
 // ---------------------------------------------------------------- selection
 size_t tb_select_workspace_bytes(int B, int Hq, int Lmax) {
-    if (B <= 0 || Hq <= 0 || Lmax <= 0) return 0;
+    // the sizes the selection calls accept
+    if (B <= 0 || Hq <= 0 || Lmax <= 0 || (long long)B * Hq > 65535 || Lmax > (1 << 24)) return 0;
     return tb::select_ws_layout(B, Hq, Lmax, nullptr, nullptr);
 }
 
@@ -359,6 +366,7 @@ tb_status tb_select_attn(const int32_t *ctx_len, const int32_t *proj_len, int B,
                                      sel_ws_bytes, &ws);
     if (e) return e;
     const size_t need = tb_attn_workspace_bytes(B, Hq, cap, 0, D);
+    TB_REQUIRE(need > 0, TB_ERR_UNSUPPORTED_SHAPE, "tb_select_attn: B * Hq * splits beyond INT_MAX");
     TB_REQUIRE(attn_ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
                "tb_select_attn: attention workspace %zu < %zu bytes", attn_ws_bytes, need);
     float *part;
@@ -372,8 +380,14 @@ tb_status tb_select_attn(const int32_t *ctx_len, const int32_t *proj_len, int B,
 
 // ---------------------------------------------------------------- attention
 size_t tb_attn_workspace_bytes(int B, int Hq, int cap, int window, int D) {
-    if (B <= 0 || Hq <= 0 || cap <= 0 || window < 0 || D <= 0) return 0;
-    return tb::attn_ws_layout(B, Hq, cap + window, D, nullptr, nullptr, nullptr);
+    if (B <= 0 || Hq <= 0 || cap <= 0 || window < 0 || (D != 64 && D != 128)) return 0;
+    // the sizes the attention calls accept: cap + window and the grid
+    // (B * Hq * splits workgroups, rounded up to 8) within INT_MAX
+    const long long rows = (long long)cap + window;
+    if (rows > 0x7fffffffLL || (long long)B * Hq > 0x7fffffffLL) return 0;
+    const long long items = (long long)B * Hq * tb::attn_nsplit((int)rows);
+    if (items > 0x7fffffffLL - 7) return 0;
+    return tb::attn_ws_layout(B, Hq, (int)rows, D, nullptr, nullptr, nullptr);
 }
 
 tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *v_cache,
@@ -396,6 +410,8 @@ tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *
     TB_REQUIRE(scale == scale, TB_ERR_INVALID_ARGUMENT, "tb_sparse_decode_attn: scale is NaN");
     const int win = ctx_len ? window : 0;
     const size_t need = tb_attn_workspace_bytes(B, Hq, cap, win, D);
+    TB_REQUIRE(need > 0, TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_sparse_decode_attn: cap + window or B * Hq * splits beyond INT_MAX");
     TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
                "tb_sparse_decode_attn: workspace %zu < %zu bytes", ws_bytes, need);
     float *part;

@@ -82,6 +82,7 @@ tb_status launch_append(const void *k_new, const void *v_new, void *kc, void *vc
                         const void *wk, int32_t *ctx, int32_t *plen, int B, int Hkv, int Lmax,
                         int D, int dp, int n_p, hipStream_t st);
 bool host_to_device(const void *ptr, const void **dev);
+int distill_ngroups(int R, int g);
 size_t distill_ws_layout(int B, int R, int Hq, int Hkv, int Lmax, void *base, float **part,
                          uint32_t **ctr);
 tb_status launch_distill(const void *q, const void *kc, const float *qhat, const void *kp,

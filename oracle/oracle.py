@@ -28,13 +28,20 @@ _i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
 _c_int = ctypes.c_int
 
 
-def build():
+# AddressSanitizer + UndefinedBehaviorSanitizer build (CPU runs of the pins)
+SANITIZE_FLAGS = ["-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer"]
+
+
+def build(path=None, extra_flags=()):
     """Compile the oracle with gcc (strict IEEE: no contraction, no fast-math;
-    OpenMP over independent outputs, which leaves every result unchanged)."""
+    OpenMP over independent outputs, which leaves every result unchanged).
+    `path` and `extra_flags` make another build of it (e.g. SANITIZE_FLAGS)."""
+    path = path or _LIB_PATH
     cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-ffp-contract=off", "-fopenmp",
-           "-fPIC", "-shared", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+           "-fPIC", "-shared"] + list(extra_flags) + ["-o", path + ".tmp", _SRC, "-lm"]
     subprocess.check_call(cmd)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    os.replace(path + ".tmp", path)
 
 
 def num_threads():
@@ -43,13 +50,18 @@ def num_threads():
 
 
 def lib():
+    """Load the oracle library, rebuilding it when the source is newer. The
+    environment variable TB_ORACLE_LIB names another build of the same source
+    to load instead (the sanitizer run uses it); that one is never rebuilt."""
     global _lib
     if _lib is not None:
         return _lib
-    if (not os.path.exists(_LIB_PATH)
-            or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
-        build()
-    L = ctypes.CDLL(_LIB_PATH)
+    path = os.environ.get("TB_ORACLE_LIB")
+    if not path:
+        path = _LIB_PATH
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
+            build()
+    L = ctypes.CDLL(path)
     L.orc_num_threads.restype = ctypes.c_int
     L.orc_num_threads.argtypes = []
     L.orc_bf16_bits.restype = ctypes.c_uint16

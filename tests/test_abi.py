@@ -138,3 +138,64 @@ def test_binding_rejects_cpu_tensors(tb):
     w2 = torch.zeros(128, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         tb.tb_predict_queries(x, w1, w2, torch.zeros(1, 128), torch.zeros(16, dtype=torch.uint8))
+
+
+BIG = 2 ** 31 - 1
+
+
+def test_workspace_queries_at_extreme_sizes(tb):
+    # every size query returns 0 for sizes its call rejects and never wraps
+    # around (the sanitizer run of this file checks the arithmetic itself)
+    L = tb.lib()
+    assert L.tb_select_workspace_bytes(1, 1, BIG) == 0            # Lmax > 2^24
+    assert L.tb_select_workspace_bytes(BIG, BIG, 1) == 0          # B * Hq > 65535
+    assert L.tb_select_workspace_bytes(1, 65535, 1 << 24) > 65535 * (1 << 24) * 8
+    assert L.tb_attn_workspace_bytes(1, 1, BIG, BIG, 128) == 0    # cap + window > INT_MAX
+    assert L.tb_attn_workspace_bytes(BIG, BIG, 1, 0, 128) == 0    # grid beyond INT_MAX
+    assert L.tb_attn_workspace_bytes(1, 1, 1, 0, BIG) == 0        # D unsupported
+    a = L.tb_attn_workspace_bytes(1, 1, BIG - 300, 256, 64)
+    assert a >= (BIG - 44) // 256 * 66 * 4
+    assert L.tb_distill_workspace_bytes(1, 1, 1, 1, BIG) == 0     # Lmax > 2^30
+    assert L.tb_distill_workspace_bytes(BIG, 1, 8, 8, 1000) == 0  # B * Hkv > 65535
+    assert L.tb_distill_workspace_bytes(1, BIG, 32, 8, 1000) == 0  # R * Hq > 2^24
+    assert L.tb_predict_workspace_bytes(BIG, 4096, 1024, 1024) == 0
+    assert L.tb_predict_workspace_bytes(1, 4096, BIG - 127, 1024) == 0
+    assert L.tb_probe_row_gather_sink_words(BIG, BIG, BIG) == 0
+
+
+def test_calls_with_extreme_sizes_are_rejected(tb):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("runs only where no kernel could be launched")
+    L = tb.lib()
+    vp = ctypes.c_void_p
+    # attention: cap + window beyond INT_MAX, grid beyond INT_MAX, huge workspace claimed
+    A = lambda B, Hq, cap, win, ctx: (vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), cap, ctx,
+                                      win, B, Hq, 1, 300, 64, ctypes.c_float(0.1), vp(FAKE),
+                                      vp(FAKE), 2 ** 62, None)
+    assert L.tb_sparse_decode_attn(*A(1, 8, BIG, BIG, vp(FAKE))) == 2
+    assert L.tb_sparse_decode_attn(*A(BIG, BIG, 64, 0, None)) == 2
+    N = lambda B, Hq, cap, win: (vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), cap, vp(FAKE),
+                                 win, B, Hq, 1, 300, 64, ctypes.c_float(0.1), vp(FAKE), None)
+    assert L.tb_sparse_decode_attn_noalloc(*N(1, 8, BIG, BIG)) == 2
+    assert L.tb_sparse_decode_attn_noalloc(*N(BIG, BIG, 64, 0)) == 2
+    # distillation: B * Hkv, R * Hq and Lmax beyond the supported range
+    Dl = lambda B, R, Hq, Hkv, Lmax: (vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), B, R, Hq,
+                                      Hkv, Lmax, 128, 32, ctypes.c_float(0.1), vp(FAKE), vp(FAKE),
+                                      2 ** 62, None)
+    assert L.tb_distill_loss(*Dl(BIG, 1, 8, 8, 1000)) == 1
+    assert L.tb_distill_loss(*Dl(1, BIG, 32, 8, 1000)) == 1
+    assert L.tb_distill_loss(*Dl(1, 4, 32, 8, BIG)) == 2
+    # selection over more than 2^24 tokens, over more than 65535 segments
+    S = lambda B, Hq, Lmax: (vp(FAKE), vp(FAKE), vp(FAKE), B, Hq, Lmax, 4, 16, 32, 1, 0, vp(FAKE),
+                             vp(FAKE), 52, vp(FAKE), 2 ** 62, None)
+    assert L.tb_select(*S(1, 8, BIG)) == 2
+    assert L.tb_select(*S(BIG, BIG, 300)) == 1
+    # prediction: B or Eh beyond the supported range
+    assert L.tb_predict_queries(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), BIG, 4096, 1024, 1024,
+                                vp(FAKE), 2 ** 62, None) == 1
+    assert L.tb_predict_queries(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), 1, 4096, BIG - 127, 1024,
+                                vp(FAKE), 2 ** 62, None) in (1, 2)
+    # probes
+    assert L.tb_probe_row_gather(vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), BIG, BIG, BIG, 1, 300,
+                                 64, vp(FAKE), 2 ** 62, None) == 2
