@@ -508,7 +508,7 @@ __global__ __launch_bounds__(T3) void thr_kernel(
     int omit_window, const uint32_t *__restrict__ info, const uint32_t *__restrict__ ccount,
     const uint32_t *__restrict__ acount, int nchunks, const uint64_t *__restrict__ cand,
     uint32_t *__restrict__ bitmap, int nwords, uint64_t *__restrict__ thr_out,
-    uint32_t *__restrict__ coff, int32_t *__restrict__ count, uint32_t *__restrict__ hist) {
+    uint32_t *__restrict__ coff, int32_t *__restrict__ count) {
     __shared__ uint64_t s_cand[LDS_CAND];
     __shared__ uint16_t s_cc[LDS_CAND];          // chunk of each LDS candidate
     __shared__ uint32_t s_off[MAX_CHUNKS];
@@ -518,13 +518,6 @@ __global__ __launch_bounds__(T3) void thr_kernel(
 
     const int seg = blockIdx.x, b = seg / Hq;
     const int tid = threadIdx.x;
-    if (hist != nullptr) {
-        // after the histogram route: its histogram back to zero for the next
-        // call (the classification launch before this one has read it)
-        uint4 *hz = reinterpret_cast<uint4 *>(hist + (size_t)seg * 4096);
-        hz[tid] = make_uint4(0, 0, 0, 0);
-        static_assert(T3 * 4 == 4096, "one 16-byte store per thread");
-    }
     constexpr int PC = MAX_CHUNKS / T3;
     // chunk c's counts sit in thread c / PC: with at most 64 PC chunks they
     // all sit in wave 0, whose shuffles then replace the block-wide scans
@@ -1233,7 +1226,7 @@ tb_status launch_after_thr(const int32_t *ctx, const int32_t *plen, int B, int H
 tb_status launch_thr_after(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
                            int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
                            bool omit_window, int32_t *idx, int32_t *count, int cap,
-                           const SelectWs &ws, hipStream_t st, bool defer_list, uint32_t *hist);
+                           const SelectWs &ws, hipStream_t st, bool defer_list);
 
 // classify, threshold, then compaction (or dilation and emission): every
 // launch of the selection after the band.
@@ -1251,20 +1244,19 @@ tb_status launch_after_band(const float *scores, const int32_t *ctx, const int32
     const tb_status e = check_launch("tb_select(classify)");
     if (e) return e;
     return launch_thr_after(scores, ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window, idx,
-                            count, cap, ws, st, defer_list, nullptr);
+                            count, cap, ws, st, defer_list);
 }
 
-// threshold (clearing the histogram of the histogram route when hist is
-// given), then the list.
+// threshold, then the list.
 tb_status launch_thr_after(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
                            int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
                            bool omit_window, int32_t *idx, int32_t *count, int cap,
-                           const SelectWs &ws, hipStream_t st, bool defer_list, uint32_t *hist) {
+                           const SelectWs &ws, hipStream_t st, bool defer_list) {
     const int nseg = B * Hq;
     const int rk = dilate ? 0 : r;
     hipLaunchKernelGGL(thr_kernel, dim3(nseg), dim3(T3), 0, st, scores, ctx, plen, Hq, Lmax, S, W,
                        K, rk, omit_window ? 1 : 0, ws.info, ws.ccount, ws.acount, ws.nchunks,
-                       ws.cand, ws.bitmap, ws.nwords, ws.thr, ws.coff, count, hist);
+                       ws.cand, ws.bitmap, ws.nwords, ws.thr, ws.coff, count);
     const tb_status e = check_launch("tb_select(threshold)");
     if (e) return e;
     return launch_after_thr(ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window, idx, count,
@@ -1324,12 +1316,12 @@ tb_status launch_score_select(const float *qhat, int n_slots, int slot, const vo
     if (hist_route_fits(Lmax, Hq / Hkv, r, dilate) && ws.hist) {
         // scoring with an exact histogram of the pooled keys, then
         // classification against the bin that holds the budget's key
-        const tb_status e = launch_score_hist_classify(qhat, n_slots, slot, kp, ctx, plen, scores,
-                                                       B, Hq, Hkv, Lmax, dp, S, W, K, r, dilate,
-                                                       ws, st);
+        const tb_status e = launch_score_hist_select(qhat, n_slots, slot, kp, ctx, plen, scores,
+                                                     B, Hq, Hkv, Lmax, dp, S, W, K, r, dilate,
+                                                     omit_window, count, ws, st);
         if (e) return e;
-        return launch_thr_after(scores, ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window,
-                                idx, count, cap, ws, st, defer_list, ws.hist);
+        return launch_after_thr(ctx, plen, B, Hq, Lmax, S, W, K, r, dilate, omit_window, idx,
+                                count, cap, ws, st, defer_list);
     }
     const int rk = dilate ? 0 : r;
     const int g = Hq / Hkv;

@@ -114,8 +114,8 @@ struct SelectWs {
     uint32_t *samp;      // [nseg][8192] sampled pooled key32
     uint32_t *dbm;       // [nseg][nwords] widened bitmap (dilation mode)
     uint32_t *dcount;    // [nseg][nchunks] widened tokens per chunk (dilation mode)
-    uint32_t *hist;      // [nseg][4096] threshold histogram, zero at rest (null when
-                         // Lmax <= kHistMinL)
+    uint32_t *hist;      // [2][nseg][4096] the histogram route's two histograms, zero
+                         // at rest (null off that route's sizes)
     int nwords;
     int nchunks;
 };
@@ -127,10 +127,11 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out);
 constexpr int kHistMinL = 8192;
 bool hist_route_fits(int Lmax, int g, int r, bool dilate);
 size_t hist_ws_bytes(int B, int Hq, int Lmax);
-tb_status launch_score_hist_classify(const float *qhat, int n_slots, int slot, const void *kp,
-                                     const int32_t *ctx, const int32_t *plen, float *scores,
-                                     int B, int Hq, int Hkv, int Lmax, int dp, int S, int W, int K,
-                                     int r, bool dilate, const SelectWs &ws, hipStream_t st);
+tb_status launch_score_hist_select(const float *qhat, int n_slots, int slot, const void *kp,
+                                   const int32_t *ctx, const int32_t *plen, float *scores, int B,
+                                   int Hq, int Hkv, int Lmax, int dp, int S, int W, int K, int r,
+                                   bool dilate, bool omit_window, int32_t *count,
+                                   const SelectWs &ws, hipStream_t st);
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
                         int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
                         bool omit_window, int32_t *idx, int32_t *count, int cap,

@@ -1,14 +1,16 @@
 """tb_score_select above 8192 tokens with radius <= 2 (0 in the dilation mode)
 takes the histogram route: scoring that counts every eligible token's pooled
-key32 in 4096 bins, then classification whose last workgroup per segment
-selects exactly inside the bin that holds the budget's key. It must equal
-tb_score followed by tb_select (the sampled-band route) bit for bit -- scores,
-list, count -- and the oracle's selection on the same scores, including
-where the bin holds every eligible token (all scores equal, integer-valued
-scores), more candidates than the threshold workgroup stages in LDS, budgets
-that cover the region or are empty, contexts shorter than the sink, nothing
-projected, ragged and lagging lengths, invalid lengths, and a workspace shared
-with the band route."""
+key32 in 4096 bins, then one workgroup per segment that finds the bin holding
+the budget's key, streams the segment's scores once and selects exactly
+inside that bin (through a second histogram of the next 12 key bits). It must
+equal tb_score followed by tb_select (the sampled-band route) bit for bit --
+scores, list, count -- and the oracle's selection on the same scores,
+including where the bin holds every eligible token (all scores equal,
+integer-valued scores), more candidates than the workgroup stages in LDS, a
+budget that takes a whole bin, budgets that cover the region or are empty,
+contexts shorter than the sink, nothing projected, ragged and lagging
+lengths, invalid lengths, a workspace shared with the band route, and a
+histogram region that was not zero at first use."""
 import numpy as np
 import pytest
 import torch
@@ -78,10 +80,10 @@ def _check(tb, orc, kp_np, qh_np, L, P, S, W, K, r, dilate=False, omit=False, re
             assert c1[b, h] == (len(want) if rc[b, h] >= 0 else -1), (b, h)
             if rc[b, h] >= 0:
                 assert np.array_equal(i1[b, h, :c1[b, h]], want), (b, h)
-    # the histograms (the workspace's last region) and the arrival counters
-    # (its first) are back at zero
+    # the two histograms (the workspace's last region) and the arrival
+    # counters (its first) are back at zero
     ws_np = host(ws)
-    hist_bytes = B * Hq * 4096 * 4
+    hist_bytes = 2 * B * Hq * 4096 * 4
     assert not ws_np[-hist_bytes:].any()
     assert not ws_np[:B * Hq * 4].any()
     return c1
@@ -129,12 +131,14 @@ def test_hist_route_integer_scores(tb, orc):
         _check(tb, orc, kp, qh, [Lmax], [Lmax], 16, 64, 4000, r)
 
 
-@pytest.mark.parametrize("n_mid,r", [(4000, 0), (5000, 0), (1500, 1)])
-def test_hist_route_candidates_around_lds_capacity(tb, orc, n_mid, r):
+@pytest.mark.parametrize("n_mid,r,K", [(4000, 0, 2000), (5000, 0, 2500), (1500, 1, 750),
+                                       (3000, 0, 3000), (9000, 0, 9000), (9000, 0, 4500)])
+def test_hist_route_candidates_around_lds_capacity(tb, orc, n_mid, r, K):
     # n_mid tokens score in [1.5, 1.7) (one bin: [1.5, 1.75)), the rest in
     # [0.5, 0.9): the budget's key lies in that bin, whose candidates number
-    # about the 4096 the threshold workgroup stages in LDS (with radius 1 each
-    # mid token's neighbours join the bin)
+    # up to beyond the 8192 the selection workgroup stages in LDS (with
+    # radius 1 each mid token's neighbours join the bin); a budget of n_mid
+    # takes the whole bin
     rng = rng_for(74, n_mid, r)
     B, Hq, Hkv, Lmax, dp = 1, 4, 1, 12000, 16
     x = 0.5 + 0.4 * rng.random(Lmax)
@@ -144,7 +148,7 @@ def test_hist_route_candidates_around_lds_capacity(tb, orc, n_mid, r):
     kpf[0, 0, :, 0] = x.astype(np.float16)
     qh = np.zeros((B, Hq * dp), np.float32)
     qh[0, ::dp] = 1.0
-    _check(tb, orc, kpf.view(np.uint16), qh, [Lmax], [Lmax], 8, 16, n_mid // 2, r)
+    _check(tb, orc, kpf.view(np.uint16), qh, [Lmax], [Lmax], 8, 16, K, r)
 
 
 def test_hist_route_edges(tb, orc):
@@ -173,3 +177,37 @@ def test_hist_route_bad_lengths_flagged(tb, orc):
         torch.cuda.synchronize()
         c = host(cnt)
         assert (c[0] == 4 + 16 + 500).all() and (c[1] == -1).all() and (c[2] == -1).all()
+
+
+@pytest.mark.parametrize("fill", ["large", "small", "second"])
+def test_hist_route_workspace_histogram_not_zero(tb, orc, fill):
+    # histogram regions that were not zero at first use: counts far above the
+    # segment's (the bin found disagrees with the pass), below its budget (no
+    # bin holds the budget's rank), or junk in the second histogram only; the
+    # selection stays exact and both regions are zero afterwards
+    kp, qh = _normal(11, 2, 8, 2, 20000, 16)
+    B, Hq, Lmax = 2, 8, 20000
+    L, P, S, W, K, r = [20000, 17000], [20000, 17000], 16, 64, 2000, 1
+    mode = tb.TB_NF_FILL
+    cap = S + W + K
+    ws = tb.new_workspace(tb.tb_select_workspace_bytes(B, Hq, Lmax))
+    s0, i0, c0 = _run(tb, False, dev32(qh), dev(kp, torch.float16), L, P, S, W, K, r, mode, cap, ws)
+    hw = B * Hq * 4096   # words of one histogram; the main one, then the second
+    rng = rng_for(75, ["large", "small", "second"].index(fill))
+    region = ws[-2 * hw * 4:].view(torch.int32)
+    if fill == "large":
+        region[:hw].copy_(torch.from_numpy(rng.integers(0, 5000, size=hw).astype(np.int32)))
+    elif fill == "small":
+        region[:hw].copy_(torch.from_numpy((rng.random(hw) < 0.02).astype(np.int32)))
+    else:
+        region[hw:].copy_(torch.from_numpy(rng.integers(0, 3, size=hw).astype(np.int32)))
+    s1, i1, c1 = _run(tb, True, dev32(qh), dev(kp, torch.float16), L, P, S, W, K, r, mode, cap, ws)
+    assert np.array_equal(c0, c1)
+    for b in range(B):
+        for h in range(Hq):
+            assert np.array_equal(i0[b, h, :c0[b, h]], i1[b, h, :c1[b, h]]), (b, h)
+    assert not host(ws)[-2 * hw * 4:].any()
+    assert not host(ws)[:B * Hq * 4].any()
+    # and the next call, on clean histograms, is exact too
+    s2, i2, c2 = _run(tb, True, dev32(qh), dev(kp, torch.float16), L, P, S, W, K, r, mode, cap, ws)
+    assert np.array_equal(c0, c2) and np.array_equal(i0, i2)
