@@ -182,7 +182,7 @@ constexpr int SS = 256;                    // tokens per wave step
 constexpr int CPW = 4;                     // chunks per workgroup
 constexpr int CAPC = 8192;                 // candidates the last workgroup stages in LDS
 constexpr int TPC = TSEL / MAXC;           // last workgroup: threads per chunk
-constexpr int PFS = 8;                     // candidate slots each of them fetches early
+constexpr int PFS = 12;                    // candidate slots each of them fetches early
 constexpr int NSW = (CPW * CHUNK / SS + NWSEL - 1) / NWSEL;   // steps per wave
 
 struct HistSelLds {
