@@ -1313,7 +1313,7 @@ tb_status launch_score_select(const float *qhat, int n_slots, int slot, const vo
                               int Hq, int Hkv, int Lmax, int dp, int S, int W, int K, int r,
                               bool dilate, bool omit_window, int32_t *idx, int32_t *count,
                               int cap, const SelectWs &ws, hipStream_t st, bool defer_list) {
-    if (hist_route_fits(Lmax, Hq / Hkv, r, dilate) && ws.hist) {
+    if (hist_route_fits(B * Hq, Lmax, Hq / Hkv, r, dilate) && ws.hist) {
         // scoring with an exact histogram of the pooled keys, then
         // classification against the bin that holds the budget's key
         const tb_status e = launch_score_hist_select(qhat, n_slots, slot, kp, ctx, plen, scores,

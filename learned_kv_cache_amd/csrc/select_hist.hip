@@ -642,20 +642,24 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
 
 }  // namespace
 
-bool hist_route_fits(int Lmax, int g, int r, bool dilate) {
+bool hist_route_fits(int nseg, int Lmax, int g, int r, bool dilate) {
     const int rk = dilate ? 0 : r;
     const int nchunks = (Lmax + CHUNK - 1) / CHUNK;
-    // measured: the histogram's flush atomics grow with the context and a
-    // group of more than 4 heads leaves one scoring workgroup per CU; beyond
-    // 64 chunks or 4 heads per group the sampled band was faster
-    return Lmax > kHistMinL && rk <= 2 && nchunks <= MAXC && g <= 4;
+    // measured: the histogram's flush atomics grow with the context and the
+    // number of scoring workgroups, and a group of more than 4 heads leaves
+    // one scoring workgroup per CU; beyond 64 chunks, 4 heads per group or 64
+    // segments (8 selection workgroups per segment then queue on the CUs)
+    // the sampled band was faster
+    return nseg <= kHistMaxSeg && Lmax > kHistMinL && rk <= 2 && nchunks <= MAXC && g <= 4;
 }
 
 size_t hist_ws_bytes(int B, int Hq, int Lmax) {
     // the histogram and the second histogram of the selection, per segment
     const int nchunks = (Lmax + CHUNK - 1) / CHUNK;
-    return (Lmax > kHistMinL && nchunks <= MAXC) ? 2 * (size_t)B * Hq * HBINS * sizeof(uint32_t)
-                                                 : 0;
+    const long long nseg = (long long)B * Hq;
+    return (nseg <= kHistMaxSeg && Lmax > kHistMinL && nchunks <= MAXC)
+               ? 2 * (size_t)nseg * HBINS * sizeof(uint32_t)
+               : 0;
 }
 
 tb_status launch_score_hist_select(const float *qhat, int n_slots, int slot, const void *kp,

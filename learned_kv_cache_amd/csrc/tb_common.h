@@ -120,12 +120,14 @@ struct SelectWs {
     int nchunks;
 };
 size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out);
-// The histogram route of tb_score_select (select_hist.hip): contexts above
-// kHistMinL tokens (below it the sampled band holds every token and is exact)
-// up to 64 chunks of 2048 tokens, radius <= 2 (0 in the dilation mode), at
-// most 4 query heads per KV head.
+// The histogram route of tb_score_select (select_hist.hip): at most
+// kHistMaxSeg segments (b, query head), contexts above kHistMinL tokens
+// (below it the sampled band holds every token and is exact) up to 64 chunks
+// of 2048 tokens, radius <= 2 (0 in the dilation mode), at most 4 query heads
+// per KV head.
 constexpr int kHistMinL = 8192;
-bool hist_route_fits(int Lmax, int g, int r, bool dilate);
+constexpr int kHistMaxSeg = 64;
+bool hist_route_fits(int nseg, int Lmax, int g, int r, bool dilate);
 size_t hist_ws_bytes(int B, int Hq, int Lmax);
 tb_status launch_score_hist_select(const float *qhat, int n_slots, int slot, const void *kp,
                                    const int32_t *ctx, const int32_t *plen, float *scores, int B,
