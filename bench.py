@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compact_attn_c2_traffic.txt")
 # sources of the step's dominant kernel (compaction + attention)
 KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_amd", "csrc", f)
-               for f in ("select.hip", "select_impl.h", "attn_impl.h")]
+               for f in ("select_attn.hip", "select_impl.h", "attn_impl.h")]
 
 
 def kernel_source_hash():

@@ -144,6 +144,9 @@ tb_status launch_score_select(const float *qhat, int n_slots, int slot, const vo
                               bool dilate, bool omit_window, int32_t *idx, int32_t *count,
                               int cap, const SelectWs &ws, hipStream_t st,
                               bool defer_list = false);
+tb_status launch_compact(const int32_t *ctx, const int32_t *plen, int B, int Hq, int Lmax, int S,
+                         int W, int K, bool omit_window, int32_t *idx, int cap, const SelectWs &ws,
+                         hipStream_t st);
 tb_status launch_select_attn(const int32_t *ctx, const int32_t *plen, int B, int Hq, int Hkv,
                              int Lmax, int S, int W, int K, bool omit_window, int32_t *idx,
                              int32_t *count, int cap, const SelectWs &ws, const void *q,
