@@ -12,40 +12,20 @@ namespace {
 
 using namespace sel;
 
-// Positions of the set bits of one chunk's 64 words (word lane of the wave,
-// list offset base for the chunk's first bit), keeping the list rows
-// [lo, hi): row p goes to sm_tok[p - lo] and to the list dst[p]. The bounds
-// are the same in every lane, so every lane takes part in every shuffle.
-__device__ __forceinline__ void emit_words_range(uint32_t mine, int c, uint32_t base, int lo,
-                                                 int hi, int *sm_tok, int32_t *dst) {
-    const int lane = threadIdx.x & 63;
+// Wave-wide: lane l holds the word of tokens [t0, t0 + 32) (t0 ascending with
+// the lane) whose first set bit is list row `base` + (set bits of the lanes
+// below); each lane stages its own rows that fall in [lo, hi) at sm_tok[row -
+// lo]. Every lane takes part in the prefix count.
+__device__ __forceinline__ void emit_rows(uint32_t mine, int t0, uint32_t base, int lo, int hi,
+                                          int *sm_tok) {
     const uint32_t pop = (uint32_t)__popc(mine);
-    uint32_t incl = pop;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-    }
-    const uint32_t first = incl - pop;
-    const uint32_t wend = __shfl(incl, 63);
-    const uint32_t s_begin = (uint32_t)lo > base ? (uint32_t)lo - base : 0u;
-    const uint32_t s_lim = (uint32_t)hi > base ? (uint32_t)hi - base : 0u;
-    const uint32_t s_end = wend < s_lim ? wend : s_lim;
-    for (uint32_t s0 = s_begin; s0 < s_end; s0 += 64) {
-        const uint32_t sl = s0 + (uint32_t)lane;
-        int lo2 = 0;
-#pragma unroll
-        for (int step = 32; step >= 1; step >>= 1) {
-            const uint32_t f = __shfl(first, lo2 + step);
-            if (f <= sl) lo2 += step;
-        }
-        const uint32_t wbits = __shfl(mine, lo2);
-        const uint32_t k = sl - __shfl(first, lo2);
-        if (sl < s_end) {
-            const int t = ((c * (CHUNK / 32) + lo2) << 5) + select_bit(wbits, k);
-            sm_tok[base + sl - lo] = t;
-            dst[base + sl] = t;
-        }
+    uint32_t p = base + wave_incl_scan(pop) - pop;
+    if (p + pop <= (uint32_t)lo || p >= (uint32_t)hi) return;
+    while (mine) {
+        const int bit = __builtin_ctz(mine);
+        if (p >= (uint32_t)lo && p < (uint32_t)hi) sm_tok[p - lo] = t0 + bit;
+        ++p;
+        mine &= mine - 1u;
     }
 }
 
@@ -168,13 +148,15 @@ __global__ __launch_bounds__(kAttnThreads) void compact_attn_kernel(
             }
             __syncthreads();
             if (act)
-                emit_words_range(s_word[wave][lane], c, s_off[c], lo, hi, sm_tok,
-                                 idx + (size_t)bh * cap);
+                emit_rows(s_word[wave][lane], (c * (CHUNK / 32) + lane) << 5, s_off[c], lo, hi,
+                          sm_tok);
             __syncthreads();
         }
-        // positions clamped to the cache, as the attention launch stages them
+        // the rows to the list (coalesced), then clamped to the cache as the
+        // attention launch stages them
         for (int i = threadIdx.x; i < hi - lo; i += kAttnThreads) {
             const int t = sm_tok[i];
+            idx[(size_t)bh * cap + lo + i] = t;
             sm_tok[i] = t < 0 ? 0 : (t >= Lmax ? Lmax - 1 : t);
         }
         __syncthreads();
