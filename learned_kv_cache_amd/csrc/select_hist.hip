@@ -17,7 +17,7 @@
 //                   (the neighbours' scores staged in LDS), a 4096-bin
 //                   histogram per head in LDS, added to the segment's
 //                   histogram in the workspace with agent-scope atomics
-//                   (nonzero bins only);
+//                   (nonzero bin pairs only, one 64-bit atomic per pair);
 //   hist_select     per segment, one 1024-thread workgroup per 4 chunks of
 //                   2048 tokens: the bin B* that holds the budget's key from
 //                   the histogram, a streaming pass over its tokens (tokens of
@@ -114,16 +114,15 @@ __global__ __launch_bounds__(TS, G <= 4 ? 8 : 4) void score_hist_kernel(
         }
     }
     __syncthreads();
-    uint32_t *hs = hist + (size_t)(b * Hq + kvh * G) * HBINS;
+    // bins 2k and 2k + 1 are adjacent 32-bit counters of the workspace: one
+    // 64-bit atomic adds both (a segment's count, below 2^25, never carries
+    // out of the low word)
+    uint64_t *hs = reinterpret_cast<uint64_t *>(hist + (size_t)(b * Hq + kvh * G) * HBINS);
     for (int i = tid; i < G * HBINS / 2; i += TS) {
         const uint32_t w = s_h[i];
         if (w == 0u) continue;
-        const int gi = i / (HBINS / 2), bin = 2 * (i % (HBINS / 2));
-        uint32_t *dst = hs + (size_t)gi * HBINS + bin;
-        if (w & 0xffffu)
-            __hip_atomic_fetch_add(dst, w & 0xffffu, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (w >> 16)
-            __hip_atomic_fetch_add(dst + 1, w >> 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t add = (uint64_t)(w & 0xffffu) | ((uint64_t)(w >> 16) << 32);
+        __hip_atomic_fetch_add(hs + i, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
