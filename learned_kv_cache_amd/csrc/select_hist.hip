@@ -433,12 +433,15 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (have_bin) {
+        // adjacent bins as one 64-bit atomic (counts never carry out of 32 bits)
         const uint4 sv = reinterpret_cast<const uint4 *>(sh.u.p.sub)[tid];
-        uint32_t *sb = sub + (size_t)seg * HBINS + 4 * tid;
-        if (sv.x) __hip_atomic_fetch_add(sb, sv.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (sv.y) __hip_atomic_fetch_add(sb + 1, sv.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (sv.z) __hip_atomic_fetch_add(sb + 2, sv.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (sv.w) __hip_atomic_fetch_add(sb + 3, sv.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint64_t *sb = reinterpret_cast<uint64_t *>(sub + (size_t)seg * HBINS + 4 * tid);
+        if (sv.x | sv.y)
+            __hip_atomic_fetch_add(sb, (uint64_t)sv.x | ((uint64_t)sv.y << 32), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (sv.z | sv.w)
+            __hip_atomic_fetch_add(sb + 1, (uint64_t)sv.z | ((uint64_t)sv.w << 32),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // arrival: every wave's stores complete before the barrier, then one
     // counter increment per workgroup
