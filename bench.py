@@ -36,15 +36,19 @@ import numpy as np
 
 METRIC = "sparse decode steps/s at 64K ctx, 8K budget; achieved HBM GB/s vs peak"
 PEAK_HBM_GBS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "compact_attn_c2_traffic.txt")
-# sources of the step's dominant kernel (compaction + attention)
-KERNEL_SRCS = [os.path.join(ROOT, "learned_kv_cache_amd", "csrc", f)
-               for f in ("select_attn.hip", "select_impl.h", "attn_impl.h")]
+# the step's dominant kernel: its committed traffic record and its sources,
+# for the split selection (threshold + list + attention) and for the deferred
+# list (compaction + attention)
+TRAFFIC_FILES = {"select": os.path.join(ROOT, "profiles", "hist_attn_c2_traffic.txt"),
+                 "list": os.path.join(ROOT, "profiles", "compact_attn_c2_traffic.txt")}
+KERNEL_SRCS = {k: [os.path.join(ROOT, "learned_kv_cache_amd", "csrc", f)
+                   for f in (first, "select_impl.h", "attn_impl.h")]
+               for k, first in (("select", "select_attn_hist.hip"), ("list", "select_attn.hip"))}
 
 
-def kernel_source_hash():
+def kernel_source_hash(defer="select"):
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
+    for f in KERNEL_SRCS[defer]:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
@@ -68,17 +72,18 @@ def planting_direction(inp, cfg):
     return np.einsum("bhc,hcd->bhd", qh, wk)
 
 
-def traffic_record():
+def traffic_record(defer="select"):
     """HBM bytes per launch of the step's dominant kernel from the committed
     rocprofv3 PMC summary, if it was taken on the kernel's current sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES[defer]
+    if not os.path.exists(path):
         return None
     rec = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    if (rec.get("kernel_source_sha256_16") != kernel_source_hash()
+    if (rec.get("kernel_source_sha256_16") != kernel_source_hash(defer)
             or "traffic_bytes_per_launch" not in rec):
         return None
     return float(rec["traffic_bytes_per_launch"])
@@ -600,6 +605,10 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured streaming-read and row-gather ceilings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--defer", choices=("select", "list"), default="select",
+                    help="the step's selection: split across the two calls "
+                         "(TB_SEL_DEFER_SELECT; the attention launch finds the threshold) or "
+                         "the list deferred (TB_SEL_DEFER_LIST)")
     ap.add_argument("--stages", action="store_true",
                     help="also time the other call sequences' stages (list written by the "
                          "selection, separate score and select)")
@@ -717,7 +726,8 @@ def main():
     tb.tb_score_select(qhat, reps[0]["kp"], ctx, ctx, scores, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt,
                        ws_s)
     tb.tb_sparse_decode_attn(reps[0]["q"], reps[0]["kc"], reps[0]["vc"], idx, cnt, out, ws_a)
-    defer = tb.TB_NF_FILL | tb.TB_SEL_DEFER_LIST
+    split = args.defer == "select"
+    defer = tb.TB_NF_FILL | (tb.TB_SEL_DEFER_SELECT if split else tb.TB_SEL_DEFER_LIST)
     tb.tb_score_select(qhat, reps[0]["kp"], ctx, ctx, scores, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt,
                        ws_s, mode=defer)
     tb.tb_select_attn(ctx, ctx, cfg.S, cfg.W, cfg.K, cfg.r, idx, cnt, ws_s, reps[0]["q"],
@@ -813,23 +823,28 @@ def main():
     # the dominant kernel alone: a graph of one compaction + attention launch
     # per replica (tb_select_attn on the selection state the last step left),
     # replayed back to back between two events on its stream, so the average
-    # is the launch's own duration (no host gaps between launches)
-    def attn_only(i):
-        fn, a = calls[i % R][-1]
-        if fn(*a):
-            raise RuntimeError(L_.tb_last_error_detail().decode())
-    g_attn = capture(attn_only, R)
-    g_attn.replay()
-    ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_attn = max(1, min(200, K // R))
-    torch.cuda.synchronize()
-    ea.record(stream)
-    for _ in range(n_attn):
-        g_attn.replay()
-    eb.record(stream)
-    torch.cuda.synchronize()
+    # is the launch's own duration (no host gaps between launches). With the
+    # split selection the attention launch consumes its state (it clears the
+    # histograms), so it cannot be replayed alone: its duration is the mean
+    # over the timed eager steps of events recorded around it on its stream.
     attn_eager_avg_s = attn_avg_s
-    attn_avg_s = ea.elapsed_time(eb) / 1e3 / (n_attn * R)
+    n_attn = K
+    if not split:
+        def attn_only(i):
+            fn, a = calls[i % R][-1]
+            if fn(*a):
+                raise RuntimeError(L_.tb_last_error_detail().decode())
+        g_attn = capture(attn_only, R)
+        g_attn.replay()
+        ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n_attn = max(1, min(200, K // R)) * R
+        torch.cuda.synchronize()
+        ea.record(stream)
+        for _ in range(n_attn // R):
+            g_attn.replay()
+        eb.record(stream)
+        torch.cuda.synchronize()
+        attn_avg_s = ea.elapsed_time(eb) / 1e3 / n_attn
 
     # algorithmic bytes of one attention launch: each distinct (kv head, token)
     # row of the g heads' attended sets, K and V, bf16 -- counted from idx
@@ -859,8 +874,9 @@ def main():
     # attention launch over it) and the separate score and select calls
     # (the attention call consumes the selection's state, so the span is timed
     # as the two calls together and score+select as the difference)
-    names = [("predict+project", calls, (0,)), ("score+select+attention", calls, (1, 2)),
-             ("list+attention", calls, (2,))]
+    names = [("predict+project", calls, (0,)), ("score+select+attention", calls, (1, 2))]
+    if not split:
+        names.append(("list+attention", calls, (2,)))
     if args.stages:
         sep = [[(L_.tb_score, (P(qhat), 1, 0, P(r["kp"]), P(ctx), P(scores), B, cfg.Hq, cfg.Hkv,
                                L, cfg.dp, sp)),
@@ -894,7 +910,10 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         stages[n] = round(e0.elapsed_time(e1) * 1e3 / (n_rep * R), 2)
-    stages["score+select"] = round(stages["score+select+attention"] - stages["list+attention"], 2)
+    if split:
+        stages["threshold+list+attention (eager events)"] = round(attn_avg_s * 1e6, 2)
+    stages["score+select"] = round(stages["score+select+attention"] -
+                                   (attn_avg_s * 1e6 if split else stages["list+attention"]), 2)
     # the last stage graphs leave the step's selection state in place again
     for i in range(R):
         run_step(i)
@@ -956,7 +975,7 @@ def main():
                   "attention_gbps": d_bytes / dil_us[1] / 1e3,
                   "fill_attended_per_head_mean": float(gc.mean()), "fill_attn_bytes": attn_bytes}
 
-    traffic = traffic_record()
+    traffic = traffic_record(args.defer)
     res = {
         "metric": METRIC,
         "value": K / elapsed,
@@ -978,10 +997,12 @@ def main():
                    "global_batch": B, "seq_len": L},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "list compaction + sparse decode attention gather "
-                               "(compact_attn_kernel<128>)",
+                     "kernel": ("threshold + list + sparse decode attention gather "
+                                "(hist_attn_kernel<128>)" if split else
+                                "list compaction + sparse decode attention gather "
+                                "(compact_attn_kernel<128>)"),
                      "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6,
-                     "launches_timed": n_attn * R,
+                     "launches_timed": n_attn,
                      "avg_launch_us_eager_events": attn_eager_avg_s * 1e6},
         "eager_steps_per_s": K / eager_elapsed,
         "step_us": step_pct,

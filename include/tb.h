@@ -65,6 +65,21 @@ typedef int tb_status;
  * list is written -- count is written, idx is not; the selection state stays
  * in the workspace for tb_select_attn, which writes idx and attends. */
 #define TB_SEL_DEFER_LIST 0x200
+/* mode flag of tb_score_select (TB_NF_FILL only), then of the tb_select_attn
+ * call that follows it: the selection is split across the two calls. Where
+ * it applies (the histogram route of tb_score_select: B * Hq <= 64,
+ * 8192 < Lmax <= 131072, radius <= 2, Hq / Hkv <= 4, and ceil(Lmax / 2048)
+ * chunks <= ceil(cap / 256)), tb_score_select writes the scores and classifies
+ * every token against the histogram bin of the budget's key, and writes
+ * neither count nor idx; tb_select_attn then finds the exact threshold in
+ * every attention workgroup (one per chunk of 2048 tokens), writes count and
+ * idx as tb_score_select without the flag would, and attends. Its out then
+ * agrees with tb_sparse_decode_attn over that list to fp32 rounding (other
+ * splits: not bit for bit). A workspace whose histograms were not zero before
+ * the first call is reported as count -1 and out 0 for the segments it
+ * affects (the call leaves them zero, so the next call is exact). Elsewhere
+ * the flag acts as TB_SEL_DEFER_LIST. tb_select rejects it. */
+#define TB_SEL_DEFER_SELECT 0x400
 
 /* Human-readable text for a status code (static storage). */
 const char *tb_status_string(tb_status s);
@@ -285,8 +300,8 @@ tb_status tb_score_select(const float *qhat, int n_slots, int slot, const void *
  * The selection's list and the sparse attention over it in one launch
  * ("Inference strategy": the three buffers; "Significance": attention reads
  * only the selected tokens). Called after tb_select or tb_score_select with
- * mode | TB_SEL_DEFER_LIST on the same workspace, arguments and stream, with
- * the same mode here: writes idx exactly as the selection without the flag
+ * mode | TB_SEL_DEFER_LIST (or tb_score_select with TB_SEL_DEFER_SELECT, see
+ * there) on the same workspace, arguments and stream, with the same mode here: writes idx exactly as the selection without the flag
  * would, and out exactly as tb_sparse_decode_attn(q, k_cache, v_cache, idx,
  * count, cap, NULL, 0, B, Hq, Hkv, Lmax, D, scale, out, attn_workspace, ...)
  * would (bit for bit: the same splits through the same code). Each attention

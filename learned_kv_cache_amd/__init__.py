@@ -23,6 +23,7 @@ TB_NF_FILL = 0
 TB_NF_DILATE = 1
 TB_SEL_OMIT_WINDOW = 0x100
 TB_SEL_DEFER_LIST = 0x200
+TB_SEL_DEFER_SELECT = 0x400
 
 _lib = None
 _vp = ctypes.c_void_p

@@ -32,6 +32,124 @@ __device__ inline void combine_lanes(float &m, float &l, float (&o)[8]) {
     }
 }
 
+// The workgroup's (max, sum, o) state from its lanes' row-group states: the
+// partial of split `split` of head bh is stored and, in the last split of the
+// head to arrive, all nsplit partials are merged into out. Returns true in
+// that last workgroup, after the merge.
+template <int D>
+__device__ __forceinline__ bool attn_store_merge(float m, float l, float (&acc)[8], int nsplit,
+                                                 float *__restrict__ part,
+                                                 uint32_t *__restrict__ ctr,
+                                                 float *__restrict__ out, int bh, int split) {
+    constexpr int LPR = D / 8;               // lanes per row
+    constexpr int RPW = 64 / LPR;            // row groups per wave
+    __shared__ float sm_o[kAttnWaves][D];
+    __shared__ float sm_m[kAttnWaves], sm_l[kAttnWaves];
+    __shared__ int sm_last;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rg = lane / LPR, cl = lane % LPR;
+
+    // merge the row groups: within each wave by butterfly, then the waves'
+    // states through LDS (wave 0)
+    combine_lanes<LPR>(m, l, acc);
+    if (rg == 0) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sm_o[wave][cl * 8 + c] = acc[c];
+        if (cl == 0) {
+            sm_m[wave] = m;
+            sm_l[wave] = l;
+        }
+    }
+    __syncthreads();
+    float *pp = part + ((size_t)bh * nsplit + split) * (D + 2);
+    if (wave == 0) {
+        float M = -1e30f;
+#pragma unroll
+        for (int i = 0; i < kAttnWaves; ++i) M = fmaxf(M, sm_m[i]);
+        float Ls = 0.f;
+        float O[D / 64];
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) O[j] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kAttnWaves; ++i) {
+            const float w = exp2f(sm_m[i] - M);
+            Ls += sm_l[i] * w;
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) O[j] += sm_o[i][lane + 64 * j] * w;
+        }
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j)
+            __hip_atomic_store(pp + 2 + lane + 64 * j, O[j], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) {
+            __hip_atomic_store(pp, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(pp + 1, Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // the partial's stores complete before the arrival is counted
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (lane == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(ctr + bh, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            sm_last = prev == (uint32_t)(nsplit - 1);
+        }
+    }
+    __syncthreads();
+    if (!sm_last) return false;
+
+    // last arrival: merge all partials of this head, kAttnThreads / LPR at a time:
+    // each row group of lanes loads one partial's (max, sum, 8 channels), the
+    // waves combine theirs by butterfly, and threads c < D fold the waves'
+    // states into a running (max, sum, o[c]) through LDS
+    constexpr int PW = D + 2;
+    constexpr int PPC = kAttnThreads / LPR;
+    const float *base = part + (size_t)bh * nsplit * PW;
+    float M = -1e30f, den = 0.f, num = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += PPC) {
+        const int sidx = s0 + wave * RPW + rg;
+        const bool valid = sidx < nsplit;
+        const float *src = base + (size_t)(valid ? sidx : 0) * PW;
+        float pm = valid ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : -1e30f;
+        float pl = valid ? __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : 0.f;
+        float po[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            po[c] = valid ? __hip_atomic_load(src + 2 + cl * 8 + c, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT)
+                          : 0.f;
+        combine_lanes<LPR>(pm, pl, po);
+        __syncthreads();
+        if (rg == 0) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) sm_o[wave][cl * 8 + c] = po[c];
+            if (cl == 0) {
+                sm_m[wave] = pm;
+                sm_l[wave] = pl;
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < D) {
+            float Mc = M;
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w) Mc = fmaxf(Mc, sm_m[w]);
+            const float r = exp2f(M - Mc);
+            den *= r;
+            num *= r;
+#pragma unroll
+            for (int w = 0; w < kAttnWaves; ++w) {
+                const float wt = exp2f(sm_m[w] - Mc);
+                den += sm_l[w] * wt;
+                num += sm_o[w][threadIdx.x] * wt;
+            }
+            M = Mc;
+        }
+    }
+    if (threadIdx.x < D) out[(size_t)bh * D + threadIdx.x] = den > 0.f ? num / den : 0.f;
+    if (threadIdx.x == 0) __hip_atomic_store(ctr + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+}
+
 // One workgroup's split of head bh (sequence b, KV head kvh): list rows
 // [lo, hi) whose positions, clamped to the cache, are staged in sm_tok[0,
 // hi - lo). Forms the split's (max, sum, o) partial and, in the last split of
@@ -49,10 +167,6 @@ __device__ __forceinline__ void attn_split(const uint16_t *__restrict__ q,
     constexpr int NG = kAttnWaves * RPW;     // row groups per workgroup
     constexpr int STRIDE = NG;               // rows per workgroup pass
     constexpr int RPG = kAttnCH / NG;        // rows per row group
-
-    __shared__ float sm_o[kAttnWaves][D];
-    __shared__ float sm_m[kAttnWaves], sm_l[kAttnWaves];
-    __shared__ int sm_last;
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rg = lane / LPR, cl = lane % LPR;
@@ -137,104 +251,110 @@ __device__ __forceinline__ void attn_split(const uint16_t *__restrict__ q,
         }
     }
 
-    // merge the row groups: within each wave by butterfly, then the waves'
-    // states through LDS (wave 0)
-    combine_lanes<LPR>(m, l, acc);
-    if (rg == 0) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) sm_o[wave][cl * 8 + c] = acc[c];
-        if (cl == 0) {
-            sm_m[wave] = m;
-            sm_l[wave] = l;
-        }
-    }
-    __syncthreads();
-    float *pp = part + ((size_t)bh * nsplit + split) * (D + 2);
-    if (wave == 0) {
-        float M = -1e30f;
-#pragma unroll
-        for (int i = 0; i < kAttnWaves; ++i) M = fmaxf(M, sm_m[i]);
-        float Ls = 0.f;
-        float O[D / 64];
-#pragma unroll
-        for (int j = 0; j < D / 64; ++j) O[j] = 0.f;
-#pragma unroll
-        for (int i = 0; i < kAttnWaves; ++i) {
-            const float w = exp2f(sm_m[i] - M);
-            Ls += sm_l[i] * w;
-#pragma unroll
-            for (int j = 0; j < D / 64; ++j) O[j] += sm_o[i][lane + 64 * j] * w;
-        }
-#pragma unroll
-        for (int j = 0; j < D / 64; ++j)
-            __hip_atomic_store(pp + 2 + lane + 64 * j, O[j], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        if (lane == 0) {
-            __hip_atomic_store(pp, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(pp + 1, Ls, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // the partial's stores complete before the arrival is counted
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (lane == 0) {
-            const uint32_t prev = __hip_atomic_fetch_add(ctr + bh, 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            sm_last = prev == (uint32_t)(nsplit - 1);
-        }
-    }
-    __syncthreads();
-    if (!sm_last) return;
+    attn_store_merge<D>(m, l, acc, nsplit, part, ctr, out, bh, split);
+}
 
-    // last arrival: merge all partials of this head, kAttnThreads / LPR at a time:
-    // each row group of lanes loads one partial's (max, sum, 8 channels), the
-    // waves combine theirs by butterfly, and threads c < D fold the waves'
-    // states into a running (max, sum, o[c]) through LDS
-    constexpr int PW = D + 2;
-    constexpr int PPC = kAttnThreads / LPR;
-    const float *base = part + (size_t)bh * nsplit * PW;
-    float M = -1e30f, den = 0.f, num = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += PPC) {
-        const int sidx = s0 + wave * RPW + rg;
-        const bool valid = sidx < nsplit;
-        const float *src = base + (size_t)(valid ? sidx : 0) * PW;
-        float pm = valid ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : -1e30f;
-        float pl = valid ? __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : 0.f;
-        float po[8];
+// The lane's row-group (max, sum, o) state over rows [0, nrows) whose
+// positions, clamped to the cache, are staged in sm_tok (nrows <= the
+// array's size, a multiple of ROWS): ROWS rows per pass, the state rescaled
+// to each pass's new maximum. Rows beyond nrows are not loaded.
+template <int D, int ROWS = kAttnCH>
+__device__ __forceinline__ void attn_rows(const uint16_t *__restrict__ q,
+                                          const uint16_t *__restrict__ kc,
+                                          const uint16_t *__restrict__ vc, int Hkv, int Lmax,
+                                          float scale_log2, int b, int kvh, int bh, int nrows,
+                                          const int *sm_tok, float &m, float &l,
+                                          float (&acc)[8]) {
+    constexpr int LPR = D / 8;               // lanes per row
+    constexpr int RPW = 64 / LPR;            // row groups per wave
+    constexpr int NG = kAttnWaves * RPW;     // row groups per workgroup
+    constexpr int STRIDE = NG;               // rows per workgroup pass
+    constexpr int RPG = ROWS / NG;           // rows per row group and pass
+    static_assert(RPG >= 1 && RPG * NG == ROWS, "whole row groups per pass");
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int rg = lane / LPR, cl = lane % LPR;
+    const int grp = wave * RPW + rg;
+
+    float qf[8];
+    {
+        const uint4 qv = *reinterpret_cast<const uint4 *>(q + (size_t)bh * D + cl * 8);
+        const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            po[c] = valid ? __hip_atomic_load(src + 2 + cl * 8 + c, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT)
-                          : 0.f;
-        combine_lanes<LPR>(pm, pl, po);
-        __syncthreads();
-        if (rg == 0) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) sm_o[wave][cl * 8 + c] = po[c];
-            if (cl == 0) {
-                sm_m[wave] = pm;
-                sm_l[wave] = pl;
-            }
-        }
-        __syncthreads();
-        if (threadIdx.x < D) {
-            float Mc = M;
-#pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) Mc = fmaxf(Mc, sm_m[w]);
-            const float r = exp2f(M - Mc);
-            den *= r;
-            num *= r;
-#pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) {
-                const float wt = exp2f(sm_m[w] - Mc);
-                den += sm_l[w] * wt;
-                num += sm_o[w][threadIdx.x] * wt;
-            }
-            M = Mc;
+        for (int e = 0; e < 4; ++e) {
+            qf[2 * e] = bf16_lo(w[e]) * scale_log2;
+            qf[2 * e + 1] = bf16_hi(w[e]) * scale_log2;
         }
     }
-    if (threadIdx.x < D) out[(size_t)bh * D + threadIdx.x] = den > 0.f ? num / den : 0.f;
-    if (threadIdx.x == 0) __hip_atomic_store(ctr + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const size_t head_off = (size_t)(b * Hkv + kvh) * Lmax * D;
+    const int head_bytes = Lmax * D * 2;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(kc + head_off), (short)0, head_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(vc + head_off), (short)0, head_bytes, kRsrcWord3);
+    const int lane_off = cl * 16;
+
+    m = -1e30f;
+    l = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+    for (int base = 0; base < nrows; base += ROWS) {
+        const int *tok = sm_tok + base;
+        const int n = nrows - base;   // rows of this pass: [0, min(n, ROWS))
+        uint4 kv[RPG];
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const int i = grp + u * STRIDE;
+            kv[u] = i < n ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          krs, tok[i] * (D * 2) + lane_off, 0, 0))
+                          : make_uint4(0, 0, 0, 0);
+        }
+        float s[RPG];
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const uint32_t w[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+            float d = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                d = __builtin_fmaf(bf16_lo(w[e]), qf[2 * e], d);
+                d = __builtin_fmaf(bf16_hi(w[e]), qf[2 * e + 1], d);
+            }
+            s[u] = d;
+        }
+        // the logits are formed (and the K registers freed) before V is requested
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) asm volatile("" ::"v"(s[u]));
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const int i = grp + u * STRIDE;
+            kv[u] = i < n ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          vrs, tok[i] * (D * 2) + lane_off, 0, 0))
+                          : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) s[u] = group_sum<LPR>(s[u]);
+        float mt = m;
+#pragma unroll
+        for (int u = 0; u < RPG; ++u)
+            if (grp + u * STRIDE < n) mt = fmaxf(mt, s[u]);
+        const float rs = exp2f(m - mt);
+        l *= rs;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] *= rs;
+        m = mt;
+#pragma unroll
+        for (int u = 0; u < RPG; ++u) {
+            const float p = (grp + u * STRIDE < n) ? exp2f(s[u] - m) : 0.f;
+            l += p;
+            const uint32_t w[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                acc[2 * e] = __builtin_fmaf(p, bf16_lo(w[e]), acc[2 * e]);
+                acc[2 * e + 1] = __builtin_fmaf(p, bf16_hi(w[e]), acc[2 * e + 1]);
+            }
+        }
+    }
 }
 
 }  // namespace tb

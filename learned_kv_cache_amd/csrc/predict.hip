@@ -128,8 +128,21 @@ __global__ __launch_bounds__(kThreads) void mlp2_kernel(const float *__restrict_
     const int n = lane & 15, kq = lane >> 4;
     const int nb = B - bt * 16 < 16 ? B - bt * 16 : 16;
     const int nblk = Eh / BLK;
+    // the thread's first partials are requested before the wave's W2 tiles,
+    // so building h waits for the partials only (loads complete in order)
+    const int q4 = Eh / 4;
+    const size_t sstride = (size_t)B * Eh;
+    float4 f[kMaxSplit];
+    const int it0 = threadIdx.x;
+    if (it0 < nb * q4) {
+        const int bl = it0 / q4, j = (it0 - bl * q4) * 4;
+        const float *p0 = part + (size_t)(bt * 16 + bl) * Eh + j;
+#pragma unroll
+        for (int sp = 0; sp < kMaxSplit; ++sp)
+            f[sp] = sp < nsplit ? *reinterpret_cast<const float4 *>(p0 + sp * sstride)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     const uint16_t *arow = w2 + (size_t)(nt * 16 + n) * Eh + kq * 32;
-    // this wave's W2 tiles are requested before h is built
     uint4 av[kMaxBlkPerWave][4];
 #pragma unroll
     for (int i = 0; i < kMaxBlkPerWave; ++i) {
@@ -142,16 +155,15 @@ __global__ __launch_bounds__(kThreads) void mlp2_kernel(const float *__restrict_
     }
     // rows of the tile beyond B are zero
     for (int i = threadIdx.x; i < (16 - nb) * Eh; i += kThreads) s_h[nb * Eh + i] = 0;
-    const int q4 = Eh / 4;
-    for (int it = threadIdx.x; it < nb * q4; it += kThreads) {
+    for (int it = it0; it < nb * q4; it += kThreads) {
         const int bl = it / q4, j = (it - bl * q4) * 4;
         const float *p0 = part + (size_t)(bt * 16 + bl) * Eh + j;
-        const size_t sstride = (size_t)B * Eh;
-        float4 f[kMaxSplit];
+        if (it != it0) {
 #pragma unroll
-        for (int sp = 0; sp < kMaxSplit; ++sp)
-            f[sp] = sp < nsplit ? *reinterpret_cast<const float4 *>(p0 + sp * sstride)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int sp = 0; sp < kMaxSplit; ++sp)
+                f[sp] = sp < nsplit ? *reinterpret_cast<const float4 *>(p0 + sp * sstride)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int sp = 0; sp < kMaxSplit; ++sp) {

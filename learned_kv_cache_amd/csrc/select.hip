@@ -1006,6 +1006,7 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     const size_t bctr_b = up(nseg * 4);
     const size_t info_b = up(nseg * 8);
+    const size_t hinfo_b = up(nseg * 12);
     const size_t cc_b = up(nseg * (size_t)nchunks * 4);
     const size_t thr_b = up(nseg * 8);
     const size_t bm_b = up(nseg * (size_t)nwords * 4);
@@ -1020,6 +1021,8 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
         p += bctr_b;
         out->info = reinterpret_cast<uint32_t *>(p);
         p += info_b;
+        out->hinfo = reinterpret_cast<uint32_t *>(p);
+        p += hinfo_b;
         out->ccount = reinterpret_cast<uint32_t *>(p);
         p += cc_b;
         out->acount = reinterpret_cast<uint32_t *>(p);
@@ -1042,7 +1045,7 @@ size_t select_ws_layout(int B, int Hq, int Lmax, void *base, SelectWs *out) {
         out->nwords = nwords;
         out->nchunks = nchunks;
     }
-    return bctr_b + info_b + 3 * cc_b + thr_b + bm_b + cand_b + samp_b + dbm_b + dc_b + hist_b;
+    return bctr_b + info_b + hinfo_b + 3 * cc_b + thr_b + bm_b + cand_b + samp_b + dbm_b + dc_b + hist_b;
 }
 
 namespace {
@@ -1140,7 +1143,17 @@ tb_status launch_score_select(const float *qhat, int n_slots, int slot, const vo
                               const int32_t *ctx, const int32_t *plen, float *scores, int B,
                               int Hq, int Hkv, int Lmax, int dp, int S, int W, int K, int r,
                               bool dilate, bool omit_window, int32_t *idx, int32_t *count,
-                              int cap, const SelectWs &ws, hipStream_t st, bool defer_list) {
+                              int cap, const SelectWs &ws, hipStream_t st, bool defer_list,
+                              bool defer_select) {
+    if (defer_select && !dilate &&
+        defer_select_fits(B, Hq, Hkv, Lmax, r, omit_window ? 0 : W, cap, ws)) {
+        // scores, histogram and classification only: tb_select_attn resolves
+        // the threshold, writes count and idx, and attends
+        return launch_score_hist_select(qhat, n_slots, slot, kp, ctx, plen, scores, B, Hq, Hkv,
+                                        Lmax, dp, S, W, K, r, false, omit_window, count, ws, st,
+                                        true);
+    }
+    defer_list = defer_list || defer_select;
     if (hist_route_fits(B * Hq, Lmax, Hq / Hkv, r, dilate) && ws.hist) {
         // scoring with an exact histogram of the pooled keys, then
         // classification against the bin that holds the budget's key

@@ -12,23 +12,6 @@ namespace {
 
 using namespace sel;
 
-// Wave-wide: lane l holds the word of tokens [t0, t0 + 32) (t0 ascending with
-// the lane) whose first set bit is list row `base` + (set bits of the lanes
-// below); each lane stages its own rows that fall in [lo, hi) at sm_tok[row -
-// lo]. Every lane takes part in the prefix count.
-__device__ __forceinline__ void emit_rows(uint32_t mine, int t0, uint32_t base, int lo, int hi,
-                                          int *sm_tok) {
-    const uint32_t pop = (uint32_t)__popc(mine);
-    uint32_t p = base + wave_incl_scan(pop) - pop;
-    if (p + pop <= (uint32_t)lo || p >= (uint32_t)hi) return;
-    while (mine) {
-        const int bit = __builtin_ctz(mine);
-        if (p >= (uint32_t)lo && p < (uint32_t)hi) sm_tok[p - lo] = t0 + bit;
-        ++p;
-        mine &= mine - 1u;
-    }
-}
-
 // Compaction and attention in one launch (tb_select_attn after a selection
 // with TB_SEL_DEFER_LIST; the fill mode, at most 64 chunks). Work items and
 // their order are those of the attention launch (b, KV head, split, query

@@ -37,11 +37,7 @@ namespace {
 
 using namespace sel;
 
-constexpr int HB = 12;                 // bits of the threshold histogram
-constexpr int HBINS = 1 << HB;
-constexpr int HSHIFT = 32 - HB;        // key32 >> HSHIFT = bin
 constexpr int TS = 1024;               // threads (one token each) of score_hist
-constexpr int MAXC = 64;               // chunks of a segment on this route
 
 template <int G, int DP, int R>
 __global__ __launch_bounds__(TS, G <= 4 ? 8 : 4) void score_hist_kernel(
@@ -198,14 +194,15 @@ struct HistSelLds {
     uint32_t ccnt[MAXC], acnt[MAXC], off[MAXC], chosen[MAXC];
 };
 
-template <int R>
+template <int R, bool PASS>
 __global__ __launch_bounds__(TSEL) void hist_select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx,
     const int32_t *__restrict__ plen, int Hq, int Lmax, int S, int W, int K, int omit_window,
     uint32_t *__restrict__ hist, uint32_t *__restrict__ sub, uint32_t *__restrict__ arrive,
     int nchunks, uint32_t *__restrict__ ccount, uint32_t *__restrict__ acount,
     uint64_t *__restrict__ cand, uint32_t *__restrict__ bitmap, int nwords,
-    uint64_t *__restrict__ thr_out, uint32_t *__restrict__ coff, int32_t *__restrict__ count) {
+    uint64_t *__restrict__ thr_out, uint32_t *__restrict__ coff, int32_t *__restrict__ count,
+    uint32_t *__restrict__ hinfo) {
     static_assert(R >= 0 && R <= 2, "the halo lanes hold radius 2");
     static_assert(TSEL * 4 == HBINS, "four bins per thread");
     static_assert(TPC * MAXC == TSEL && (CHUNK / 32) == 64, "chunk bookkeeping");
@@ -315,6 +312,12 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
     }
     const uint32_t bstar = sh.m[0], A = sh.m[1], C = sh.m[2];
     const bool have_bin = C > 0;   // else the histogram does not hold the budget's rank
+    if (PASS && part == 0 && tid == 0) {
+        // for the attention launch that resolves the threshold
+        hinfo[(size_t)seg * 3] = bstar;
+        hinfo[(size_t)seg * 3 + 1] = A;
+        hinfo[(size_t)seg * 3 + 2] = C;
+    }
 
     // 2. the pass over this workgroup's chunks
     if (have_bin) {
@@ -406,9 +409,13 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
                         const uint32_t low = ((uint32_t)(0xffffff - c) << 8) |
                                              ((uint32_t)(0x7f - d) << 1) |
                                              (uint32_t)(t <= c ? 1 : 0);
-                        if (slot < (uint32_t)CHUNK && (c_lo + ci) * CHUNK + (int)slot < Lmax)
-                            __hip_atomic_store(cl + slot, ((uint64_t)bk << 32) | low,
-                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (slot < (uint32_t)CHUNK && (c_lo + ci) * CHUNK + (int)slot < Lmax) {
+                            if constexpr (PASS)
+                                cl[slot] = ((uint64_t)bk << 32) | low;
+                            else
+                                __hip_atomic_store(cl + slot, ((uint64_t)bk << 32) | low,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        }
                     }
                     first += (uint32_t)__popcll(cm[j]);
                 }
@@ -422,15 +429,24 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
     // before the arrival is counted, and the last workgroup reads them with
     // agent-scope loads. (Release / acquire fences instead write back and
     // invalidate the whole L2 of the XCD: measured about 10 us here.)
-    for (int w = tid; w < (c_hi - c_lo) * 64; w += TSEL)
-        if (c_lo * 64 + w < nwords)
-            __hip_atomic_store(bitmap + (size_t)seg * nwords + c_lo * 64 + w, sh.u.p.bm[w],
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (PASS: the state is read by the next launch only, so plain stores)
+    for (int w = tid; w < (c_hi - c_lo) * 64; w += TSEL) {
+        if (c_lo * 64 + w < nwords) {
+            uint32_t *dst = bitmap + (size_t)seg * nwords + c_lo * 64 + w;
+            if constexpr (PASS) *dst = sh.u.p.bm[w];
+            else __hip_atomic_store(dst, sh.u.p.bm[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
     if (tid < c_hi - c_lo) {
-        __hip_atomic_store(ccount + (size_t)seg * nchunks + c_lo + tid, sh.cc[tid],
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(acount + (size_t)seg * nchunks + c_lo + tid, sh.ac[tid],
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t *dc = ccount + (size_t)seg * nchunks + c_lo + tid;
+        uint32_t *da = acount + (size_t)seg * nchunks + c_lo + tid;
+        if constexpr (PASS) {
+            *dc = sh.cc[tid];
+            *da = sh.ac[tid];
+        } else {
+            __hip_atomic_store(dc, sh.cc[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(da, sh.ac[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     if (have_bin) {
         // adjacent bins as one 64-bit atomic (counts never carry out of 32 bits)
@@ -443,6 +459,8 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
             __hip_atomic_fetch_add(sb + 1, (uint64_t)sv.z | ((uint64_t)sv.w << 32),
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // PASS: the attention launch resolves the threshold (no arrival here)
+    if constexpr (PASS) return;
     // arrival: every wave's stores complete before the barrier, then one
     // counter increment per workgroup
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -668,7 +686,7 @@ tb_status launch_score_hist_select(const float *qhat, int n_slots, int slot, con
                                    const int32_t *ctx, const int32_t *plen, float *scores, int B,
                                    int Hq, int Hkv, int Lmax, int dp, int S, int W, int K, int r,
                                    bool dilate, bool omit_window, int32_t *count,
-                                   const SelectWs &ws, hipStream_t st) {
+                                   const SelectWs &ws, hipStream_t st, bool pass_only) {
     const int rk = dilate ? 0 : r;
     const int g = Hq / Hkv;
     score_hist_fn fn = nullptr;
@@ -693,14 +711,18 @@ tb_status launch_score_hist_select(const float *qhat, int n_slots, int slot, con
                        Hkv, Lmax, S, W, K, nxs, ws.hist);
     tb_status e = check_launch("tb_score_select(score + histogram)");
     if (e) return e;
-    auto sel = rk == 0 ? hist_select_kernel<0> : rk == 1 ? hist_select_kernel<1>
-                                                         : hist_select_kernel<2>;
+    auto sel = pass_only ? (rk == 0   ? hist_select_kernel<0, true>
+                            : rk == 1 ? hist_select_kernel<1, true>
+                                      : hist_select_kernel<2, true>)
+                         : (rk == 0   ? hist_select_kernel<0, false>
+                            : rk == 1 ? hist_select_kernel<1, false>
+                                      : hist_select_kernel<2, false>);
     const int nparts = (ws.nchunks + CPW - 1) / CPW;
     hipLaunchKernelGGL(sel, dim3(nparts, B * Hq), dim3(TSEL), 0, st, scores, ctx, plen, Hq, Lmax,
                        S, W, K, omit_window ? 1 : 0, ws.hist, ws.hist + (size_t)B * Hq * HBINS,
                        ws.bctr, ws.nchunks, ws.ccount, ws.acount, ws.cand, ws.bitmap, ws.nwords,
-                       ws.thr, ws.coff, count);
-    return check_launch("tb_score_select(select)");
+                       ws.thr, ws.coff, count, ws.hinfo);
+    return check_launch(pass_only ? "tb_score_select(classify)" : "tb_score_select(select)");
 }
 
 }  // namespace tb

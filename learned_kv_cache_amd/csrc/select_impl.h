@@ -15,6 +15,12 @@ namespace sel {
 constexpr int CHUNK = 2048;          // tokens per classify workgroup
 constexpr int MAXR = 64;             // largest neighbour radius
 constexpr int GMAX = 64;             // boundary group size ranked directly
+// the histogram route: 4096 bins of the 12 high bits of key32 (sign,
+// exponent, three mantissa bits), at most 64 chunks per segment
+constexpr int HB = 12;
+constexpr int HBINS = 1 << HB;
+constexpr int HSHIFT = 32 - HB;      // key32 >> HSHIFT = bin
+constexpr int MAXC = 64;
 
 struct Region {
     int L, P, e0, e1, need;
@@ -120,6 +126,23 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
         if (lane >= off) x += y;
     }
     return x;
+}
+
+// Wave-wide: lane l holds the word of tokens [t0, t0 + 32) (t0 ascending with
+// the lane) whose first set bit is list row `base` + (set bits of the lanes
+// below); each lane stages its own rows that fall in [lo, hi) at sm_tok[row -
+// lo]. Every lane takes part in the prefix count.
+__device__ __forceinline__ void emit_rows(uint32_t mine, int t0, uint32_t base, int lo, int hi,
+                                          int *sm_tok) {
+    const uint32_t pop = (uint32_t)__popc(mine);
+    uint32_t p = base + wave_incl_scan(pop) - pop;
+    if (p + pop <= (uint32_t)lo || p >= (uint32_t)hi) return;
+    while (mine) {
+        const int bit = __builtin_ctz(mine);
+        if (p >= (uint32_t)lo && p < (uint32_t)hi) sm_tok[p - lo] = t0 + bit;
+        ++p;
+        mine &= mine - 1u;
+    }
 }
 
 // Pooled key of eligible token t read straight from the scores (global).
@@ -239,9 +262,9 @@ template <int NT, class Visit>
 __device__ __forceinline__ uint64_t kth_largest(const Visit &visit, int k, uint64_t prefix,
                                                 uint64_t mask, int shift, int grp,
                                                 KthLds<NT> &sh) {
-    static_assert(NT == 256 || NT == 1024, "one radix bin per thread");
+    static_assert(NT == 256 || NT == 512 || NT == 1024, "one radix bin per thread");
     constexpr int RBINS = NT;
-    constexpr int RBITS = NT == 1024 ? 10 : 8;
+    constexpr int RBITS = NT == 1024 ? 10 : (NT == 512 ? 9 : 8);
     const int tid = threadIdx.x;
     while (grp > GMAX && shift > 0) {
         const int width = shift < RBITS ? shift : RBITS;

@@ -274,12 +274,14 @@ tb_status check_select(const char *fn, const int32_t *ctx_len, const int32_t *pr
     TB_REQUIRE(sink >= 0 && window >= 0 && budget >= 0 && radius >= 0, TB_ERR_INVALID_ARGUMENT,
                "%s: negative sink/window/budget/radius", fn);
     TB_REQUIRE(radius <= 64, TB_ERR_UNSUPPORTED_SHAPE, "%s: radius > 64", fn);
-    TB_REQUIRE((mode & ~(0xff | TB_SEL_OMIT_WINDOW | TB_SEL_DEFER_LIST)) == 0,
+    TB_REQUIRE((mode & ~(0xff | TB_SEL_OMIT_WINDOW | TB_SEL_DEFER_LIST | TB_SEL_DEFER_SELECT)) == 0,
                TB_ERR_INVALID_ARGUMENT, "%s: unknown mode bits 0x%x", fn, mode);
     TB_REQUIRE((mode & 0xff) == TB_NF_FILL || (mode & 0xff) == TB_NF_DILATE,
                TB_ERR_INVALID_ARGUMENT, "%s: unknown neighbour mode %d", fn, mode & 0xff);
-    TB_REQUIRE(!((mode & TB_SEL_DEFER_LIST) && (mode & 0xff) == TB_NF_DILATE),
-               TB_ERR_INVALID_ARGUMENT, "%s: TB_SEL_DEFER_LIST needs TB_NF_FILL", fn);
+    TB_REQUIRE(!((mode & (TB_SEL_DEFER_LIST | TB_SEL_DEFER_SELECT)) &&
+                 (mode & 0xff) == TB_NF_DILATE),
+               TB_ERR_INVALID_ARGUMENT, "%s: TB_SEL_DEFER_LIST / TB_SEL_DEFER_SELECT need TB_NF_FILL",
+               fn);
     const bool omit = (mode & TB_SEL_OMIT_WINDOW) != 0;
     const bool dilate = (mode & 0xff) == TB_NF_DILATE;
     const long long imp = dilate ? (2LL * radius + 1) * budget : (long long)budget;
@@ -303,6 +305,8 @@ tb_status tb_select(const float *scores, const int32_t *ctx_len, const int32_t *
                     void *stream) {
     TB_REQUIRE(scores, TB_ERR_INVALID_ARGUMENT, "tb_select: null pointer");
     TB_REQUIRE(aligned4(scores), TB_ERR_INVALID_ARGUMENT, "tb_select: misaligned pointer");
+    TB_REQUIRE((mode & TB_SEL_DEFER_SELECT) == 0, TB_ERR_INVALID_ARGUMENT,
+               "tb_select: TB_SEL_DEFER_SELECT is a mode of tb_score_select only");
     tb::SelectWs ws;
     const tb_status e = check_select("tb_select", ctx_len, proj_len, B, Hq, Lmax, sink, window,
                                      budget, radius, mode, idx, count, cap, workspace, ws_bytes,
@@ -338,7 +342,8 @@ tb_status tb_score_select(const float *qhat, int n_slots, int slot, const void *
                                    (mode & 0xff) == TB_NF_DILATE,
                                    (mode & TB_SEL_OMIT_WINDOW) != 0, idx, count, cap, ws,
                                    static_cast<hipStream_t>(stream),
-                                   (mode & TB_SEL_DEFER_LIST) != 0);
+                                   (mode & TB_SEL_DEFER_LIST) != 0,
+                                   (mode & TB_SEL_DEFER_SELECT) != 0);
 }
 
 tb_status tb_select_attn(const int32_t *ctx_len, const int32_t *proj_len, int B, int Hq, int Hkv,
@@ -358,8 +363,9 @@ tb_status tb_select_attn(const int32_t *ctx_len, const int32_t *proj_len, int B,
     TB_REQUIRE((long long)Lmax * D * 2 <= 0x7fffffffLL, TB_ERR_UNSUPPORTED_SHAPE,
                "tb_select_attn: one head's cache must be below 2 GiB (Lmax * D * 2)");
     TB_REQUIRE(scale == scale, TB_ERR_INVALID_ARGUMENT, "tb_select_attn: scale is NaN");
-    TB_REQUIRE((mode & TB_SEL_DEFER_LIST) != 0, TB_ERR_INVALID_ARGUMENT,
-               "tb_select_attn: mode must carry TB_SEL_DEFER_LIST, as the selection it follows");
+    TB_REQUIRE((mode & (TB_SEL_DEFER_LIST | TB_SEL_DEFER_SELECT)) != 0, TB_ERR_INVALID_ARGUMENT,
+               "tb_select_attn: mode must carry TB_SEL_DEFER_LIST or TB_SEL_DEFER_SELECT, as the "
+               "selection it follows");
     tb::SelectWs ws;
     const tb_status e = check_select("tb_select_attn", ctx_len, proj_len, B, Hq, Lmax, sink, window,
                                      budget, radius, mode, idx, count, cap, sel_workspace,
@@ -372,6 +378,13 @@ tb_status tb_select_attn(const int32_t *ctx_len, const int32_t *proj_len, int B,
     float *part;
     uint32_t *ctr;
     tb::attn_ws_layout(B, Hq, cap, D, attn_workspace, &part, &ctr);
+    if ((mode & TB_SEL_DEFER_SELECT) &&
+        tb::defer_select_fits(B, Hq, Hkv, Lmax, radius,
+                              (mode & TB_SEL_OMIT_WINDOW) ? 0 : window, cap, ws))
+        return tb::launch_hist_attn(ctx_len, proj_len, B, Hq, Hkv, Lmax, sink, window, budget,
+                                    radius, (mode & TB_SEL_OMIT_WINDOW) != 0, idx, count, cap, ws,
+                                    q, k_cache, v_cache, D, scale, out, part, ctr,
+                                    static_cast<hipStream_t>(stream));
     return tb::launch_select_attn(ctx_len, proj_len, B, Hq, Hkv, Lmax, sink, window, budget,
                                   (mode & TB_SEL_OMIT_WINDOW) != 0, idx, count, cap, ws, q,
                                   k_cache, v_cache, D, scale, out, part, ctr,

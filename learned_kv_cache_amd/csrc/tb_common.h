@@ -116,6 +116,7 @@ struct SelectWs {
     uint32_t *dcount;    // [nseg][nchunks] widened tokens per chunk (dilation mode)
     uint32_t *hist;      // [2][nseg][4096] the histogram route's two histograms, zero
                          // at rest (null off that route's sizes)
+    uint32_t *hinfo;     // [nseg][3] the histogram route's bin B*, tokens above it, in it
     int nwords;
     int nchunks;
 };
@@ -133,7 +134,17 @@ tb_status launch_score_hist_select(const float *qhat, int n_slots, int slot, con
                                    const int32_t *ctx, const int32_t *plen, float *scores, int B,
                                    int Hq, int Hkv, int Lmax, int dp, int S, int W, int K, int r,
                                    bool dilate, bool omit_window, int32_t *count,
-                                   const SelectWs &ws, hipStream_t st);
+                                   const SelectWs &ws, hipStream_t st, bool pass_only = false);
+// The split form of tb_score_select + tb_select_attn (TB_SEL_DEFER_SELECT):
+// on the histogram route, with chunk-aligned attention splits that fit the
+// attention workspace of cap rows; both calls decide it alike.
+bool defer_select_fits(int B, int Hq, int Hkv, int Lmax, int r, int win, int cap,
+                       const SelectWs &ws);
+tb_status launch_hist_attn(const int32_t *ctx, const int32_t *plen, int B, int Hq, int Hkv,
+                           int Lmax, int S, int W, int K, int r, bool omit_window, int32_t *idx,
+                           int32_t *count, int cap, const SelectWs &ws, const void *q,
+                           const void *kc, const void *vc, int D, float scale, float *out,
+                           float *part, uint32_t *ctr, hipStream_t st);
 tb_status launch_select(const float *scores, const int32_t *ctx, const int32_t *plen, int B,
                         int Hq, int Lmax, int S, int W, int K, int r, bool dilate,
                         bool omit_window, int32_t *idx, int32_t *count, int cap,
@@ -143,7 +154,7 @@ tb_status launch_score_select(const float *qhat, int n_slots, int slot, const vo
                               int Hq, int Hkv, int Lmax, int dp, int S, int W, int K, int r,
                               bool dilate, bool omit_window, int32_t *idx, int32_t *count,
                               int cap, const SelectWs &ws, hipStream_t st,
-                              bool defer_list = false);
+                              bool defer_list = false, bool defer_select = false);
 tb_status launch_compact(const int32_t *ctx, const int32_t *plen, int B, int Hq, int Lmax, int S,
                          int W, int K, bool omit_window, int32_t *idx, int cap, const SelectWs &ws,
                          hipStream_t st);
