@@ -309,7 +309,7 @@ def test_select_threshold_staging_beyond_prefetched_slots(tb, orc, r):
     ws = assert_same_selection(orc, tb, s, [L], [L], S, W, K, r, "staging r=%d" % r)
     up = lambda x: (x + 255) // 256 * 256
     nseg, nchunks = B * Hq, -(-L // 2048)
-    off = up(nseg * 4) + up(nseg * 8)
+    off = up(nseg * 4) + up(nseg * 8) + up(nseg * 12)   # counters, band, bin info
     cc = host(ws[off: off + nseg * nchunks * 4].view(torch.int32)).reshape(nseg, nchunks)
     assert nchunks <= 32
     assert (cc.max(axis=1) > 96).all() and (cc.sum(axis=1) <= 8192).all(), cc
@@ -326,7 +326,7 @@ def test_select_threshold_candidates_beyond_lds(tb, orc):
     ws = assert_same_selection(orc, tb, s, [L], [L], S, W, K, 0, "candidates beyond LDS")
     up = lambda x: (x + 255) // 256 * 256
     nseg, nchunks = B * Hq, -(-L // 2048)
-    off = up(nseg * 4) + up(nseg * 8)
+    off = up(nseg * 4) + up(nseg * 8) + up(nseg * 12)   # counters, band, bin info
     cc = host(ws[off: off + nseg * nchunks * 4].view(torch.int32)).reshape(nseg, nchunks)
     assert nchunks <= 32 and (cc.sum(axis=1) > 8192).all(), cc.sum(axis=1)
 
