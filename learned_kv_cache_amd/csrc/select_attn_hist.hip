@@ -41,11 +41,13 @@ constexpr int kMaxWinShare = 512;
 // attention rows per pass: 128 keeps the kernel within 64 VGPRs (four
 // workgroups per CU) without spilling
 constexpr int kRowsPerPass = 128;
-static_assert(BPT == 8 && NT / MAXC == 8 && CHUNK % kAttnCH == 0, "bookkeeping below");
+static_assert(BPT == 8 && NT / MAXC == 8 && CHUNK % kAttnCH == 0 && NT * 4 == CHUNK,
+              "bookkeeping below");
 
 struct HistAttnLds {
     KthLds<NT> k;
     uint32_t word[CHUNK / 32];      // the chunk's row bits
+    uint32_t wrow[CHUNK / 32];      // list row of each word's first bit, within the chunk
     uint32_t ccnt[MAXC], acnt[MAXC], chosen[MAXC], off[MAXC];
     uint32_t m[8];
     int tok[CHUNK + kMaxWinShare];  // the chunk's rows, then its share of the window
@@ -242,7 +244,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
     }
     __syncthreads();
 
-    // 3. chunk offsets of the list; the count; the chunk's rows, ascending
+    // 3. chunk offsets of the list; the count; the list row of each word's
+    // first bit
     if (wave == 0) {
         if (partial) {
             uint32_t v = 0u;
@@ -258,10 +261,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
         } else {
             sh.off[lane] = off_l;
         }
-        const uint32_t mine = sh.word[lane];
-        emit_rows(mine, (c * (CHUNK / 32) + lane) << 5, 0u, 0, CHUNK, sh.tok);
-        const uint32_t tot = wave_incl_scan((uint32_t)__popc(mine));
-        if (lane == 63) sh.m[3] = tot;
+        const uint32_t pop = (uint32_t)__popc(sh.word[lane]);
+        const uint32_t incl = wave_incl_scan(pop);
+        sh.wrow[lane] = incl - pop;
+        if (lane == 63) sh.m[3] = incl;
     }
     __syncthreads();
     // this chunk's share of the window rows: they follow the sink and the
@@ -274,18 +277,35 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
     const int nrows = nch + nwin;
     const uint32_t off = sh.off[c];
     const uint32_t woff = (uint32_t)(slo + gr.need + ws0);
-    for (int i = tid; i < nrows; i += NT) {
-        const int t = i < nch ? sh.tok[i] : w0 + ws0 + (i - nch);
-        const uint32_t pos = i < nch ? off + (uint32_t)i : woff + (uint32_t)(i - nch);
-        if (pos < (uint32_t)cap) idx[(size_t)seg * cap + pos] = t;
-        sh.tok[i] = t < 0 ? 0 : (t >= Lmax ? Lmax - 1 : t);
+    {
+        // the chunk's rows, ascending, to the row table: every thread takes
+        // four bits of one word (a wave alone would walk up to 32 bits per
+        // lane while the CU's other workgroups attend). Every row lies in
+        // [0, L), so the table holds the list's values.
+        const int wi = tid >> 3, nib = (tid & 7) * 4;
+        const uint32_t word = sh.word[wi];
+        uint32_t left = (word >> nib) & 15u;
+        uint32_t p = sh.wrow[wi] + (uint32_t)__popc(word & ((1u << nib) - 1u));
+        const int tb = ((c * (CHUNK / 32) + wi) << 5) + nib;
+        while (left) {
+            sh.tok[p++] = tb + __builtin_ctz(left);
+            left &= left - 1u;
+        }
     }
+    for (int i = tid; i < nwin; i += NT) sh.tok[nch + i] = w0 + ws0 + i;
     __syncthreads();
 
     // 4. attention over the chunk's rows; the last split of the head merges
     float m, l, acc[8];
     attn_rows<D, kRowsPerPass>(q, kc, vc, Hkv, Lmax, scale_log2, b, kvh, seg, nrows, sh.tok, m, l,
                                acc);
+    // the chunk's rows to the list only now: stores issued while the CU's
+    // other workgroups stream K/V wait for the memory pipeline, and nothing
+    // in this launch reads them
+    for (int i = tid; i < nrows; i += NT) {
+        const uint32_t pos = i < nch ? off + (uint32_t)i : woff + (uint32_t)(i - nch);
+        if (pos < (uint32_t)cap) idx[(size_t)seg * cap + pos] = sh.tok[i];
+    }
     if (attn_store_merge<D>(m, l, acc, nchunks, part, ctr, out, seg, c)) {
         // every workgroup of the segment has read the histograms
         for (int i = tid; i < HBINS / 4; i += NT) {
