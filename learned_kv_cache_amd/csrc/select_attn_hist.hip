@@ -19,10 +19,11 @@
 // sub-bin ranked directly) and counts every chunk's chosen candidates, so it
 // knows the list offset of its chunk without waiting for any other
 // workgroup; every workgroup of the segment reaches the same threshold. It
-// writes its chunk's rows to the list (bitmap words, chosen candidates, sink
-// and window, ascending) and attends over them, kAttnCH rows per pass; the
-// last split of the head to arrive merges the partials and clears both
-// histograms for the next call. Counts that disagree with the histograms (a
+// attends over its chunk's rows (bitmap words, chosen candidates, sink and a
+// share of the window, ascending), 128 rows per pass, and writes them to the
+// list; the last split of the head to arrive merges the partials and clears
+// the second histogram, and every workgroup clears a share of the first one
+// for the next call. Counts that disagree with the histograms (a
 // workspace that was not zero at first use) are reported as an invalid
 // segment (count -1, out 0); the next call is exact again.
 #include "attn_impl.h"
@@ -79,16 +80,6 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
     const int b = rest / Hkv;
     const int seg = b * Hq + kvh * g + hg;   // the selection's segment, the attention's head
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const Region gr = region(ctx, plen, b, Lmax, S, W, K);
-    const int L = gr.L;
-    const int nE = gr.e1 - gr.e0;
-    const bool partial = !gr.bad && gr.need > 0 && gr.need < nE;
-    const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
-    const int slo = S < L ? S : L;
-    // window-only rows [w0, L) (rows below slo are sink rows) are the list's
-    // last rows; they are shared out evenly over the segment's chunk splits
-    // (the window's own chunk would otherwise hold about twice the rows)
-    const int w0 = wlo > slo ? wlo : slo;
     uint4 *hs = reinterpret_cast<uint4 *>(hist + (size_t)seg * HBINS);
     uint4 *ss = reinterpret_cast<uint4 *>(hist + (size_t)(nseg + seg) * HBINS);
     const uint64_t *cseg = cand + (size_t)seg * Lmax;
@@ -99,36 +90,42 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
     const int tpc = (NT >> lgc) < 64 ? (NT >> lgc) : 64;
     const int pch = tid / tpc, pln = tid % tpc;
 
-    // 1. the one round trip
-    uint4 h0 = make_uint4(0u, 0u, 0u, 0u), h1 = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t bstar = 0u, A = 0u, C = 0u, cc_l = 0u, ac_l = 0u, off_l = 0u, bits = 0u;
+    // 1. the one round trip, requested before the lengths arrive: every
+    // address lies in the workspace whatever they are, and what a segment's
+    // lengths make unused is ignored below
+    // bins 4095 - 8 tid - j, j < 8: descending thread order
+    const uint4 *sq = ss + HBINS / 4 - 2 * (tid + 1);
+    const uint4 h0 = sq[1], h1 = sq[0];
+    const uint32_t bstar = hinfo[(size_t)seg * 3], A = hinfo[(size_t)seg * 3 + 1],
+                   C = hinfo[(size_t)seg * 3 + 2];
+    uint32_t cc_l = 0u, ac_l = 0u, bits = 0u;
+    if (tid < nchunks) {
+        cc_l = ccount[(size_t)seg * nchunks + tid];
+        ac_l = acount[(size_t)seg * nchunks + tid];
+    }
     uint64_t pv[PFC];
 #pragma unroll
-    for (int j = 0; j < PFC; ++j) pv[j] = 0ull;
-    if (partial) {
-        // bins 4095 - 8 tid - j, j < 8: descending thread order
-        const uint4 *sq = ss + HBINS / 4 - 2 * (tid + 1);
-        h0 = sq[1];
-        h1 = sq[0];
-        bstar = hinfo[(size_t)seg * 3];
-        A = hinfo[(size_t)seg * 3 + 1];
-        C = hinfo[(size_t)seg * 3 + 2];
-        if (tid < nchunks) {
-            cc_l = ccount[(size_t)seg * nchunks + tid];
-            ac_l = acount[(size_t)seg * nchunks + tid];
-        }
-#pragma unroll
-        for (int j = 0; j < PFC; ++j) {
-            const int slot = pln + tpc * j;
-            if (pch < nchunks && pch * CHUNK + slot < Lmax) pv[j] = cseg[(size_t)pch * CHUNK + slot];
-        }
-    } else if (!gr.bad && tid < nchunks) {
-        off_l = coff[(size_t)seg * nchunks + tid];   // all or none: offsets from the pass
+    for (int j = 0; j < PFC; ++j) {
+        const int slot = pln + tpc * j;
+        pv[j] = pch < nchunks && pch * CHUNK + slot < Lmax ? cseg[(size_t)pch * CHUNK + slot] : 0ull;
     }
-    if (!gr.bad && wave == 0) {
+    if (wave == 0) {
         const int w = c * (CHUNK / 32) + lane;
         bits = w < nwords ? bitmap[(size_t)seg * nwords + w] : 0u;
     }
+    // the first histogram is read by the classification pass only, which has
+    // ended: each workgroup clears its share of it for the next call
+    for (int i = c + nchunks * tid; i < HBINS / 4; i += nchunks * NT) hs[i] = make_uint4(0u, 0u, 0u, 0u);
+    const Region gr = region(ctx, plen, b, Lmax, S, W, K);
+    const int L = gr.L;
+    const int nE = gr.e1 - gr.e0;
+    const bool partial = !gr.bad && gr.need > 0 && gr.need < nE;
+    const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
+    const int slo = S < L ? S : L;
+    // window-only rows [w0, L) (rows below slo are sink rows) are the list's
+    // last rows; they are shared out evenly over the segment's chunk splits
+    // (the window's own chunk would otherwise hold about twice the rows)
+    const int w0 = wlo > slo ? wlo : slo;
 
     // the chunk's sink rows and its tokens above B* (no window-only rows:
     // the eligible region ends below the window)
@@ -259,7 +256,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
                 thr_out[seg] = thr;
             }
         } else {
-            sh.off[lane] = off_l;
+            // all or none: offsets from the pass
+            sh.off[lane] = !gr.bad && lane < nchunks ? coff[(size_t)seg * nchunks + lane] : 0u;
         }
         const uint32_t pop = (uint32_t)__popc(sh.word[lane]);
         const uint32_t incl = wave_incl_scan(pop);
@@ -299,19 +297,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
     float m, l, acc[8];
     attn_rows<D, kRowsPerPass>(q, kc, vc, Hkv, Lmax, scale_log2, b, kvh, seg, nrows, sh.tok, m, l,
                                acc);
+    if (attn_store_merge<D>(m, l, acc, nchunks, part, ctr, out, seg, c)) {
+        // every workgroup of the segment has read the second histogram
+        for (int i = tid; i < HBINS / 4; i += NT) ss[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
     // the chunk's rows to the list only now: stores issued while the CU's
-    // other workgroups stream K/V wait for the memory pipeline, and nothing
-    // in this launch reads them
+    // other workgroups stream K/V wait for the memory pipeline (and the
+    // partial's stores above wait for every earlier store), and nothing in
+    // this launch reads them
     for (int i = tid; i < nrows; i += NT) {
         const uint32_t pos = i < nch ? off + (uint32_t)i : woff + (uint32_t)(i - nch);
         if (pos < (uint32_t)cap) idx[(size_t)seg * cap + pos] = sh.tok[i];
-    }
-    if (attn_store_merge<D>(m, l, acc, nchunks, part, ctr, out, seg, c)) {
-        // every workgroup of the segment has read the histograms
-        for (int i = tid; i < HBINS / 4; i += NT) {
-            hs[i] = make_uint4(0u, 0u, 0u, 0u);
-            ss[i] = make_uint4(0u, 0u, 0u, 0u);
-        }
     }
 }
 

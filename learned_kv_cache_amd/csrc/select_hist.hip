@@ -180,6 +180,128 @@ constexpr int TPC = TSEL / MAXC;           // last workgroup: threads per chunk
 constexpr int PFS = 12;                    // candidate slots each of them fetches early
 constexpr int NSW = (CPW * CHUNK / SS + NWSEL - 1) / NWSEL;   // steps per wave
 
+// Lane rotations of a wave through DPP (no LDS traffic): lane i takes the
+// value of lane i - n (rotr_lanes) or of lane i + n (rotl_lanes), modulo 64.
+__device__ __forceinline__ uint32_t rotr_lanes(uint32_t x, int n) {
+    for (int i = 0; i < n; ++i) x = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x13C, 0xF, 0xF, false);
+    return x;
+}
+__device__ __forceinline__ uint32_t rotl_lanes(uint32_t x, int n) {
+    for (int i = 0; i < n; ++i) x = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x134, 0xF, 0xF, false);
+    return x;
+}
+
+// One 256-token step of the classification pass, by one wave with every lane
+// active: lane l holds the scores of tokens base + l + 64 j in v[j] and, in
+// lanes l < R, those of base - R + l (hl) and base + 256 + l (hr); positions
+// outside the eligible range [e0, e1) take no part. A token's pooled key
+// takes its neighbours from the adjacent lanes. Tokens whose key lies above
+// bin bstar set their bits in the words bm (word 0: tokens 32 w0 onward) and
+// are counted in *ac; tokens of bin bstar take their chunk's next candidate
+// slots (counted in *cc; slots at or beyond lim are not written), their
+// 64-bit ranking keys go to cl[slot] and their next 12 key bits to the second
+// histogram sub. AGENT: the candidates are stored at agent scope.
+template <int R, bool AGENT>
+__device__ __forceinline__ void classify_step(int base, const float (&v)[4], float hl, float hr,
+                                              int e0, int e1, uint32_t bstar, uint32_t *bm,
+                                              int w0, uint32_t *ac, uint32_t *cc, uint32_t *sub,
+                                              uint64_t *cl, int lim) {
+    const int lane = threadIdx.x & 63;
+    auto kof = [&](int p, float x) -> uint32_t {
+        return (p >= e0 && p < e1) ? order_key(x) : 0u;
+    };
+    uint32_t k[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k[j] = kof(base + lane + 64 * j, v[j]);
+    const uint32_t hlk = lane < R ? kof(base - R + lane, hl) : 0u;
+    const uint32_t hrk = lane < R ? kof(base + SS + lane, hr) : 0u;
+    // keys of the window of token (lane, j): slot R + u is position t + u
+    uint32_t wk[4][2 * R + 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wk[j][R] = k[j];
+#pragma unroll
+    for (int u = 1; u <= R; ++u) {
+        uint32_t rm[4], rp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            rm[j] = rotr_lanes(k[j], u);
+            rp[j] = rotl_lanes(k[j], u);
+        }
+        const uint32_t hlu = rotl_lanes(hlk, R - u);
+        const uint32_t hru = rotl_lanes(hrk, u);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            wk[j][R - u] = lane >= u ? rm[j] : (j > 0 ? rm[j > 0 ? j - 1 : 0] : hlu);
+            wk[j][R + u] = lane + u <= 63 ? rp[j] : (j < 3 ? rp[j < 3 ? j + 1 : 3] : hru);
+        }
+    }
+    uint32_t best[4];
+    bool sel[4], isc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = base + lane + 64 * j;
+        uint32_t bk = 0u;
+#pragma unroll
+        for (int u = 0; u <= 2 * R; ++u) bk = wk[j][u] > bk ? wk[j][u] : bk;
+        best[j] = bk;
+        const bool el = t >= e0 && t < e1;
+        sel[j] = el && (bk >> HSHIFT) > bstar;
+        isc[j] = el && (bk >> HSHIFT) == bstar;
+    }
+    uint64_t cm[4];
+    uint32_t na = 0, ncw = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint64_t m = __ballot(sel[j]);
+        if (lane == 0) {
+            const int w = ((base + 64 * j) >> 5) - w0;
+            bm[w] = (uint32_t)m;
+            bm[w + 1] = (uint32_t)(m >> 32);
+        }
+        na += (uint32_t)__popcll(m);
+        cm[j] = __ballot(isc[j]);
+        ncw += (uint32_t)__popcll(cm[j]);
+    }
+    if (lane == 0 && na) atomicAdd(ac, na);
+    if (ncw) {
+        // candidate (lane, j) takes chunk slot first + (those of rows
+        // < j) + (lanes below it in row j); a chunk has CHUNK slots
+        uint32_t first = 0;
+        if (lane == 0) first = atomicAdd(cc, ncw);
+        first = (uint32_t)__builtin_amdgcn_readfirstlane((int)first);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (isc[j]) {
+                const int t = base + lane + 64 * j;
+                const uint32_t slot =
+                    first + (uint32_t)__popcll(cm[j] & ((1ull << lane) - 1ull));
+                atomicAdd(&sub[(best[j] >> 8) & (HBINS - 1)], 1u);
+                int c = t;
+                uint32_t bk = 0u;
+#pragma unroll
+                for (int u = 0; u <= 2 * R; ++u) {
+                    if (wk[j][u] > bk) {
+                        bk = wk[j][u];
+                        c = t - R + u;
+                    }
+                }
+                const int d = t < c ? c - t : t - c;
+                const uint32_t low = ((uint32_t)(0xffffff - c) << 8) |
+                                     ((uint32_t)(0x7f - d) << 1) |
+                                     (uint32_t)(t <= c ? 1 : 0);
+                if (slot < (uint32_t)CHUNK && (int)slot < lim) {
+                    if constexpr (AGENT)
+                        __hip_atomic_store(cl + slot, ((uint64_t)bk << 32) | low,
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        cl[slot] = ((uint64_t)bk << 32) | low;
+                }
+            }
+            first += (uint32_t)__popcll(cm[j]);
+        }
+    }
+}
+
 struct HistSelLds {
     union {
         struct {
@@ -194,15 +316,14 @@ struct HistSelLds {
     uint32_t ccnt[MAXC], acnt[MAXC], off[MAXC], chosen[MAXC];
 };
 
-template <int R, bool PASS>
+template <int R>
 __global__ __launch_bounds__(TSEL) void hist_select_kernel(
     const float *__restrict__ scores, const int32_t *__restrict__ ctx,
     const int32_t *__restrict__ plen, int Hq, int Lmax, int S, int W, int K, int omit_window,
     uint32_t *__restrict__ hist, uint32_t *__restrict__ sub, uint32_t *__restrict__ arrive,
     int nchunks, uint32_t *__restrict__ ccount, uint32_t *__restrict__ acount,
     uint64_t *__restrict__ cand, uint32_t *__restrict__ bitmap, int nwords,
-    uint64_t *__restrict__ thr_out, uint32_t *__restrict__ coff, int32_t *__restrict__ count,
-    uint32_t *__restrict__ hinfo) {
+    uint64_t *__restrict__ thr_out, uint32_t *__restrict__ coff, int32_t *__restrict__ count) {
     static_assert(R >= 0 && R <= 2, "the halo lanes hold radius 2");
     static_assert(TSEL * 4 == HBINS, "four bins per thread");
     static_assert(TPC * MAXC == TSEL && (CHUNK / 32) == 64, "chunk bookkeeping");
@@ -312,114 +433,17 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
     }
     const uint32_t bstar = sh.m[0], A = sh.m[1], C = sh.m[2];
     const bool have_bin = C > 0;   // else the histogram does not hold the budget's rank
-    if (PASS && part == 0 && tid == 0) {
-        // for the attention launch that resolves the threshold
-        hinfo[(size_t)seg * 3] = bstar;
-        hinfo[(size_t)seg * 3 + 1] = A;
-        hinfo[(size_t)seg * 3 + 2] = C;
-    }
 
     // 2. the pass over this workgroup's chunks
     if (have_bin) {
-        auto kof = [&](int p, float x) -> uint32_t {
-            return (p >= e0 && p < e1) ? order_key(x) : 0u;
-        };
 #pragma unroll
         for (int i = 0; i < NSW; ++i) {
             if (s0 + i >= s1) break;
             const int base = a0 + (s0 + i) * SS;
-            uint32_t k[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) k[j] = kof(base + lane + 64 * j, v[i][j]);
-            const uint32_t hlk = lane < R ? kof(base - R + lane, hl[i]) : 0u;
-            const uint32_t hrk = lane < R ? kof(base + SS + lane, hr[i]) : 0u;
-            // keys of the window of token (lane, j): slot R + u is position t + u
-            uint32_t wk[4][2 * R + 1];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wk[j][R] = k[j];
-#pragma unroll
-            for (int u = 1; u <= R; ++u) {
-                uint32_t rm[4], rp[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    rm[j] = (uint32_t)__shfl((int)k[j], (lane - u) & 63);
-                    rp[j] = (uint32_t)__shfl((int)k[j], (lane + u) & 63);
-                }
-                const uint32_t hlu = (uint32_t)__shfl((int)hlk, (lane - u + R) & 63);
-                const uint32_t hru = (uint32_t)__shfl((int)hrk, (lane + u) & 63);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    wk[j][R - u] = lane >= u ? rm[j] : (j > 0 ? rm[j > 0 ? j - 1 : 0] : hlu);
-                    wk[j][R + u] = lane + u <= 63 ? rp[j] : (j < 3 ? rp[j < 3 ? j + 1 : 3] : hru);
-                }
-            }
-            uint32_t best[4];
-            bool sel[4], isc[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = base + lane + 64 * j;
-                uint32_t bk = 0u;
-#pragma unroll
-                for (int u = 0; u <= 2 * R; ++u) bk = wk[j][u] > bk ? wk[j][u] : bk;
-                best[j] = bk;
-                const bool el = t >= e0 && t < e1;
-                sel[j] = el && (bk >> HSHIFT) > bstar;
-                isc[j] = el && (bk >> HSHIFT) == bstar;
-            }
             const int ci = (base >> 11) - c_lo;   // the step's chunk in the workgroup
-            uint64_t cm[4];
-            uint32_t na = 0, ncw = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint64_t m = __ballot(sel[j]);
-                if (lane == 0) {
-                    const int w = ((base + 64 * j) >> 5) - c_lo * 64;   // < CPW * 64
-                    sh.u.p.bm[w] = (uint32_t)m;
-                    sh.u.p.bm[w + 1] = (uint32_t)(m >> 32);
-                }
-                na += (uint32_t)__popcll(m);
-                cm[j] = __ballot(isc[j]);
-                ncw += (uint32_t)__popcll(cm[j]);
-            }
-            if (lane == 0 && na) atomicAdd(&sh.ac[ci], na);
-            if (ncw) {
-                // candidate (lane, j) takes chunk slot first + (those of rows
-                // < j) + (lanes below it in row j); a chunk has CHUNK slots
-                uint32_t first = 0;
-                if (lane == 0) first = atomicAdd(&sh.cc[ci], ncw);
-                first = (uint32_t)__shfl((int)first, 0);
-                uint64_t *cl = cseg + (size_t)(c_lo + ci) * CHUNK;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if (isc[j]) {
-                        const int t = base + lane + 64 * j;
-                        const uint32_t slot =
-                            first + (uint32_t)__popcll(cm[j] & ((1ull << lane) - 1ull));
-                        atomicAdd(&sh.u.p.sub[(best[j] >> 8) & (HBINS - 1)], 1u);
-                        int c = t;
-                        uint32_t bk = 0u;
-#pragma unroll
-                        for (int u = 0; u <= 2 * R; ++u) {
-                            if (wk[j][u] > bk) {
-                                bk = wk[j][u];
-                                c = t - R + u;
-                            }
-                        }
-                        const int d = t < c ? c - t : t - c;
-                        const uint32_t low = ((uint32_t)(0xffffff - c) << 8) |
-                                             ((uint32_t)(0x7f - d) << 1) |
-                                             (uint32_t)(t <= c ? 1 : 0);
-                        if (slot < (uint32_t)CHUNK && (c_lo + ci) * CHUNK + (int)slot < Lmax) {
-                            if constexpr (PASS)
-                                cl[slot] = ((uint64_t)bk << 32) | low;
-                            else
-                                __hip_atomic_store(cl + slot, ((uint64_t)bk << 32) | low,
-                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                    }
-                    first += (uint32_t)__popcll(cm[j]);
-                }
-            }
+            classify_step<R, true>(base, v[i], hl[i], hr[i], e0, e1, bstar, sh.u.p.bm, c_lo * 64,
+                                   &sh.ac[ci], &sh.cc[ci], sh.u.p.sub,
+                                   cseg + (size_t)(c_lo + ci) * CHUNK, Lmax - (c_lo + ci) * CHUNK);
         }
     }
     __syncthreads();
@@ -429,24 +453,16 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
     // before the arrival is counted, and the last workgroup reads them with
     // agent-scope loads. (Release / acquire fences instead write back and
     // invalidate the whole L2 of the XCD: measured about 10 us here.)
-    // (PASS: the state is read by the next launch only, so plain stores)
     for (int w = tid; w < (c_hi - c_lo) * 64; w += TSEL) {
-        if (c_lo * 64 + w < nwords) {
-            uint32_t *dst = bitmap + (size_t)seg * nwords + c_lo * 64 + w;
-            if constexpr (PASS) *dst = sh.u.p.bm[w];
-            else __hip_atomic_store(dst, sh.u.p.bm[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (c_lo * 64 + w < nwords)
+            __hip_atomic_store(bitmap + (size_t)seg * nwords + c_lo * 64 + w, sh.u.p.bm[w],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid < c_hi - c_lo) {
-        uint32_t *dc = ccount + (size_t)seg * nchunks + c_lo + tid;
-        uint32_t *da = acount + (size_t)seg * nchunks + c_lo + tid;
-        if constexpr (PASS) {
-            *dc = sh.cc[tid];
-            *da = sh.ac[tid];
-        } else {
-            __hip_atomic_store(dc, sh.cc[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(da, sh.ac[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
+        __hip_atomic_store(ccount + (size_t)seg * nchunks + c_lo + tid, sh.cc[tid],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(acount + (size_t)seg * nchunks + c_lo + tid, sh.ac[tid],
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (have_bin) {
         // adjacent bins as one 64-bit atomic (counts never carry out of 32 bits)
@@ -459,8 +475,6 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
             __hip_atomic_fetch_add(sb + 1, (uint64_t)sv.z | ((uint64_t)sv.w << 32),
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    // PASS: the attention launch resolves the threshold (no arrival here)
-    if constexpr (PASS) return;
     // arrival: every wave's stores complete before the barrier, then one
     // counter increment per workgroup
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -660,6 +674,175 @@ __global__ __launch_bounds__(TSEL) void hist_select_kernel(
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// hist_pass: the classification alone, for tb_select_attn to resolve the
+// threshold (TB_SEL_DEFER_SELECT). One 512-thread workgroup per (segment,
+// chunk), each wave one 256-token step of the chunk: the bin B* from the
+// segment's histogram (eight bins per thread), then the pass of hist_select
+// over the chunk; the chunk's bitmap words, candidate and above-bin counts,
+// its candidates and its part of the second histogram are stored for the
+// next launch (plain stores), and the first chunk's workgroup stores B*, A
+// and C. No workgroup waits for another; four of them share a CU.
+constexpr int TP = 512;                    // threads of hist_pass
+constexpr int NWP = TP / 64;               // its waves, one step each
+static_assert(NWP * SS == CHUNK && TP * 8 == HBINS, "one step per wave, eight bins per thread");
+
+struct HistPassLds {
+    uint32_t bm[CHUNK / 32];   // the chunk's bitmap words
+    uint32_t sub[HBINS];       // its second histogram
+    uint32_t w[NWP];           // block scan
+    uint32_t cc, ac;           // candidates, tokens above B*
+    uint32_t m[3];             // B*, A, C
+};
+
+template <int R>
+__global__ __launch_bounds__(TP) void hist_pass_kernel(
+    const float *__restrict__ scores, const int32_t *__restrict__ ctx,
+    const int32_t *__restrict__ plen, int Hq, int Lmax, int S, int W, int K, int omit_window,
+    uint32_t *__restrict__ hist, uint32_t *__restrict__ sub, int nchunks,
+    uint32_t *__restrict__ ccount, uint32_t *__restrict__ acount, uint64_t *__restrict__ cand,
+    uint32_t *__restrict__ bitmap, int nwords, uint32_t *__restrict__ coff,
+    int32_t *__restrict__ count, uint32_t *__restrict__ hinfo, int n_items) {
+    static_assert(R >= 0 && R <= 2, "the halo lanes hold radius 2");
+    __shared__ __align__(16) HistPassLds sh;
+    // XCD-aware order: the chunks of a segment on one XCD (workgroups are
+    // dealt to the 8 XCDs in turn), so its histogram is read from that XCD's
+    // L2 after the first miss
+    const int nb = gridDim.x, bid = blockIdx.x;
+    const int item = (bid & 7) * (nb >> 3) + (bid >> 3);
+    if (item >= n_items) return;
+    const int c = item % nchunks, seg = item / nchunks, b = seg / Hq;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint4 *hs = reinterpret_cast<uint4 *>(hist + (size_t)seg * HBINS);
+    uint4 *ss = reinterpret_cast<uint4 *>(sub + (size_t)seg * HBINS);
+    const float *sc = scores + (size_t)seg * Lmax;
+    // bins 4095 - 8 tid - j, j < 8 (descending thread order), and this wave's
+    // step, requested before the lengths arrive (scores from addresses clamped
+    // into the cache; values at positions outside E are never used)
+    const uint4 *sq = hs + HBINS / 4 - 2 * (tid + 1);
+    const uint4 h0 = sq[1], h1 = sq[0];
+    const int base = c * CHUNK + wave * SS;
+    auto clampL = [&](int p) { return p < 0 ? 0 : (p >= Lmax ? Lmax - 1 : p); };
+    float v[4], hl = 0.f, hr = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = sc[clampL(base + lane + 64 * j)];
+    if (R > 0) {
+        hl = sc[clampL(base - R + lane)];
+        hr = sc[clampL(base + SS + lane)];
+    }
+    const Region g = region(ctx, plen, b, Lmax, S, W, K);
+    const int nE = g.e1 - g.e0;
+    const bool partial = !g.bad && g.need > 0 && g.need < nE;
+    const int L = g.L;
+    const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
+    const int slo = S < L ? S : L;
+    const int e0 = g.e0, e1 = g.e1;
+    const bool act = partial && base < e1;
+
+    if (!partial) {
+        // every eligible token or none: the chunk's words; the first chunk's
+        // workgroup writes every chunk's offset and the count, and clears
+        // both histograms (untouched by the scoring launch, unless the
+        // workspace was not zero at first use)
+        const bool all = !g.bad && g.need == nE && nE > 0;
+        const int w = c * (CHUNK / 32) + tid;
+        if (tid < CHUNK / 32 && w < nwords) {
+            const int t0 = w << 5;
+            bitmap[(size_t)seg * nwords + w] =
+                all ? (bits_below(g.e1 - t0) & ~bits_below(g.e0 - t0)) : 0u;
+        }
+        if (c != 0) return;
+        for (int i = tid; i < HBINS / 4; i += TP) {
+            hs[i] = make_uint4(0u, 0u, 0u, 0u);
+            ss[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        if (wave == 0) {
+            if (g.bad) {
+                if (lane == 0) count[seg] = -1;
+                return;
+            }
+            uint32_t v2 = 0;
+            if (lane < nchunks) {
+                const int t0 = lane * CHUNK, t1 = t0 + CHUNK;
+                const int a = t0 > g.e0 ? t0 : g.e0, z = t1 < g.e1 ? t1 : g.e1;
+                v2 = (uint32_t)((all && z > a ? z - a : 0) + fixed_in(t0, t1, slo, wlo, L));
+            }
+            const uint32_t incl = wave_incl_scan(v2);
+            if (lane < nchunks) coff[(size_t)seg * nchunks + lane] = incl - v2;
+            if (lane == 63) count[seg] = (int32_t)incl;
+        }
+        return;
+    }
+
+    // 1. the bin that holds the budget's key
+    if (tid < CHUNK / 32) sh.bm[tid] = 0u;
+    for (int i = tid; i < HBINS / 4; i += TP)
+        reinterpret_cast<uint4 *>(sh.sub)[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (tid == 0) {
+        sh.cc = 0u;
+        sh.ac = 0u;
+        sh.m[0] = sh.m[1] = sh.m[2] = 0u;
+    }
+    const uint32_t need = (uint32_t)g.need;
+    {
+        const uint32_t cnt[8] = {h0.w, h0.z, h0.y, h0.x, h1.w, h1.z, h1.y, h1.x};
+        uint32_t sum = 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += cnt[j];
+        uint32_t tot;
+        const uint32_t incl = block_incl_scan<TP>(sum, sh.w, &tot);
+        uint32_t run = incl - sum;
+        if (tot >= need && run < need && need <= incl) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (run < need && need <= run + cnt[j]) {
+                    sh.m[0] = (uint32_t)(HBINS - 1 - 8 * tid - j);
+                    sh.m[1] = run;
+                    sh.m[2] = cnt[j];
+                }
+                run += cnt[j];
+            }
+        }
+        __syncthreads();
+    }
+    const uint32_t bstar = sh.m[0], C = sh.m[2];
+    const bool have_bin = C > 0;   // else the histogram does not hold the budget's rank
+    if (c == 0 && tid == 0) {
+        hinfo[(size_t)seg * 3] = bstar;
+        hinfo[(size_t)seg * 3 + 1] = sh.m[1];
+        hinfo[(size_t)seg * 3 + 2] = C;
+    }
+
+    // 2. the pass over the wave's step
+    if (have_bin && act)
+        classify_step<R, false>(base, v, hl, hr, e0, e1, bstar, sh.bm, c * (CHUNK / 32), &sh.ac,
+                                &sh.cc, sh.sub, cand + (size_t)seg * Lmax + (size_t)c * CHUNK,
+                                Lmax - c * CHUNK);
+    __syncthreads();
+
+    // 3. the chunk's state for the attention launch
+    const int w = c * (CHUNK / 32) + tid;
+    if (tid < CHUNK / 32 && w < nwords) bitmap[(size_t)seg * nwords + w] = sh.bm[tid];
+    if (tid == 0) {
+        ccount[(size_t)seg * nchunks + c] = sh.cc;
+        acount[(size_t)seg * nchunks + c] = sh.ac;
+    }
+    if (have_bin) {
+        // adjacent bins as one 64-bit atomic (counts never carry out of 32 bits)
+        for (int i = tid; i < HBINS / 4; i += TP) {
+            const uint4 sv = reinterpret_cast<const uint4 *>(sh.sub)[i];
+            uint64_t *sb = reinterpret_cast<uint64_t *>(sub + (size_t)seg * HBINS + 4 * i);
+            if (sv.x | sv.y)
+                __hip_atomic_fetch_add(sb, (uint64_t)sv.x | ((uint64_t)sv.y << 32),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (sv.z | sv.w)
+                __hip_atomic_fetch_add(sb + 1, (uint64_t)sv.z | ((uint64_t)sv.w << 32),
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
 }  // namespace
 
 bool hist_route_fits(int nseg, int Lmax, int g, int r, bool dilate) {
@@ -711,18 +894,23 @@ tb_status launch_score_hist_select(const float *qhat, int n_slots, int slot, con
                        Hkv, Lmax, S, W, K, nxs, ws.hist);
     tb_status e = check_launch("tb_score_select(score + histogram)");
     if (e) return e;
-    auto sel = pass_only ? (rk == 0   ? hist_select_kernel<0, true>
-                            : rk == 1 ? hist_select_kernel<1, true>
-                                      : hist_select_kernel<2, true>)
-                         : (rk == 0   ? hist_select_kernel<0, false>
-                            : rk == 1 ? hist_select_kernel<1, false>
-                                      : hist_select_kernel<2, false>);
+    if (pass_only) {
+        auto pass = rk == 0 ? hist_pass_kernel<0> : rk == 1 ? hist_pass_kernel<1> : hist_pass_kernel<2>;
+        const long long items = (long long)B * Hq * ws.nchunks;   // at most 64 x 64 on this route
+        const long long nb = (items + 7) / 8 * 8;
+        hipLaunchKernelGGL(pass, dim3((unsigned)nb), dim3(TP), 0, st, scores, ctx, plen, Hq, Lmax,
+                           S, W, K, omit_window ? 1 : 0, ws.hist, ws.hist + (size_t)B * Hq * HBINS,
+                           ws.nchunks, ws.ccount, ws.acount, ws.cand, ws.bitmap, ws.nwords,
+                           ws.coff, count, ws.hinfo, (int)items);
+        return check_launch("tb_score_select(classify)");
+    }
+    auto sel = rk == 0 ? hist_select_kernel<0> : rk == 1 ? hist_select_kernel<1> : hist_select_kernel<2>;
     const int nparts = (ws.nchunks + CPW - 1) / CPW;
     hipLaunchKernelGGL(sel, dim3(nparts, B * Hq), dim3(TSEL), 0, st, scores, ctx, plen, Hq, Lmax,
                        S, W, K, omit_window ? 1 : 0, ws.hist, ws.hist + (size_t)B * Hq * HBINS,
                        ws.bctr, ws.nchunks, ws.ccount, ws.acount, ws.cand, ws.bitmap, ws.nwords,
-                       ws.thr, ws.coff, count, ws.hinfo);
-    return check_launch(pass_only ? "tb_score_select(classify)" : "tb_score_select(select)");
+                       ws.thr, ws.coff, count);
+    return check_launch("tb_score_select(select)");
 }
 
 }  // namespace tb
