@@ -227,8 +227,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
             for (uint32_t slot = pln + tpc * PFC; slot < nmine && pch * CHUNK + (int)slot < Lmax;
                  slot += tpc)
                 take(cseg[(size_t)pch * CHUNK + slot]);
-            // the tpc threads of a chunk are adjacent lanes
-            for (int mm = tpc / 2; mm >= 1; mm >>= 1) nch += (uint32_t)__shfl_xor((int)nch, mm);
+            // the tpc threads of a chunk are adjacent lanes (rows of 16 lanes
+            // summed by DPP)
+            if (tpc >= 16) {
+                nch = row16_sum(nch);
+                for (int mm = 16; mm < tpc; mm <<= 1) nch += (uint32_t)__shfl_xor((int)nch, mm);
+            } else {
+                for (int mm = tpc / 2; mm >= 1; mm >>= 1) nch += (uint32_t)__shfl_xor((int)nch, mm);
+            }
             if (pln == 0 && pch < nchunks) sh.chosen[pch] = nch;
         } else {
             // the counts disagree with the histograms (a workspace that was

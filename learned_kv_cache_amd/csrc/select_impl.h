@@ -89,6 +89,36 @@ __device__ __forceinline__ int key_token(uint64_t key) {
     return (low & 1u) ? c - d : c + d;
 }
 
+// x of another lane through DPP, or 0 where the control has no source lane
+// for this one or the row / bank masks leave it out.
+template <int CTRL, int ROW_MASK = 0xF, int BANK_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_or0(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, BANK_MASK, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane order), by DPP:
+// within each row of 16 lanes by shifts of 1, 2, 4 and 8 lanes, then the
+// last lane of row 0 broadcast into row 1 (and of row 2 into row 3), then
+// lane 31 into rows 2 and 3. No LDS traffic.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += dpp_or0<0x111>(x);              // row_shr:1
+    x += dpp_or0<0x112>(x);              // row_shr:2
+    x += dpp_or0<0x114>(x);              // row_shr:4
+    x += dpp_or0<0x118>(x);              // row_shr:8
+    x += dpp_or0<0x142, 0xA>(x);         // row_bcast:15 into rows 1 and 3
+    x += dpp_or0<0x143, 0xC>(x);         // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Sum over each row of 16 lanes, in every lane of the row, by DPP.
+__device__ __forceinline__ uint32_t row16_sum(uint32_t x) {
+    x += dpp_or0<0xB1>(x);               // quad_perm [1, 0, 3, 2]
+    x += dpp_or0<0x4E>(x);               // quad_perm [2, 3, 0, 1]
+    x += dpp_or0<0x124>(x);              // row_ror:4
+    x += dpp_or0<0x128>(x);              // row_ror:8
+    return x;
+}
+
 // Inclusive prefix sum over the threads of the block (thread order). s_w
 // holds NT / 64 slots. Two barriers, and s_w may be reused after return;
 // with TRAIL false only the first, and the caller must pass another barrier
@@ -97,12 +127,7 @@ template <int NT, bool TRAIL = true>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *s_w, uint32_t *total) {
     constexpr int NW = NT / 64;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63) s_w[wave] = x;
     __syncthreads();
     uint32_t before = 0, tot = 0;
@@ -117,16 +142,6 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t *s_w, u
     return before + x;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave (lane order).
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(x, off);
-        if (lane >= off) x += y;
-    }
-    return x;
-}
 
 // Wave-wide: lane l holds the word of tokens [t0, t0 + 32) (t0 ascending with
 // the lane) whose first set bit is list row `base` + (set bits of the lanes
