@@ -96,56 +96,65 @@ __device__ __forceinline__ bool attn_store_merge(float m, float l, float (&acc)[
     __syncthreads();
     if (!sm_last) return false;
 
-    // last arrival: merge all partials of this head, kAttnThreads / LPR at a time:
-    // each row group of lanes loads one partial's (max, sum, 8 channels), the
-    // waves combine theirs by butterfly, and threads c < D fold the waves'
-    // states into a running (max, sum, o[c]) through LDS
+    // last arrival: thread t folds channel c = t % D of partials q, q + Q,
+    // q + 2Q, ... (q = t / D, Q = kAttnThreads / D), KP of them per round
+    // trip (every load of a round requested at once), into a running (max,
+    // sum, o[c]); threads c < D then fold the Q states through LDS
     constexpr int PW = D + 2;
-    constexpr int PPC = kAttnThreads / LPR;
+    constexpr int Q = kAttnThreads / D;
+    constexpr int KP = 8;
+    static_assert(Q <= kAttnWaves, "one LDS row per state");
+    const int ch = threadIdx.x % D, q = threadIdx.x / D;
     const float *base = part + (size_t)bh * nsplit * PW;
+    auto ld = [](const float *p) {
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
     float M = -1e30f, den = 0.f, num = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += PPC) {
-        const int sidx = s0 + wave * RPW + rg;
-        const bool valid = sidx < nsplit;
-        const float *src = base + (size_t)(valid ? sidx : 0) * PW;
-        float pm = valid ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : -1e30f;
-        float pl = valid ? __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : 0.f;
-        float po[8];
+    for (int s0 = 0; s0 < nsplit; s0 += Q * KP) {
+        float pm[KP], pl[KP], po[KP];
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            po[c] = valid ? __hip_atomic_load(src + 2 + cl * 8 + c, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT)
-                          : 0.f;
-        combine_lanes<LPR>(pm, pl, po);
-        __syncthreads();
-        if (rg == 0) {
-#pragma unroll
-            for (int c = 0; c < 8; ++c) sm_o[wave][cl * 8 + c] = po[c];
-            if (cl == 0) {
-                sm_m[wave] = pm;
-                sm_l[wave] = pl;
-            }
+        for (int k = 0; k < KP; ++k) {
+            const int sidx = s0 + q + Q * k;
+            const bool valid = sidx < nsplit;
+            const float *src = base + (size_t)(valid ? sidx : 0) * PW;
+            pm[k] = valid ? ld(src) : -1e30f;
+            pl[k] = valid ? ld(src + 1) : 0.f;
+            po[k] = valid ? ld(src + 2 + ch) : 0.f;
         }
-        __syncthreads();
-        if (threadIdx.x < D) {
-            float Mc = M;
+        float Mc = M;
 #pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) Mc = fmaxf(Mc, sm_m[w]);
-            const float r = exp2f(M - Mc);
-            den *= r;
-            num *= r;
+        for (int k = 0; k < KP; ++k) Mc = fmaxf(Mc, pm[k]);
+        const float r = exp2f(M - Mc);
+        den *= r;
+        num *= r;
 #pragma unroll
-            for (int w = 0; w < kAttnWaves; ++w) {
-                const float wt = exp2f(sm_m[w] - Mc);
-                den += sm_l[w] * wt;
-                num += sm_o[w][threadIdx.x] * wt;
-            }
-            M = Mc;
+        for (int k = 0; k < KP; ++k) {
+            const float w = exp2f(pm[k] - Mc);
+            den += pl[k] * w;
+            num += po[k] * w;
         }
+        M = Mc;
     }
-    if (threadIdx.x < D) out[(size_t)bh * D + threadIdx.x] = den > 0.f ? num / den : 0.f;
+    // (sm_o, sm_m and sm_l were last read before the barrier above)
+    sm_o[q][ch] = num;
+    if (ch == 0) {
+        sm_m[q] = M;
+        sm_l[q] = den;
+    }
+    __syncthreads();
+    if (threadIdx.x < D) {
+        float Mt = -1e30f;
+#pragma unroll
+        for (int w = 0; w < Q; ++w) Mt = fmaxf(Mt, sm_m[w]);
+        float dt = 0.f, nt = 0.f;
+#pragma unroll
+        for (int w = 0; w < Q; ++w) {
+            const float wt = exp2f(sm_m[w] - Mt);
+            dt += sm_l[w] * wt;
+            nt += sm_o[w][threadIdx.x] * wt;
+        }
+        out[(size_t)bh * D + threadIdx.x] = dt > 0.f ? nt / dt : 0.f;
+    }
     if (threadIdx.x == 0) __hip_atomic_store(ctr + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
 }
