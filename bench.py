@@ -39,7 +39,7 @@ PEAK_HBM_GBS = 8000.0
 # the step's dominant kernel: its committed traffic record and its sources,
 # for the split selection (threshold + list + attention) and for the deferred
 # list (compaction + attention)
-TRAFFIC_FILES = {"select": os.path.join(ROOT, "profiles", "hist_attn_c2_traffic.txt"),
+TRAFFIC_FILES = {"select": os.path.join(ROOT, "profiles", "split_attn_c2_traffic.txt"),
                  "list": os.path.join(ROOT, "profiles", "compact_attn_c2_traffic.txt")}
 KERNEL_SRCS = {k: [os.path.join(ROOT, "learned_kv_cache_amd", "csrc", f)
                    for f in (first, "select_impl.h", "attn_impl.h")]
@@ -1011,7 +1011,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": ("threshold + list + sparse decode attention gather "
-                                "(hist_attn_kernel<128>)" if split else
+                                "(split_attn_kernel<128>)" if split else
                                 "list compaction + sparse decode attention gather "
                                 "(compact_attn_kernel<128>)"),
                      "bytes_per_launch": attn_bytes, "avg_launch_us": attn_avg_s * 1e6,

@@ -68,12 +68,15 @@ typedef int tb_status;
 /* mode flag of tb_score_select (TB_NF_FILL only), then of the tb_select_attn
  * call that follows it: the selection is split across the two calls. Where
  * it applies (the histogram route of tb_score_select: B * Hq <= 64,
- * 8192 < Lmax <= 131072, radius <= 2, Hq / Hkv <= 4, and ceil(Lmax / 2048)
- * chunks <= ceil(cap / 256)), tb_score_select writes the scores and classifies
- * every token against the histogram bin of the budget's key, and writes
- * neither count nor idx; tb_select_attn then finds the exact threshold in
- * every attention workgroup (one per chunk of 2048 tokens), writes count and
- * idx as tb_score_select without the flag would, and attends. Its out then
+ * 8192 < Lmax <= 131072, radius <= 2, Hq / Hkv <= 4, and, with n =
+ * ceil(Lmax / 2048) chunks, ceil(n / 2) + ceil(n / 4) <= ceil(cap / 256)),
+ * tb_score_select writes the scores and classifies every token against the
+ * histogram bin of the budget's key, and writes neither count nor idx;
+ * tb_select_attn then attends the rows already fixed (sink, window, tokens
+ * above that bin) from the start, while its threshold workgroups (one per 4
+ * chunks of 2048 tokens) find the exact threshold, attend the chosen tokens
+ * of the bin and write count and idx as tb_score_select without the flag
+ * would. Its out then
  * agrees with tb_sparse_decode_attn over that list to fp32 rounding (other
  * splits: not bit for bit). A workspace whose histograms were not zero before
  * the first call is reported as count -1 and out 0 for the segments it

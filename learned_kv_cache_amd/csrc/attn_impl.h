@@ -35,12 +35,14 @@ __device__ inline void combine_lanes(float &m, float &l, float (&o)[8]) {
 // The workgroup's (max, sum, o) state from its lanes' row-group states: the
 // partial of split `split` of head bh is stored and, in the last split of the
 // head to arrive, all nsplit partials are merged into out. Returns true in
-// that last workgroup, after the merge.
+// that last workgroup, after the merge. poison: the split stores a partial
+// (sum -1) that makes the head's output 0 whatever the other splits hold.
 template <int D>
 __device__ __forceinline__ bool attn_store_merge(float m, float l, float (&acc)[8], int nsplit,
                                                  float *__restrict__ part,
                                                  uint32_t *__restrict__ ctr,
-                                                 float *__restrict__ out, int bh, int split) {
+                                                 float *__restrict__ out, int bh, int split,
+                                                 bool poison = false) {
     constexpr int LPR = D / 8;               // lanes per row
     constexpr int RPW = 64 / LPR;            // row groups per wave
     __shared__ float sm_o[kAttnWaves][D];
@@ -77,6 +79,12 @@ __device__ __forceinline__ bool attn_store_merge(float m, float l, float (&acc)[
 #pragma unroll
             for (int j = 0; j < D / 64; ++j) O[j] += sm_o[i][lane + 64 * j] * w;
         }
+        if (poison) {
+            M = -1e30f;
+            Ls = -1.f;
+#pragma unroll
+            for (int j = 0; j < D / 64; ++j) O[j] = 0.f;
+        }
 #pragma unroll
         for (int j = 0; j < D / 64; ++j)
             __hip_atomic_store(pp + 2 + lane + 64 * j, O[j], __ATOMIC_RELAXED,
@@ -110,6 +118,7 @@ __device__ __forceinline__ bool attn_store_merge(float m, float l, float (&acc)[
         return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
     float M = -1e30f, den = 0.f, num = 0.f;
+    bool bad = false;   // a poisoned partial (sum -1)
     for (int s0 = 0; s0 < nsplit; s0 += Q * KP) {
         float pm[KP], pl[KP], po[KP];
 #pragma unroll
@@ -123,7 +132,10 @@ __device__ __forceinline__ bool attn_store_merge(float m, float l, float (&acc)[
         }
         float Mc = M;
 #pragma unroll
-        for (int k = 0; k < KP; ++k) Mc = fmaxf(Mc, pm[k]);
+        for (int k = 0; k < KP; ++k) {
+            Mc = fmaxf(Mc, pm[k]);
+            bad |= pl[k] < 0.f;
+        }
         const float r = exp2f(M - Mc);
         den *= r;
         num *= r;
@@ -139,7 +151,7 @@ __device__ __forceinline__ bool attn_store_merge(float m, float l, float (&acc)[
     sm_o[q][ch] = num;
     if (ch == 0) {
         sm_m[q] = M;
-        sm_l[q] = den;
+        sm_l[q] = bad ? -1.f : den;
     }
     __syncthreads();
     if (threadIdx.x < D) {
@@ -147,13 +159,15 @@ __device__ __forceinline__ bool attn_store_merge(float m, float l, float (&acc)[
 #pragma unroll
         for (int w = 0; w < Q; ++w) Mt = fmaxf(Mt, sm_m[w]);
         float dt = 0.f, nt = 0.f;
+        bool anybad = false;
 #pragma unroll
         for (int w = 0; w < Q; ++w) {
             const float wt = exp2f(sm_m[w] - Mt);
+            anybad |= sm_l[w] < 0.f;
             dt += sm_l[w] * wt;
             nt += sm_o[w][threadIdx.x] * wt;
         }
-        out[(size_t)bh * D + threadIdx.x] = dt > 0.f ? nt / dt : 0.f;
+        out[(size_t)bh * D + threadIdx.x] = !anybad && dt > 0.f ? nt / dt : 0.f;
     }
     if (threadIdx.x == 0) __hip_atomic_store(ctr + bh, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return true;
@@ -266,14 +280,15 @@ __device__ __forceinline__ void attn_split(const uint16_t *__restrict__ q,
 // The lane's row-group (max, sum, o) state over rows [0, nrows) whose
 // positions, clamped to the cache, are staged in sm_tok (nrows <= the
 // array's size, a multiple of ROWS): ROWS rows per pass, the state rescaled
-// to each pass's new maximum. Rows beyond nrows are not loaded.
+// to each pass's new maximum. Rows beyond nrows are not loaded. fresh false:
+// the rows extend the state passed in instead of starting a new one.
 template <int D, int ROWS = kAttnCH>
 __device__ __forceinline__ void attn_rows(const uint16_t *__restrict__ q,
                                           const uint16_t *__restrict__ kc,
                                           const uint16_t *__restrict__ vc, int Hkv, int Lmax,
                                           float scale_log2, int b, int kvh, int bh, int nrows,
                                           const int *sm_tok, float &m, float &l,
-                                          float (&acc)[8]) {
+                                          float (&acc)[8], bool fresh = true) {
     constexpr int LPR = D / 8;               // lanes per row
     constexpr int RPW = 64 / LPR;            // row groups per wave
     constexpr int NG = kAttnWaves * RPW;     // row groups per workgroup
@@ -303,10 +318,12 @@ __device__ __forceinline__ void attn_rows(const uint16_t *__restrict__ q,
         __builtin_amdgcn_make_buffer_rsrc((void *)(vc + head_off), (short)0, head_bytes, kRsrcWord3);
     const int lane_off = cl * 16;
 
-    m = -1e30f;
-    l = 0.f;
+    if (fresh) {
+        m = -1e30f;
+        l = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+        for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+    }
     for (int base = 0; base < nrows; base += ROWS) {
         const int *tok = sm_tok + base;
         const int n = nrows - base;   // rows of this pass: [0, min(n, ROWS))

@@ -11,21 +11,24 @@
 // histogram of the candidates' next 12 key bits, and B*, A (tokens above it)
 // and C (tokens in it). No workgroup of that launch waits for another.
 //
-// Here one workgroup per (b, KV head, chunk, query head in group) -- the
-// chunk is its attention split -- reads, in one round trip, the second
-// histogram, every chunk's counts, the first candidate slots of every chunk
-// and its own chunk's bitmap words. From these it finds the exact key of the
-// budget's rank inside B* (the sub-bin holding it, then the few keys of that
-// sub-bin ranked directly) and counts every chunk's chosen candidates, so it
-// knows the list offset of its chunk without waiting for any other
-// workgroup; every workgroup of the segment reaches the same threshold. It
-// attends over its chunk's rows (bitmap words, chosen candidates, sink and a
-// share of the window, ascending), 128 rows per pass, and writes them to the
-// list; the last split of the head to arrive merges the partials and clears
-// the second histogram, and every workgroup clears a share of the first one
-// for the next call. Counts that disagree with the histograms (a
+// Most of a head's rows are known at that point: the sink, the window and
+// the tokens above B*. Here they are attended by rows-known workgroups (two
+// chunks each, one round trip for their bitmap words) from the start, while
+// threshold workgroups (four chunks each, dispatched first) read, in one
+// round trip, the second histogram, every chunk's counts and the first
+// candidate slots of every chunk, find the exact key of the budget's rank
+// inside B* (the sub-bin holding it, then the few keys of that sub-bin
+// ranked directly), count every chunk's chosen candidates (so each knows its
+// chunks' list offsets without waiting for any other workgroup; every one of
+// them reaches the same threshold), attend the chosen candidates of their
+// chunks and write their chunks' list rows (bitmap words, chosen candidates,
+// sink and a share of the window, ascending). Both kinds store partials of
+// the head; the last to arrive merges them (log-sum-exp) and clears the
+// second histogram, and the threshold workgroups clear shares of the first
+// one for the next call. Counts that disagree with the histograms (a
 // workspace that was not zero at first use) are reported as an invalid
-// segment (count -1, out 0); the next call is exact again.
+// segment (count -1, out 0: the threshold workgroups' partials are
+// poisoned); the next call is exact again.
 #include "attn_impl.h"
 #include "select_impl.h"
 
@@ -45,55 +48,142 @@ constexpr int kRowsPerPass = 128;
 static_assert(BPT == 8 && NT / MAXC == 8 && CHUNK % kAttnCH == 0 && NT * 4 == CHUNK,
               "bookkeeping below");
 
-struct HistAttnLds {
+constexpr int KC = 2;                        // chunks per rows-known workgroup
+constexpr int TC = 4;                        // chunks per threshold workgroup
+constexpr int KW = KC * (CHUNK / 32);        // their words
+constexpr int TW = TC * (CHUNK / 32);
+constexpr int KB = KW * 32 / NT;             // bits each thread stages
+constexpr int TB = TW * 32 / NT;
+static_assert(KW <= NT && TW <= NT && TC * 64 <= NT && 32 % KB == 0 && 32 % TB == 0 && KB >= 4 &&
+                  TB >= 4,
+              "a word (or a run of its bits) per thread");
+
+struct SplitAttnLds {
     KthLds<NT> k;
-    uint32_t word[CHUNK / 32];      // the chunk's row bits
-    uint32_t wrow[CHUNK / 32];      // list row of each word's first bit, within the chunk
+    uint32_t word[KW > TW ? KW : TW];    // rows-known: the rows' bits; threshold: chosen bits
+    uint32_t wrow[KW > TW ? KW : TW];    // attention row of each word's first bit
+    uint32_t lword[TW];                  // threshold: the list's bits
+    uint32_t lrow[TW];                   // list row of each word's first bit, within its chunk
+    uint32_t crow[TC];                   // attention row of each chunk's first chosen row
     uint32_t ccnt[MAXC], acnt[MAXC], chosen[MAXC], off[MAXC];
     uint32_t m[8];
-    int tok[CHUNK + kMaxWinShare];  // the chunk's rows, then its share of the window
+    int tok[KC * (CHUNK + kMaxWinShare)];   // rows to attend
 };
 
+// Rows of the bits of word w (whose bit 0 is token tbase, whose first set bit
+// is row `first`) to tok[row]: thread t takes bits [NB (t % (32 / NB)), +NB).
+template <int NB>
+__device__ __forceinline__ void stage_bits(uint32_t w, uint32_t first, int tbase, int *tok) {
+    const int lo = (threadIdx.x % (32 / NB)) * NB;
+    uint32_t left = (w >> lo) & (NB == 32 ? ~0u : (1u << NB) - 1u);
+    uint32_t p = first + (uint32_t)__popc(w & ((1u << lo) - 1u));
+    while (left) {
+        tok[p++] = tbase + lo + __builtin_ctz(left);
+        left &= left - 1u;
+    }
+}
+// The same for the rows [r0, r0 + n) only, to tok[row - r0].
+template <int NB>
+__device__ __forceinline__ void stage_bits_range(uint32_t w, uint32_t first, int tbase, int *tok,
+                                                 uint32_t r0, uint32_t n) {
+    const int lo = (threadIdx.x % (32 / NB)) * NB;
+    uint32_t left = (w >> lo) & (NB == 32 ? ~0u : (1u << NB) - 1u);
+    uint32_t p = first + (uint32_t)__popc(w & ((1u << lo) - 1u));
+    while (left) {
+        if (p - r0 < n) tok[p - r0] = tbase + lo + __builtin_ctz(left);
+        ++p;
+        left &= left - 1u;
+    }
+}
+
 template <int D>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hist_attn_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void split_attn_kernel(
     const int32_t *__restrict__ ctx, const int32_t *__restrict__ plen, int Hq, int Hkv, int Lmax,
-    int S, int W, int K, int omit_window, const uint32_t *__restrict__ hinfo, uint32_t *__restrict__ hist, int nseg,
-    const uint32_t *__restrict__ ccount, const uint32_t *__restrict__ acount,
-    const uint64_t *__restrict__ cand, const uint32_t *__restrict__ bitmap, int nwords,
-    int nchunks, const uint32_t *__restrict__ coff, uint64_t *__restrict__ thr_out,
+    int S, int W, int K, int omit_window, const uint32_t *__restrict__ hinfo,
+    uint32_t *__restrict__ hist, int nseg, const uint32_t *__restrict__ ccount,
+    const uint32_t *__restrict__ acount, const uint64_t *__restrict__ cand,
+    const uint32_t *__restrict__ bitmap, int nwords, int nchunks, int nK, int nT,
+    const uint32_t *__restrict__ coff, uint64_t *__restrict__ thr_out,
     int32_t *__restrict__ count, int32_t *__restrict__ idx, int cap,
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, float scale_log2, int n_items, float *__restrict__ part,
     uint32_t *__restrict__ ctr, float *__restrict__ out) {
-    __shared__ __align__(16) HistAttnLds sh;
+    __shared__ __align__(16) SplitAttnLds sh;
     const int nb = gridDim.x, bid = blockIdx.x;
-    // work items in the attention launch's XCD-aware order: the query heads
-    // of a group, then the chunks, of one (b, KV head) on one XCD
+    // XCD-aware order: per (b, KV head) the threshold workgroups of its g
+    // query heads (dispatched first: their chain is the longer one), then the
+    // rows-known ones, on one XCD
     const int item = (bid & 7) * (nb >> 3) + (bid >> 3);
     if (item >= n_items) return;
     const int g = Hq / Hkv;
-    const int hg = item % g;
-    int rest = item / g;
-    const int c = rest % nchunks;
-    rest /= nchunks;
-    const int kvh = rest % Hkv;
-    const int b = rest / Hkv;
-    const int seg = b * Hq + kvh * g + hg;   // the selection's segment, the attention's head
+    const int per = g * (nT + nK);
+    const int grp = item / per;
+    int r = item % per;
+    const bool thr_role = r < g * nT;
+    if (!thr_role) r -= g * nT;
+    const int hg = r % g, j = r / g;
+    const int kvh = grp % Hkv, b = grp / Hkv;
+    const int seg = b * Hq + kvh * g + hg;
+    const int nsplit = nK + nT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint4 *hs = reinterpret_cast<uint4 *>(hist + (size_t)seg * HBINS);
     uint4 *ss = reinterpret_cast<uint4 *>(hist + (size_t)(nseg + seg) * HBINS);
+
+    if (!thr_role) {
+        // ---- rows known before the threshold: chunks [c0, c1)
+        const int c0 = j * KC, c1 = c0 + KC < nchunks ? c0 + KC : nchunks;
+        const int wg = c0 * (CHUNK / 32) + tid;   // this thread's word
+        uint32_t bits = 0u;
+        if (tid < (c1 - c0) * (CHUNK / 32) && wg < nwords) bits = bitmap[(size_t)seg * nwords + wg];
+        const Region gr = region(ctx, plen, b, Lmax, S, W, K);
+        const int L = gr.L;
+        const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
+        const int slo = S < L ? S : L;
+        const int w0 = wlo > slo ? wlo : slo;
+        uint32_t wv = 0u;
+        if (!gr.bad && tid < KW) {
+            // sink rows and tokens above B* (the pass's words), no window-only rows
+            const int t0 = wg << 5;
+            wv = gr.need == 0 ? 0u : bits;
+            wv |= bits_below(slo - t0);
+            wv &= bits_below(w0 - t0);
+        }
+        if (tid < KW) sh.word[tid] = wv;
+        uint32_t tot;
+        const uint32_t incl = block_incl_scan<NT>(tid < KW ? (uint32_t)__popc(wv) : 0u, sh.k.w, &tot);
+        if (tid < KW) sh.wrow[tid] = incl - (uint32_t)__popc(wv);
+        // the chunks' shares of the window rows (the list's last rows)
+        const int nW = !gr.bad && L > w0 ? L - w0 : 0;
+        const int share = (nW + nchunks - 1) / nchunks;
+        const int wa = c0 * share < nW ? c0 * share : nW;
+        const int wz = c1 * share < nW ? c1 * share : nW;
+        __syncthreads();
+        {
+            const int wi = tid / (32 / KB);
+            stage_bits<KB>(sh.word[wi], sh.wrow[wi], (c0 * (CHUNK / 32) + wi) << 5, sh.tok);
+        }
+        for (int i = tid; i < wz - wa; i += NT) sh.tok[tot + i] = w0 + wa + i;
+        __syncthreads();
+        const int nrows = (int)tot + (wz - wa);
+        float m, l, acc[8];
+        attn_rows<D, kRowsPerPass>(q, kc, vc, Hkv, Lmax, scale_log2, b, kvh, seg, nrows, sh.tok, m,
+                                   l, acc);
+        if (attn_store_merge<D>(m, l, acc, nsplit, part, ctr, out, seg, j))
+            for (int i = tid; i < HBINS / 4; i += NT) ss[i] = make_uint4(0u, 0u, 0u, 0u);
+        return;
+    }
+
+    // ---- threshold workgroup: chunks [c0, c1)
+    const int c0 = j * TC, c1 = c0 + TC < nchunks ? c0 + TC : nchunks;
     const uint64_t *cseg = cand + (size_t)seg * Lmax;
-    // candidate bookkeeping: tpc adjacent threads per chunk (512 over the
-    // chunk count rounded up to a power of two, at most a wave), thread pln
-    // of chunk pch holding slots pln + tpc j
     const int lgc = nchunks <= 1 ? 0 : 32 - __clz(nchunks - 1);
     const int tpc = (NT >> lgc) < 64 ? (NT >> lgc) : 64;
     const int pch = tid / tpc, pln = tid % tpc;
+    // the first histogram is read by the classification pass only, which has
+    // ended: each threshold workgroup clears its share of it for the next call
+    for (int i = j + nT * tid; i < HBINS / 4; i += nT * NT) hs[i] = make_uint4(0u, 0u, 0u, 0u);
 
-    // 1. the one round trip, requested before the lengths arrive: every
-    // address lies in the workspace whatever they are, and what a segment's
-    // lengths make unused is ignored below
-    // bins 4095 - 8 tid - j, j < 8: descending thread order
+    // 1. the one round trip, requested before the lengths arrive
     const uint4 *sq = ss + HBINS / 4 - 2 * (tid + 1);
     const uint4 h0 = sq[1], h1 = sq[0];
     const uint32_t bstar = hinfo[(size_t)seg * 3], A = hinfo[(size_t)seg * 3 + 1],
@@ -105,39 +195,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
     }
     uint64_t pv[PFC];
 #pragma unroll
-    for (int j = 0; j < PFC; ++j) {
-        const int slot = pln + tpc * j;
-        pv[j] = pch < nchunks && pch * CHUNK + slot < Lmax ? cseg[(size_t)pch * CHUNK + slot] : 0ull;
+    for (int jj = 0; jj < PFC; ++jj) {
+        const int slot = pln + tpc * jj;
+        pv[jj] = pch < nchunks && pch * CHUNK + slot < Lmax ? cseg[(size_t)pch * CHUNK + slot] : 0ull;
     }
-    if (wave == 0) {
-        const int w = c * (CHUNK / 32) + lane;
-        bits = w < nwords ? bitmap[(size_t)seg * nwords + w] : 0u;
-    }
-    // the first histogram is read by the classification pass only, which has
-    // ended: each workgroup clears its share of it for the next call
-    for (int i = c + nchunks * tid; i < HBINS / 4; i += nchunks * NT) hs[i] = make_uint4(0u, 0u, 0u, 0u);
+    const int wg = c0 * (CHUNK / 32) + tid;
+    if (tid < (c1 - c0) * (CHUNK / 32) && wg < nwords) bits = bitmap[(size_t)seg * nwords + wg];
     const Region gr = region(ctx, plen, b, Lmax, S, W, K);
     const int L = gr.L;
     const int nE = gr.e1 - gr.e0;
     const bool partial = !gr.bad && gr.need > 0 && gr.need < nE;
     const int wlo = omit_window ? L : (L - W > 0 ? L - W : 0);
     const int slo = S < L ? S : L;
-    // window-only rows [w0, L) (rows below slo are sink rows) are the list's
-    // last rows; they are shared out evenly over the segment's chunk splits
-    // (the window's own chunk would otherwise hold about twice the rows)
     const int w0 = wlo > slo ? wlo : slo;
 
-    // the chunk's sink rows and its tokens above B* (no window-only rows:
-    // the eligible region ends below the window)
-    if (wave == 0) {
-        const int t0 = (c * (CHUNK / 32) + lane) << 5;
+    if (tid < TW) {
+        const int t0 = wg << 5;
         uint32_t wv = 0u;
         if (!gr.bad) {
             wv = gr.need == 0 ? 0u : bits;
             wv |= bits_below(slo - t0);
             wv &= bits_below(w0 - t0);
         }
-        sh.word[lane] = wv;
+        sh.lword[tid] = wv;
+        sh.word[tid] = 0u;
     }
     if (tid < MAXC) {
         sh.chosen[tid] = 0u;
@@ -152,7 +233,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
     uint64_t thr = ~0ull;
 
     if (partial) {
-        // 2. the threshold, as the selection's last workgroup finds it
+        // 2. the threshold
         if (wave == 0) {
             const uint32_t ccl = lane < nchunks ? (cc_l < (uint32_t)CHUNK ? cc_l : (uint32_t)CHUNK)
                                                 : 0u;
@@ -168,7 +249,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
         const uint32_t cnt2[BPT] = {h0.w, h0.z, h0.y, h0.x, h1.w, h1.z, h1.y, h1.x};
         uint32_t sum2 = 0u;
 #pragma unroll
-        for (int j = 0; j < BPT; ++j) sum2 += cnt2[j];
+        for (int jj = 0; jj < BPT; ++jj) sum2 += cnt2[jj];
         uint32_t tot2;
         const uint32_t incl2 = block_incl_scan<NT>(sum2, sh.k.w, &tot2);
         const uint32_t need = (uint32_t)gr.need;
@@ -182,13 +263,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
                 uint32_t run = incl2 - sum2;
                 if (run < need1 && need1 <= incl2) {
 #pragma unroll
-                    for (int j = 0; j < BPT; ++j) {
-                        if (run < need1 && need1 <= run + cnt2[j]) {
-                            sh.m[4] = (uint32_t)(HBINS - 1 - BPT * tid - j);
+                    for (int jj = 0; jj < BPT; ++jj) {
+                        if (run < need1 && need1 <= run + cnt2[jj]) {
+                            sh.m[4] = (uint32_t)(HBINS - 1 - BPT * tid - jj);
                             sh.m[5] = run;
-                            sh.m[6] = cnt2[j];
+                            sh.m[6] = cnt2[jj];
                         }
-                        run += cnt2[j];
+                        run += cnt2[jj];
                     }
                 }
                 __syncthreads();
@@ -200,35 +281,37 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
                 const uint32_t nmine = pch < nchunks ? sh.ccnt[pch] : 0u;
                 auto visit = [&](auto f) {
 #pragma unroll
-                    for (int j = 0; j < PFC; ++j)
-                        if ((uint32_t)(pln + tpc * j) < nmine) f(pv[j]);
+                    for (int jj = 0; jj < PFC; ++jj)
+                        if ((uint32_t)(pln + tpc * jj) < nmine) f(pv[jj]);
                     for (uint32_t slot = pln + tpc * PFC;
                          slot < nmine && pch * CHUNK + (int)slot < Lmax; slot += tpc)
                         f(cseg[(size_t)pch * CHUNK + slot]);
                 };
                 thr = kth_largest<NT>(visit, need2, prefix, mask, 40, n2, sh.k);
             }
-            // each chunk's chosen candidates; this chunk's into its words
+            // each chunk's chosen candidates; those of this workgroup's chunks
+            // into their words
             const uint32_t nmine = pch < nchunks ? sh.ccnt[pch] : 0u;
+            const bool mine = pch >= c0 && pch < c1;
             uint32_t nch = 0u;
             auto take = [&](uint64_t key) {
                 if (key >= thr) {
                     ++nch;
-                    const int t = key_token(key) - c * CHUNK;
+                    const int t = key_token(key) - pch * CHUNK;
                     // a candidate's position lies in its chunk after the pass
                     // this call follows; anything else is not written
-                    if (pch == c && (uint32_t)t < (uint32_t)CHUNK)
-                        atomicOr(&sh.word[t >> 5], 1u << (t & 31));
+                    if (mine && (uint32_t)t < (uint32_t)CHUNK) {
+                        const int tw = t + (pch - c0) * CHUNK;
+                        atomicOr(&sh.word[tw >> 5], 1u << (tw & 31));
+                    }
                 }
             };
 #pragma unroll
-            for (int j = 0; j < PFC; ++j)
-                if ((uint32_t)(pln + tpc * j) < nmine) take(pv[j]);
+            for (int jj = 0; jj < PFC; ++jj)
+                if ((uint32_t)(pln + tpc * jj) < nmine) take(pv[jj]);
             for (uint32_t slot = pln + tpc * PFC; slot < nmine && pch * CHUNK + (int)slot < Lmax;
                  slot += tpc)
                 take(cseg[(size_t)pch * CHUNK + slot]);
-            // the tpc threads of a chunk are adjacent lanes (rows of 16 lanes
-            // summed by DPP)
             if (tpc >= 16) {
                 nch = row16_sum(nch);
                 for (int mm = 16; mm < tpc; mm <<= 1) nch += (uint32_t)__shfl_xor((int)nch, mm);
@@ -238,17 +321,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
             if (pln == 0 && pch < nchunks) sh.chosen[pch] = nch;
         } else {
             // the counts disagree with the histograms (a workspace that was
-            // not zero at first use): the segment is reported as invalid,
-            // count -1 and no rows; the histograms are cleared below, so the
-            // next call is exact again
-            if (wave == 0) sh.word[lane] = 0u;
+            // not zero at first use): count -1, no list rows, and a poisoned
+            // partial (output 0); the histograms are cleared, so the next
+            // call is exact again
+            if (tid < TW) sh.lword[tid] = 0u;
             if (tid == 0) sh.m[2] = 1u;
         }
     }
     __syncthreads();
 
-    // 3. chunk offsets of the list; the count; the list row of each word's
-    // first bit
+    // 3. chunk offsets of the list, the count; per chunk of this workgroup
+    // (one wave each) the list row and the attention row of each word
     if (wave == 0) {
         if (partial) {
             uint32_t v = 0u;
@@ -257,7 +340,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
                     (uint32_t)fixed_in(lane * CHUNK, (lane + 1) * CHUNK, slo, wlo, L);
             const uint32_t incl = wave_incl_scan(v);
             sh.off[lane] = incl - v;
-            if (c == 0 && lane == 63) {
+            if (j == 0 && lane == 63) {
                 count[seg] = sh.m[2] ? -1 : (int32_t)incl;
                 thr_out[seg] = thr;
             }
@@ -265,56 +348,73 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(8))) void hi
             // all or none: offsets from the pass
             sh.off[lane] = !gr.bad && lane < nchunks ? coff[(size_t)seg * nchunks + lane] : 0u;
         }
-        const uint32_t pop = (uint32_t)__popc(sh.word[lane]);
-        const uint32_t incl = wave_incl_scan(pop);
-        sh.wrow[lane] = incl - pop;
-        if (lane == 63) sh.m[3] = incl;
+    }
+    if (wave < c1 - c0) {
+        const int wi = wave * 64 + lane;
+        const uint32_t cw = sh.word[wi];
+        const uint32_t lw = sh.lword[wi] | cw;
+        sh.lword[wi] = lw;
+        // list rows (low half) and chosen rows (high half) in one scan
+        const uint32_t pk = (uint32_t)__popc(lw) | ((uint32_t)__popc(cw) << 16);
+        const uint32_t inc = wave_incl_scan(pk) - pk;
+        sh.lrow[wi] = inc & 0xffffu;
+        sh.wrow[wi] = inc >> 16;
+    }
+    // chosen rows of each chunk follow those of the chunks before it
+    if (tid == 0) {
+        uint32_t run = 0u;
+        for (int ci = 0; ci < c1 - c0; ++ci) {
+            sh.crow[ci] = run;
+            run += sh.chosen[c0 + ci];
+        }
+        sh.m[3] = run;
     }
     __syncthreads();
-    // this chunk's share of the window rows: they follow the sink and the
-    // important rows (need of them: the budget, all of the region, or none)
-    const int nW = !gr.bad && !sh.m[2] && L > w0 ? L - w0 : 0;
-    const int share = (nW + nchunks - 1) / nchunks;
-    const int ws0 = c * share < nW ? c * share : nW;
-    const int nwin = ws0 + share < nW ? share : nW - ws0;
-    const int nch = (int)sh.m[3];
-    const int nrows = nch + nwin;
-    const uint32_t off = sh.off[c];
-    const uint32_t woff = (uint32_t)(slo + gr.need + ws0);
+    const int ncz = (int)sh.m[3];
+    // the chosen rows, as many at a time as the row table holds (all of them
+    // unless far more than the budget's share fall in these chunks)
+    constexpr int TOKCAP = KC * (CHUNK + kMaxWinShare);
+    float m, l, acc[8];
+    for (int r0 = 0; r0 == 0 || r0 < ncz; r0 += TOKCAP) {
+        const int wi = tid / (32 / TB);
+        if (wi < (c1 - c0) * 64)
+            stage_bits_range<TB>(sh.word[wi], sh.wrow[wi] + sh.crow[wi >> 6],
+                                 (c0 * (CHUNK / 32) + wi) << 5, sh.tok, (uint32_t)r0, TOKCAP);
+        __syncthreads();
+        const int n = ncz - r0 < TOKCAP ? ncz - r0 : TOKCAP;
+        attn_rows<D, kRowsPerPass>(q, kc, vc, Hkv, Lmax, scale_log2, b, kvh, seg, n, sh.tok, m, l,
+                                   acc, r0 == 0);
+        __syncthreads();   // the table is read before it is staged again
+    }
+    if (attn_store_merge<D>(m, l, acc, nsplit, part, ctr, out, seg, nK + j, sh.m[2] != 0u))
+        for (int i = tid; i < HBINS / 4; i += NT) ss[i] = make_uint4(0u, 0u, 0u, 0u);
+
+    // 4. the chunks' rows to the list (nothing in this launch reads them):
+    // the words' rows, then each chunk's share of the window rows (the list's
+    // last rows, after the sink and the need: all of the region's, or none)
     {
-        // the chunk's rows, ascending, to the row table: every thread takes
-        // four bits of one word (a wave alone would walk up to 32 bits per
-        // lane while the CU's other workgroups attend). Every row lies in
-        // [0, L), so the table holds the list's values.
-        const int wi = tid >> 3, nib = (tid & 7) * 4;
-        const uint32_t word = sh.word[wi];
-        uint32_t left = (word >> nib) & 15u;
-        uint32_t p = sh.wrow[wi] + (uint32_t)__popc(word & ((1u << nib) - 1u));
-        const int tb = ((c * (CHUNK / 32) + wi) << 5) + nib;
-        while (left) {
-            sh.tok[p++] = tb + __builtin_ctz(left);
-            left &= left - 1u;
+        const int wi = tid / (32 / TB);
+        const int ci = wi >> 6;
+        if (ci < c1 - c0) {
+            const uint32_t w = sh.lword[wi];
+            const int lo = (tid % (32 / TB)) * TB;
+            uint32_t left = (w >> lo) & (TB == 32 ? ~0u : (1u << TB) - 1u);
+            uint32_t p = sh.off[c0 + ci] + sh.lrow[wi] + (uint32_t)__popc(w & ((1u << lo) - 1u));
+            const int tb = ((c0 * (CHUNK / 32) + wi) << 5) + lo;
+            while (left) {
+                if (p < (uint32_t)cap) idx[(size_t)seg * cap + p] = tb + __builtin_ctz(left);
+                ++p;
+                left &= left - 1u;
+            }
         }
     }
-    for (int i = tid; i < nwin; i += NT) sh.tok[nch + i] = w0 + ws0 + i;
-    __syncthreads();
-
-    // 4. attention over the chunk's rows; the last split of the head merges
-    float m, l, acc[8];
-    attn_rows<D, kRowsPerPass>(q, kc, vc, Hkv, Lmax, scale_log2, b, kvh, seg, nrows, sh.tok, m, l,
-                               acc);
-    if (attn_store_merge<D>(m, l, acc, nchunks, part, ctr, out, seg, c)) {
-        // every workgroup of the segment has read the second histogram
-        for (int i = tid; i < HBINS / 4; i += NT) ss[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    // the chunk's rows to the list only now: stores issued while the CU's
-    // other workgroups stream K/V wait for the memory pipeline (and the
-    // partial's stores above wait for every earlier store), and nothing in
-    // this launch reads them
-    for (int i = tid; i < nrows; i += NT) {
-        const uint32_t pos = i < nch ? off + (uint32_t)i : woff + (uint32_t)(i - nch);
-        if (pos < (uint32_t)cap) idx[(size_t)seg * cap + pos] = sh.tok[i];
-    }
+    const int nW = !gr.bad && !sh.m[2] && L > w0 ? L - w0 : 0;
+    const int share = (nW + nchunks - 1) / nchunks;
+    const int wa = c0 * share < nW ? c0 * share : nW;
+    const int wz = c1 * share < nW ? c1 * share : nW;
+    const uint32_t woff = (uint32_t)(slo + gr.need + wa);
+    for (int i = tid; i < wz - wa; i += NT)
+        if (woff + (uint32_t)i < (uint32_t)cap) idx[(size_t)seg * cap + woff + i] = w0 + wa + i;
 }
 
 }  // namespace
@@ -325,8 +425,9 @@ bool defer_select_fits(int B, int Hq, int Hkv, int Lmax, int r, int win, int cap
     const int nchunks = (Lmax + CHUNK - 1) / CHUNK;
     // one split per chunk (the attention workspace holds attn_nsplit(cap)
     // partials per head); each takes at most kMaxWinShare window rows
+    const int nsplit = (nchunks + KC - 1) / KC + (nchunks + TC - 1) / TC;
     return hist_route_fits(B * Hq, Lmax, Hq / Hkv, r, false) && nchunks <= MAXC &&
-           nchunks <= attn_nsplit(cap) && win >= 0 &&
+           nsplit <= attn_nsplit(cap) && win >= 0 &&
            (win + nchunks - 1) / nchunks <= kMaxWinShare;
 }
 
@@ -339,14 +440,15 @@ tb_status launch_hist_attn(const int32_t *ctx, const int32_t *plen, int B, int H
         set_error("tb_select_attn: the deferred selection does not apply to this shape");
         return TB_ERR_UNSUPPORTED_SHAPE;
     }
-    const long long items = (long long)B * Hq * ws.nchunks;
+    const int nK = (ws.nchunks + KC - 1) / KC, nT = (ws.nchunks + TC - 1) / TC;
+    const long long items = (long long)B * Hq * (nK + nT);
     const long long nb = (items + 7) / 8 * 8;
     const float scale_log2 = scale * 1.4426950408889634f;
-    auto fn = D == 128 ? hist_attn_kernel<128> : hist_attn_kernel<64>;
+    auto fn = D == 128 ? split_attn_kernel<128> : split_attn_kernel<64>;
     hipLaunchKernelGGL(fn, dim3((unsigned)nb), dim3(NT), 0, st, ctx, plen, Hq, Hkv, Lmax, S, W, K,
-                       omit_window ? 1 : 0, ws.hinfo, ws.hist, B * Hq, ws.ccount,
-                       ws.acount, ws.cand, ws.bitmap, ws.nwords, ws.nchunks, ws.coff, ws.thr,
-                       count, idx, cap, static_cast<const uint16_t *>(q),
+                       omit_window ? 1 : 0, ws.hinfo, ws.hist, B * Hq, ws.ccount, ws.acount,
+                       ws.cand, ws.bitmap, ws.nwords, ws.nchunks, nK, nT, ws.coff, ws.thr, count,
+                       idx, cap, static_cast<const uint16_t *>(q),
                        static_cast<const uint16_t *>(kc), static_cast<const uint16_t *>(vc),
                        scale_log2, (int)items, part, ctr, out);
     return check_launch("tb_select_attn");

@@ -40,9 +40,11 @@ def _inputs(seed, B, Hq, Hkv, Lmax, D, dp):
 
 
 def _case(tb, seed, B, Hq, Hkv, Lmax, D, dp, L, P, S, W, K, r, omit=False, orc=None,
-          junk=False, expect_split=True):
-    say("defer_select", seed, B, Hq, Hkv, Lmax, D, dp, L, P, S, W, K, r, omit, junk)
+          junk=False, expect_split=True, flat=False):
+    say("defer_select", seed, B, Hq, Hkv, Lmax, D, dp, L, P, S, W, K, r, omit, junk, flat)
     kp, qh, kc_h, vc_h, q_h = _inputs(seed, B, Hq, Hkv, Lmax, D, dp)
+    if flat:
+        kp.zero_()   # every score 0: ties broken by position
     kc, vc, q = (dev(x, torch.bfloat16) for x in (kc_h, vc_h, q_h))
     ctx, pl = dev32(np.asarray(L, np.int32)), dev32(np.asarray(P, np.int32))
     mode = tb.TB_NF_FILL | (tb.TB_SEL_OMIT_WINDOW if omit else 0)
@@ -126,6 +128,11 @@ def test_defer_select_edges(tb):
     _case(tb, 8, 2, 8, 2, 9000, 64, 16, [3, 8999], [3, 8999], 4, 16, 2300, 1)   # short context
     c = _case(tb, 9, 3, 8, 2, 9000, 64, 16, [9000, 9001, -1], [9000, 10, 5], 4, 16, 2300, 1)
     assert (c[0] >= 0).all() and (c[1] == -1).all() and (c[2] == -1).all()
+    # every score equal: the budget's tokens are the first positions, so the
+    # chosen candidates of the first chunks outnumber what one workgroup's
+    # row table holds at once
+    _case(tb, 11, 1, 8, 2, 65536, 128, 32, [65536], [65536], 64, 256, 7872, 1, flat=True)
+    _case(tb, 12, 1, 4, 1, 40000, 64, 16, [40000], [40000], 8, 64, 12000, 2, flat=True)
 
 
 def test_defer_select_off_route_acts_as_defer_list(tb):
