@@ -57,6 +57,53 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class FenceFreeEvent:
+    """A timing event of the HIP runtime torch uses, created with
+    hipEventDisableSystemFence: recording it writes no caches back and
+    invalidates none, so the work timed between two of them runs as it does
+    between kernels (events recorded with the default system-scope fence add
+    about 3 us around a single launch on this part)."""
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            path = None
+            for line in open("/proc/self/maps"):
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded")
+            h = ctypes.CDLL(path)
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        self.e = ctypes.c_void_p()
+        if self._lib().hipEventCreateWithFlags(ctypes.byref(self.e), 0x20000000):
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if self._lib().hipEventRecord(self.e, ctypes.c_void_p(stream.cuda_stream)):
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        ms = ctypes.c_float()
+        if self._lib().hipEventElapsedTime(ctypes.byref(ms), self.e, end.e):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.e:
+            self._hip.hipEventDestroy(self.e)
+
+
 def planting_direction(inp, cfg):
     """Key direction that raises head h's score fastest (Wk^T q_hat_h), from a
     float64 numpy evaluation of the predictor on the host; only used to build
@@ -826,16 +873,15 @@ def main():
     # is the launch's own duration (no host gaps between launches). With the
     # split selection the attention launch consumes its state (it clears the
     # histograms), so it cannot be replayed alone: its duration is the mean of
-    # events recorded around it on its stream over whole eager steps, issued
-    # behind a GPU spin long enough that the host stays ahead of the GPU (no
-    # host gaps inside the events).
+    # fence-free events recorded around it on its stream over whole eager
+    # steps, issued behind a GPU spin long enough that the host stays ahead of
+    # the GPU (no host gaps inside the events).
     attn_eager_avg_s = attn_avg_s
     n_attn = K
     g_attn = None
     if split:
         n_attn = min(K, 600)
-        evs2 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                for _ in range(n_attn)]
+        evs2 = [(FenceFreeEvent(), FenceFreeEvent()) for _ in range(n_attn)]
         torch.cuda.synchronize()
         torch.cuda._sleep(int(2.4e9 * (n_attn * 40e-6 + 5e-3)))   # cycles at ~2.4 GHz
         for i in range(n_attn):
