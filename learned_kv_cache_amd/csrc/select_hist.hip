@@ -48,7 +48,11 @@ __global__ __launch_bounds__(TS, G <= 4 ? 8 : 4) void score_hist_kernel(
     constexpr int V = DP / 8;   // 16-byte vectors per key row
     __shared__ uint32_t s_h[G * HBINS / 2];    // two 16-bit counters per word
     __shared__ float s_sc[G][TS + 2 * R];      // slot j: position t0 - R + j
-    const int blk = blockIdx.x;
+    // XCD-aware order when the grid divides into the 8 XCDs (workgroups are
+    // dealt to them in turn): a KV head's blocks on one XCD, as the
+    // classification pass and the attention launch place that head's work
+    const int nbk = gridDim.x, bq = blockIdx.x;
+    const int blk = (nbk & 7) == 0 ? (bq & 7) * (nbk >> 3) + (bq >> 3) : bq;
     const int x = blk % nxs, kvh = (blk / nxs) % Hkv, b = blk / (nxs * Hkv);
     const int tid = threadIdx.x;
     const int t0 = x * TS;
