@@ -51,22 +51,28 @@ __device__ __forceinline__ void merge2(float &m, float &z, float m2, float z2) {
 }
 
 // Add one logit x (base 2) to a running (max m, sum z[, weighted sum a]),
-// branch-free. exp2 is the hardware instruction: its arguments are <= 0 and
+// branch-free, with one exp2: of the old maximum and x, the larger takes the
+// factor 2^0 = 1 and the other 2^-|x - m|, so the running sums are rescaled
+// when x is the new maximum and take the term 2^(x - m) otherwise (the same
+// roundings as forming both factors; no contraction, so a + e w rounds the
+// product first). exp2 is the hardware instruction: its argument is <= 0 and
 // results below 2^-126 (flushed) are negligible against the sum, which
 // always holds a term of 1.
 __device__ __forceinline__ void add3(float &m, float &z, float &a, float x, float w) {
-    const float mm = fmaxf(m, x);
-    const float r = __builtin_amdgcn_exp2f(m - mm);
-    const float e = __builtin_amdgcn_exp2f(x - mm);
-    z = __builtin_fmaf(z, r, e);
-    a = __builtin_fmaf(a, r, e * w);
-    m = mm;
+#pragma clang fp contract(off)
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x - m));
+    const bool up = x > m;
+    const float ew = e * w;
+    z = up ? __builtin_fmaf(z, e, 1.f) : z + e;
+    a = up ? __builtin_fmaf(a, e, w) : a + ew;
+    m = fmaxf(m, x);
 }
 
 __device__ __forceinline__ void add2(float &m, float &z, float x) {
-    const float mm = fmaxf(m, x);
-    z = __builtin_fmaf(z, __builtin_amdgcn_exp2f(m - mm), __builtin_amdgcn_exp2f(x - mm));
-    m = mm;
+#pragma clang fp contract(off)
+    const float e = __builtin_amdgcn_exp2f(-fabsf(x - m));
+    z = x > m ? __builtin_fmaf(z, e, 1.f) : z + e;
+    m = fmaxf(m, x);
 }
 
 template <int D, int DP>
