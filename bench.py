@@ -182,9 +182,11 @@ def run_interval(cfg, args, emit=True):
     """Prediction-interval pipeline over all layers of a multi-layer workload:
     once per interval, run every producer's predictor, score and select every
     consumer layer (the window left out of the list); then I decode steps,
-    each appending one token's K/V per sequence to every layer (tb_append_kv,
-    which projects the pending keys once N_p of them have accumulated) and
-    running sparse attention on every layer with the sliding window. Every
+    each appending one token's K/V per sequence to every layer (which projects
+    the pending keys once N_p of them have accumulated) and running sparse
+    attention on every layer with the sliding window, both in one launch per
+    layer (tb_append_attn; --append separate: tb_append_kv for every layer,
+    then tb_sparse_decode_attn for every layer). Every
     interval starts from the same lengths (the appended rows are rewritten).
     steps/s = I / interval time, with each interval replayed from one HIP
     graph of the whole interval (the same intervals issued call by call are
@@ -260,6 +262,7 @@ def run_interval(cfg, args, emit=True):
     v_new = [randn(B, Hkv, D) for _ in range(I)]
     mode = tb.TB_NF_FILL | tb.TB_SEL_OMIT_WINDOW
     stream = torch.cuda.current_stream()
+    fused = args.append == "fused"
 
     def interval(attn_ev=None, app_ev=None):
         lens.copy_(lens0)
@@ -269,6 +272,16 @@ def run_interval(cfg, args, emit=True):
             tb.tb_score_select(qhat[l // cfg.producer_stride], Kp[l], ctx0, ctx0, scores, cfg.S,
                                cfg.W, cfg.K, cfg.r, idx[l], cnt[l], ws_s, mode=mode)
         for j in range(I):
+            if fused:
+                # each layer's append and attention in one launch
+                if attn_ev is not None:
+                    attn_ev[j][0].record(stream)
+                for l in range(nl):
+                    tb.tb_append_attn(k_new[j], v_new[j], K[l], V[l], Kp[l], Wk[l], lens[l, 0],
+                                      lens[l, 1], Np, Q[l], idx[l], cnt[l], out, ws_a, window=cfg.W)
+                if attn_ev is not None:
+                    attn_ev[j][1].record(stream)
+                continue
             if app_ev is not None:
                 app_ev[j][0].record(stream)
             for l in range(nl):
@@ -324,12 +337,15 @@ def run_interval(cfg, args, emit=True):
     pct = lambda v: {"p10": round(float(np.percentile(v, 10)), 4),
                      "p50": round(float(np.percentile(v, 50)), 4),
                      "p90": round(float(np.percentile(v, 90)), 4), "intervals": len(v)}
-    app = np.array([[a.elapsed_time(b) * 1e3 / nl for a, b in row] for row in aevs])
-    proj_step = Np - 1 if Np <= I else None   # the step whose appends project the batch
-    append = {"us_per_layer_call": round(float(np.median(app)), 2),
-              "us_per_layer_call_projecting": (round(float(np.median(app[:, proj_step])), 2)
-                                               if proj_step is not None else None),
-              "n_p": Np}
+    if fused:
+        append = {"fused_with_attention": True, "n_p": Np}
+    else:
+        app = np.array([[a.elapsed_time(b) * 1e3 / nl for a, b in row] for row in aevs])
+        proj_step = Np - 1 if Np <= I else None   # the step whose appends project the batch
+        append = {"us_per_layer_call": round(float(np.median(app)), 2),
+                  "us_per_layer_call_projecting": (round(float(np.median(app[:, proj_step])), 2)
+                                                   if proj_step is not None else None),
+                  "n_p": Np}
     # compulsory gather bytes of one layer's attention launch at the first step
     gi, gc = idx[0].cpu().numpy(), cnt[0].cpu().numpy()
     rows = 0
@@ -356,7 +372,9 @@ def run_interval(cfg, args, emit=True):
                    "global_batch": B, "seq_len": int(L0.max())},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "sparse decode attention gather (one layer, one step)",
+                     "kernel": ("append + sparse decode attention gather (one layer, one step, "
+                                "one launch)" if fused else
+                                "sparse decode attention gather (one layer, one step)"),
                      "bytes_per_launch": attn_bytes, "avg_launch_us": attn_us},
         "append": append,
         "eager_steps_per_s": n_int * I / el_eager,
@@ -652,6 +670,9 @@ def main():
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured streaming-read and row-gather ceilings")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--append", choices=("fused", "separate"), default="fused",
+                    help="interval steps: each layer's K/V append and attention in one launch "
+                         "(tb_append_attn) or as tb_append_kv then tb_sparse_decode_attn")
     ap.add_argument("--defer", choices=("select", "list"), default="select",
                     help="the step's selection: split across the two calls "
                          "(TB_SEL_DEFER_SELECT; the attention launch finds the threshold) or "

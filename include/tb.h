@@ -323,6 +323,28 @@ tb_status tb_select_attn(const int32_t *ctx_len, const int32_t *proj_len, int B,
                          void *attn_workspace, size_t attn_ws_bytes, void *stream);
 
 /*
+ * The decode step's append and attention in one launch ("Inference strategy":
+ * the newest token joins the retained cache and the attention reads the sink,
+ * important and local-window rows): the same results, bit for bit, as
+ *     tb_append_kv(k_new, v_new, k_cache, v_cache, kp, wk, ctx_len, proj_len,
+ *                  B, Hkv, Lmax, D, dp, n_p, stream);
+ *     tb_sparse_decode_attn(q, k_cache, v_cache, idx, count, cap, ctx_len,
+ *                           window, B, Hq, Hkv, Lmax, D, scale, out,
+ *                           workspace, ws_bytes, stream);
+ * (arguments as there): the new rows are appended and the pending keys
+ * projected, and the attention's window ends at the length the append
+ * leaves, so it holds the new token. ctx_len and proj_len are advanced in
+ * place within the launch, after every workgroup has read them. workspace is
+ * sized by tb_attn_workspace_bytes(B, Hq, cap, window, D) and shared with
+ * tb_sparse_decode_attn (zero at rest).
+ */
+tb_status tb_append_attn(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                         void *kp, const void *wk, int32_t *ctx_len, int32_t *proj_len, int n_p,
+                         const void *q, const int32_t *idx, const int32_t *count, int cap,
+                         int window, int B, int Hq, int Hkv, int Lmax, int D, int dp, float scale,
+                         float *out, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Sparse decode attention ("Significance": attend over the retained cache
  * reading only the selected tokens):
  *     out[b, h] = sum_{t in F} softmax_t( scale * q[b,h] . k[b, h/g, t] ) v[b, h/g, t]

@@ -86,6 +86,9 @@ def lib():
     L.tb_select_attn.restype = _i
     L.tb_select_attn.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _i, _i, _i, _i, _vp, _vp, _i, _vp,
                                  _sz, _vp, _vp, _vp, _i, ctypes.c_float, _vp, _vp, _sz, _vp]
+    L.tb_append_attn.restype = _i
+    L.tb_append_attn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i,
+                                 _i, _i, _i, _i, _i, _i, ctypes.c_float, _vp, _vp, _sz, _vp]
     L.tb_attn_workspace_bytes.restype = _sz
     L.tb_attn_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
     L.tb_sparse_decode_attn.restype = _i
@@ -400,6 +403,37 @@ def tb_sparse_decode_attn(q, k_cache, v_cache, idx, count, out, workspace, scale
                                        _ptr(count, torch.int32, "count", 2), cap, ctx, int(window),
                                        B, Hq, Hkv, Lmax, D, float(scale), _ptr(out, torch.float32, "out", 3),
                                        wp, wn, _stream(stream)))
+    return out
+
+
+def tb_append_attn(k_new, v_new, k_cache, v_cache, kp, wk, ctx_len, proj_len, n_p, q, idx, count,
+                   out, workspace, window=0, scale=None, stream=None):
+    """tb_append_kv then tb_sparse_decode_attn(ctx_len=ctx_len, window=window) in one launch."""
+    B, Hkv, Lmax, D = k_cache.shape
+    dp = wk.shape[1]
+    Hq = q.shape[1]
+    cap = idx.shape[-1]
+    if (tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D)
+            or tuple(v_cache.shape) != (B, Hkv, Lmax, D) or tuple(wk.shape) != (Hkv, dp, D)
+            or tuple(kp.shape) != (B, Hkv, Lmax, dp) or ctx_len.numel() != B
+            or proj_len.numel() != B or tuple(q.shape) != (B, Hq, D)
+            or tuple(idx.shape) != (B, Hq, cap) or tuple(count.shape) != (B, Hq)
+            or tuple(out.shape) != (B, Hq, D)):
+        raise ValueError("tb_append_attn: shape mismatch")
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    wp, wn = _ws(workspace)
+    _check(lib().tb_append_attn(_ptr(k_new, torch.bfloat16, "k_new", 3),
+                                _ptr(v_new, torch.bfloat16, "v_new", 3),
+                                _ptr(k_cache, torch.bfloat16, "k_cache", 4),
+                                _ptr(v_cache, torch.bfloat16, "v_cache", 4),
+                                _ptr(kp, torch.float16, "kp", 4), _ptr(wk, torch.bfloat16, "wk", 3),
+                                _ptr(ctx_len, torch.int32, "ctx_len"),
+                                _ptr(proj_len, torch.int32, "proj_len"), int(n_p),
+                                _ptr(q, torch.bfloat16, "q", 3), _ptr(idx, torch.int32, "idx", 3),
+                                _ptr(count, torch.int32, "count", 2), cap, int(window), B, Hq, Hkv,
+                                Lmax, D, dp, float(scale), _ptr(out, torch.float32, "out", 3), wp,
+                                wn, _stream(stream)))
     return out
 
 

@@ -176,9 +176,9 @@ __device__ __forceinline__ bool attn_store_merge(float m, float l, float (&acc)[
 // One workgroup's split of head bh (sequence b, KV head kvh): list rows
 // [lo, hi) whose positions, clamped to the cache, are staged in sm_tok[0,
 // hi - lo). Forms the split's (max, sum, o) partial and, in the last split of
-// the head to arrive, merges all nsplit partials into out.
+// the head to arrive, merges all nsplit partials into out (and returns true).
 template <int D>
-__device__ __forceinline__ void attn_split(const uint16_t *__restrict__ q,
+__device__ __forceinline__ bool attn_split(const uint16_t *__restrict__ q,
                                            const uint16_t *__restrict__ kc,
                                            const uint16_t *__restrict__ vc, int Hkv, int Lmax,
                                            float scale_log2, int nsplit,
@@ -274,7 +274,7 @@ __device__ __forceinline__ void attn_split(const uint16_t *__restrict__ q,
         }
     }
 
-    attn_store_merge<D>(m, l, acc, nsplit, part, ctr, out, bh, split);
+    return attn_store_merge<D>(m, l, acc, nsplit, part, ctr, out, bh, split);
 }
 
 // The lane's row-group (max, sum, o) state over rows [0, nrows) whose

@@ -95,76 +95,23 @@ __global__ __launch_bounds__(kProjThreads) void project_kernel(
     project_block<D, DP>(kc, wk, kp, pos0, ntok, Hkv, Lmax, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// Decode-step append with batched projection, one workgroup per sequence:
-// the new K/V rows go to position L = ctx_len[b] of every KV head; once the
-// pending keys [P, L + 1) number n_p, the waves project them (16 tokens of
-// one head per item, the new token's row read from k_new rather than from
-// the cache it was just written to); then the lengths are advanced.
+// Decode-step append with batched projection, one workgroup per sequence
+// (append_rows), then the lengths are advanced.
 template <int D, int DP>
 __global__ __launch_bounds__(kProjThreads) void append_kernel(
     const uint16_t *__restrict__ k_new, const uint16_t *__restrict__ v_new,
     uint16_t *__restrict__ kc, uint16_t *__restrict__ vc, uint16_t *__restrict__ kp,
     const uint16_t *__restrict__ wk, int32_t *__restrict__ ctx, int32_t *__restrict__ plen,
     int Hkv, int Lmax, int n_p) {
-    constexpr int NV = D / 32;   // 16-byte pieces per lane per row
-    constexpr int MT = DP / 16;
-    constexpr int R16 = D / 8;   // 16-byte pieces per row
     const int b = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int L = ctx[b], P = plen[b];
-    if (!(P >= 0 && P <= L && L < Lmax)) return;
-    for (int i = threadIdx.x; i < 2 * Hkv * R16; i += kProjThreads) {
-        const int which = i / (Hkv * R16), r = i % (Hkv * R16);
-        const int j = r / R16, v = r % R16;
-        const uint4 *src = reinterpret_cast<const uint4 *>((which ? v_new : k_new) +
-                                                           ((size_t)b * Hkv + j) * D) + v;
-        uint4 *dst = reinterpret_cast<uint4 *>((which ? vc : kc) +
-                                               (((size_t)b * Hkv + j) * Lmax + L) * D) + v;
-        *dst = *src;
-    }
-    const int L1 = L + 1;
-    const bool proj = L1 - P >= n_p;
-    if (proj) {
-        const int n = lane & 15, kq = lane >> 4;
-        const int nb = (L1 - P + 15) / 16;
-        for (int item = wave; item < Hkv * nb; item += kProjThreads / 64) {
-            const int j = item / nb, blk = item % nb;
-            const int t = P + blk * 16 + n;
-            const bool valid = t < L1;
-            const size_t head = (size_t)b * Hkv + j;
-            uint4 kv[NV];
-            if (valid) {
-                const uint16_t *rowp = t == L ? k_new + head * D : kc + (head * Lmax + t) * D;
-                const uint4 *row = reinterpret_cast<const uint4 *>(rowp + kq * (D / 4));
-#pragma unroll
-                for (int v = 0; v < NV; ++v) kv[v] = row[v];
-            } else {
-#pragma unroll
-                for (int v = 0; v < NV; ++v) kv[v] = make_uint4(0, 0, 0, 0);
-            }
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const uint4 *wrow = reinterpret_cast<const uint4 *>(
-                    wk + ((size_t)j * DP + mt * 16 + n) * D + kq * (D / 4));
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int v = 0; v < NV; ++v)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, wrow[v]), __builtin_bit_cast(bf16x8_t, kv[v]),
-                        acc, 0, 0, 0);
-                if (valid) {
-                    const uint32_t lo = f32_to_f16_bits(acc[0]) | (f32_to_f16_bits(acc[1]) << 16);
-                    const uint32_t hi = f32_to_f16_bits(acc[2]) | (f32_to_f16_bits(acc[3]) << 16);
-                    *reinterpret_cast<uint2 *>(kp + (head * Lmax + t) * DP + mt * 16 + 4 * kq) =
-                        make_uint2(lo, hi);
-                }
-            }
-        }
-    }
+    if (!append_applies(L, P, Lmax)) return;
+    const bool proj = append_rows<D, DP, kProjThreads>(k_new, v_new, kc, vc, kp, wk, b, L, P, Hkv,
+                                                      Lmax, n_p);
     __syncthreads();
     if (threadIdx.x == 0) {
-        ctx[b] = L1;
-        if (proj) plen[b] = L1;
+        ctx[b] = L + 1;
+        if (proj) plen[b] = L + 1;
     }
 }
 

@@ -434,4 +434,39 @@ tb_status tb_sparse_decode_attn(const void *q, const void *k_cache, const void *
                            D, scale, out, part, ctr, static_cast<hipStream_t>(stream));
 }
 
+tb_status tb_append_attn(const void *k_new, const void *v_new, void *k_cache, void *v_cache,
+                         void *kp, const void *wk, int32_t *ctx_len, int32_t *proj_len, int n_p,
+                         const void *q, const int32_t *idx, const int32_t *count, int cap,
+                         int window, int B, int Hq, int Hkv, int Lmax, int D, int dp, float scale,
+                         float *out, void *workspace, size_t ws_bytes, void *stream) {
+    TB_REQUIRE(k_new && v_new && k_cache && v_cache && kp && wk && ctx_len && proj_len && q &&
+                   idx && count && out && workspace,
+               TB_ERR_INVALID_ARGUMENT, "tb_append_attn: null pointer");
+    TB_REQUIRE(aligned16(k_new) && aligned16(v_new) && aligned16(k_cache) && aligned16(v_cache) &&
+                   aligned16(kp) && aligned16(wk) && aligned4(ctx_len) && aligned4(proj_len) &&
+                   aligned16(q) && aligned4(idx) && aligned4(count) && aligned4(out) &&
+                   aligned16(workspace),
+               TB_ERR_INVALID_ARGUMENT, "tb_append_attn: misaligned pointer");
+    TB_REQUIRE(B >= 1 && B <= 65535 && Hq >= 1 && Hkv >= 1 && Hkv <= 65535 && Lmax >= 1 &&
+                   cap >= 1 && window >= 0 && n_p >= 1,
+               TB_ERR_INVALID_ARGUMENT, "tb_append_attn: bad sizes");
+    TB_REQUIRE(Hq % Hkv == 0, TB_ERR_INVALID_ARGUMENT, "tb_append_attn: Hq %% Hkv != 0");
+    TB_REQUIRE((D == 64 || D == 128) && (dp == 16 || dp == 32), TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_append_attn: D must be 64 or 128 and dp 16 or 32 (got %d, %d)", D, dp);
+    TB_REQUIRE((long long)Lmax * D * 2 <= 0x7fffffffLL, TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_append_attn: one head's cache must be below 2 GiB (Lmax * D * 2)");
+    TB_REQUIRE(scale == scale, TB_ERR_INVALID_ARGUMENT, "tb_append_attn: scale is NaN");
+    const size_t need = tb_attn_workspace_bytes(B, Hq, cap, window, D);
+    TB_REQUIRE(need > 0, TB_ERR_UNSUPPORTED_SHAPE,
+               "tb_append_attn: cap + window or B * Hq * splits beyond INT_MAX");
+    TB_REQUIRE(ws_bytes >= need, TB_ERR_WORKSPACE_TOO_SMALL,
+               "tb_append_attn: workspace %zu < %zu bytes", ws_bytes, need);
+    float *part;
+    uint32_t *ctr, *bctr;
+    tb::attn_ws_layout(B, Hq, cap + window, D, workspace, &part, &ctr, &bctr);
+    return tb::launch_append_attn(k_new, v_new, k_cache, v_cache, kp, wk, ctx_len, proj_len, n_p,
+                                  q, idx, count, cap, window, B, Hq, Hkv, Lmax, D, dp, scale, out,
+                                  part, ctr, bctr, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

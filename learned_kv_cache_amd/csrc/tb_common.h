@@ -164,7 +164,13 @@ tb_status launch_select_attn(const int32_t *ctx, const int32_t *plen, int B, int
                              const void *kc, const void *vc, int D, float scale, float *out,
                              float *part, uint32_t *ctr, hipStream_t st);
 int attn_nsplit(int rows);
-size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr);
+size_t attn_ws_layout(int B, int Hq, int rows, int D, void *base, float **part, uint32_t **ctr,
+                      uint32_t **bctr = nullptr);
+tb_status launch_append_attn(const void *k_new, const void *v_new, void *kc, void *vc, void *kp,
+                             const void *wk, int32_t *ctx, int32_t *plen, int n_p, const void *q,
+                             const int32_t *idx, const int32_t *count, int cap, int window, int B,
+                             int Hq, int Hkv, int Lmax, int D, int dp, float scale, float *out,
+                             float *part, uint32_t *ctr, uint32_t *bctr, hipStream_t st);
 tb_status launch_attn(const void *q, const void *kc, const void *vc, const int32_t *idx,
                       const int32_t *count, int cap, const int32_t *ctx, int window, int B,
                       int Hq, int Hkv, int Lmax, int D, float scale, float *out, float *part,

@@ -28,7 +28,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(tb):
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 24
     lib = ctypes.CDLL(tb.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -107,6 +107,17 @@ def test_validation_rejects_before_launch(tb):
     assert L.tb_sparse_decode_attn(*A(8, 64, 16)) == 3
     assert L.tb_sparse_decode_attn(*A(9, 64, ws)) == 1
     assert L.tb_sparse_decode_attn(*A(8, 64, ws, -1)) == 1
+    # the fused append + attention: the union of both calls' checks
+    AA = lambda Hq, D, dp, wsb, n_p=4, win=16: (vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE), vp(FAKE),
+                                                vp(FAKE), vp(FAKE), vp(FAKE), n_p, vp(FAKE),
+                                                vp(FAKE), vp(FAKE), 64, win, 1, Hq, 2, 300, D, dp,
+                                                ctypes.c_float(0.1), vp(FAKE), vp(FAKE), wsb, None)
+    assert L.tb_append_attn(*AA(8, 96, 32, ws)) == 2
+    assert L.tb_append_attn(*AA(8, 64, 24, ws)) == 2
+    assert L.tb_append_attn(*AA(8, 64, 16, 16)) == 3
+    assert L.tb_append_attn(*AA(9, 64, 16, ws)) == 1
+    assert L.tb_append_attn(*AA(8, 64, 16, ws, 0)) == 1
+    assert L.tb_append_attn(*AA(8, 64, 16, ws, 4, -1)) == 1
     assert L.tb_select(*args(4, 16, 32, 1, 0x400, 52, ws)) == 1   # unknown mode bit
     assert L.tb_select(*args(4, 16, 32, 1, 0x201, 115, ws)) == 1  # deferred list with dilation
     # list + attention after a deferred selection: its checks reject before launch
