@@ -5,7 +5,7 @@ step (steps that project the pending keys included), with ragged lengths,
 lengths the append refuses (a full cache, a projected length past the
 context), no window, D 64 and 128, and the 256K per-layer shape of the
 interval workload; the workspace's arrival counters are zero after every
-call."""
+call; and steps captured in a graph, replayed with eager calls between."""
 import numpy as np
 import pytest
 import torch
@@ -93,3 +93,56 @@ def test_append_attn_interval_layer_shape(tb):
     # one layer of the 256K interval workload: 32 query heads, 8 KV heads,
     # sink + budget rows in the list, a 256-row window, projection every 16
     _run(tb, 5, 1, 32, 8, 262144, 128, 32, [262000], [261990], 7936, 256, 16, 3)
+
+
+def test_append_attn_graph_replays(tb):
+    """Steps of the fused call captured in a graph and replayed from the same
+    starting lengths, with eager calls between replays: every replay gives
+    the eager run's output, lengths and cache rows."""
+    B, Hq, Hkv, Lmax, D, dp, cap, window, n_p, steps = 2, 8, 2, 3000, 128, 32, 256, 64, 4, 6
+    say("append_attn graph", B, Hq, Lmax, steps)
+    rng = rng_for(71, 9)
+    kc = dev(normal_bf16(rng, (B, Hkv, Lmax, D)), torch.bfloat16)
+    vc = dev(normal_bf16(rng, (B, Hkv, Lmax, D)), torch.bfloat16)
+    kp = dev(normal_f16(rng, (B, Hkv, Lmax, dp), std=0.5), torch.float16)
+    wk = dev(xavier_bf16(rng, dp, D, lead=(Hkv,)), torch.bfloat16)
+    q = dev(normal_bf16(rng, (B, Hq, D)), torch.bfloat16)
+    idx = np.zeros((B, Hq, cap), np.int32)
+    for b in range(B):
+        for h in range(Hq):
+            idx[b, h] = np.sort(rng.choice(2000, cap, replace=False))
+    idx, cnt = dev32(idx), dev32(np.full((B, Hq), cap, np.int32))
+    kn = [dev(normal_bf16(rng, (B, Hkv, D)), torch.bfloat16) for _ in range(steps)]
+    vn = [dev(normal_bf16(rng, (B, Hkv, D)), torch.bfloat16) for _ in range(steps)]
+    lens0 = dev32(np.array([[2500, 2998], [2497, 2990]], np.int32))   # [ctx, proj] x B
+    lens = lens0.clone()
+    ws = tb.new_workspace(tb.tb_attn_workspace_bytes(B, Hq, cap, window, D))
+    outs = [torch.zeros(B, Hq, D, device="cuda") for _ in range(steps)]
+
+    def run():
+        lens.copy_(lens0)
+        for j in range(steps):
+            tb.tb_append_attn(kn[j], vn[j], kc, vc, kp, wk, lens[0], lens[1], n_p, q, idx, cnt,
+                              outs[j], ws, window=window)
+
+    run()
+    torch.cuda.synchronize()
+    ref = ([host(o).copy() for o in outs], host(lens).copy(), bits(kc).copy(), bits(kp).copy())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for j in range(steps):
+            assert np.array_equal(host(outs[j]).view(np.uint32), ref[0][j].view(np.uint32)), (rep, j)
+        assert np.array_equal(host(lens), ref[1]), rep
+        assert np.array_equal(bits(kc), ref[2]) and np.array_equal(bits(kp), ref[3]), rep
+        run()   # eager work between replays
+        torch.cuda.synchronize()
